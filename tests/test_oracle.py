@@ -1,0 +1,247 @@
+"""Pins of the CPU oracle against things other than itself: numpy's integer
+matmul (brute force), closed forms of the absmean rule on Gaussian weights,
+invariants of the contraction, and hand-derived fixtures under tests/golden/.
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from conftest import read_golden
+from workloads import bf16_bits_to_f32, f32_to_bf16_bits
+
+
+# ---------------------------------------------------------------- contraction
+
+@pytest.mark.parametrize("seed", range(8))
+def test_linear_matches_int64_matmul(orc, seed):
+    rng = np.random.default_rng(seed)
+    M = int(rng.integers(1, 5))
+    K = int(rng.integers(1, 65))
+    N = int(rng.integers(1, 17))
+    q = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    t = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    ref = q.astype(np.int64) @ t.astype(np.int64).T
+    acc = orc.linear(q, t)
+    assert acc.dtype == np.int32
+    np.testing.assert_array_equal(acc.astype(np.int64), ref)
+
+
+def test_linear_extremes(orc):
+    K = 8192
+    q = np.full((2, K), 127, dtype=np.int8)
+    q[1] = -127
+    t = np.ones((3, K), dtype=np.int8)
+    t[1] = -1
+    t[2, ::2] = -1
+    acc = orc.linear(q, t)
+    ref = q.astype(np.int64) @ t.astype(np.int64).T
+    np.testing.assert_array_equal(acc, ref)
+    assert acc[0, 0] == 127 * 8192 and acc[1, 0] == -127 * 8192
+
+
+def test_linear_invariants(orc):
+    rng = np.random.default_rng(5)
+    M, K, N = 3, 96, 7
+    q = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    # zero weights give zero
+    assert not orc.linear(q, np.zeros((N, K), np.int8)).any()
+    # all +1 row gives the activation row sum, all -1 its negation
+    t = np.zeros((N, K), np.int8)
+    t[0] = 1
+    t[1] = -1
+    k0 = 17
+    t[2, k0] = 1  # one-hot
+    acc = orc.linear(q, t)
+    rowsum = q.astype(np.int64).sum(axis=1)
+    np.testing.assert_array_equal(acc[:, 0], rowsum)
+    np.testing.assert_array_equal(acc[:, 1], -rowsum)
+    np.testing.assert_array_equal(acc[:, 2], q[:, k0])
+    # negating the weights negates the result
+    tr = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    np.testing.assert_array_equal(orc.linear(q, -tr), -orc.linear(q, tr))
+    # width invariance: row m of an M-wide call equals the 1-wide call
+    full = orc.linear(q, tr)
+    for m in range(M):
+        np.testing.assert_array_equal(full[m], orc.linear(q[m:m + 1], tr)[0])
+    # bound
+    assert np.all(np.abs(full) <= 127 * np.count_nonzero(tr, axis=1)[None, :])
+
+
+# --------------------------------------------------------------- ternarize
+
+def test_ternarize_gaussian_closed_form(orc):
+    # For W ~ N(0, s^2) and gamma = E|W| = s*sqrt(2/pi), t = 0 iff
+    # |W| <= gamma/2, so P(t = 0) = 2*Phi(sqrt(2/pi)/2) - 1 = 0.3101 for any s.
+    p0 = math.erf(math.sqrt(2 / math.pi) / 2 / math.sqrt(2))
+    assert abs(p0 - 0.3101) < 1e-4
+    for sigma in (1.0, 0.02):
+        rng = np.random.default_rng(0)
+        W = rng.standard_normal((512, 256), dtype=np.float32) * np.float32(sigma)
+        t, g = orc.ternarize_absmean(W)
+        frac0 = np.mean(t == 0)
+        assert abs(frac0 - p0) < 0.01
+        assert abs(np.mean(t == 1) - (1 - p0) / 2) < 0.01
+        # gamma is the mean absolute value, rounded once to fp32
+        mean = float(np.mean(np.abs(W.astype(np.float64))))
+        assert abs(g - mean) <= 2 ** -23 * mean
+        assert abs(g / sigma - math.sqrt(2 / math.pi)) < 0.01
+
+
+def test_ternarize_threshold_characterisation(orc):
+    # clamp(rint(v), -1, 1) with ties to even equals sign(v) for |v| > 1/2 and
+    # 0 for |v| <= 1/2; check that form on random weights, using the fp32
+    # quotient, and check signs.
+    rng = np.random.default_rng(3)
+    W = rng.standard_normal((64, 160), dtype=np.float32)
+    t, g = orc.ternarize_absmean(W)
+    v = W / np.float32(g)
+    expect = np.where(np.abs(v) > 0.5, np.sign(v), 0).astype(np.int8)
+    np.testing.assert_array_equal(t, expect)
+    assert set(np.unique(t)) <= {-1, 0, 1}
+
+
+def test_ternarize_ties_and_zero(orc):
+    # gamma = (1 + 7) / 4 = 2: W/gamma = 0.5, 3.5 -> 0 (half-even) and 1.
+    t, g = orc.ternarize_absmean(np.array([[1, 7, 0, 0]], np.float32))
+    assert g == 2.0
+    assert t.tolist() == [[0, 1, 0, 0]]
+    t, g = orc.ternarize_absmean(np.array([[-1, 7, 0, 0]], np.float32))
+    assert t.tolist() == [[0, 1, 0, 0]]
+    t, g = orc.ternarize_absmean(np.zeros((3, 32), np.float32))
+    assert g == 0.0 and not t.any()
+    # negation symmetry
+    W = np.random.default_rng(9).standard_normal((8, 48), dtype=np.float32)
+    t1, g1 = orc.ternarize_absmean(W)
+    t2, g2 = orc.ternarize_absmean(-W)
+    assert g1 == g2
+    np.testing.assert_array_equal(t2, -t1)
+
+
+def test_ternarize_rejects_nonfinite(orc):
+    W = np.ones((2, 16), np.float32)
+    W[1, 3] = np.inf
+    with pytest.raises(ValueError):
+        orc.ternarize_absmean(W)
+
+
+# ---------------------------------------------------------------- quantize
+
+def test_quantize_crafted_ties(orc):
+    x = f32_to_bf16_bits(np.array([[127, 62.5, -62.5, 0.5, 1.5, 2.5]], np.float32))
+    q, s = orc.quantize_act(x)
+    assert q.tolist() == [[127, 62, -62, 0, 2, 2]]
+    assert s[0] == np.float32(1.0)
+    # absmax 254 gives inv = 0.5 exactly: 125 * 0.5 = 62.5 -> 62, 3 * .5 -> 2
+    x = f32_to_bf16_bits(np.array([[254, 125, 3, -5, 1]], np.float32))
+    q, s = orc.quantize_act(x)
+    assert q.tolist() == [[127, 62, 2, -2, 0]]
+    assert s[0] == np.float32(2.0)
+
+
+def test_quantize_properties(orc):
+    rng = np.random.default_rng(11)
+    xf = rng.standard_normal((16, 512), dtype=np.float32)
+    xf[3, 10:40] *= 20.0
+    xf[5] = 0.0
+    xb = f32_to_bf16_bits(xf)
+    q, s = orc.quantize_act(xb)
+    xw = bf16_bits_to_f32(xb).astype(np.float64)
+    a = np.abs(xw).max(axis=1)
+    for m in range(16):
+        if a[m] == 0:
+            assert not q[m].any() and s[m] == 0
+            continue
+        assert np.abs(q[m]).max() == 127
+        assert q[m][np.argmax(np.abs(xw[m]))] == np.sign(xw[m][np.argmax(np.abs(xw[m]))]) * 127
+        # exact-real view: q is a nearest integer of x*127/a, up to the fp32
+        # rounding of 127/a and of the product (relative 2^-23 together)
+        v = xw[m] * 127.0 / a[m]
+        assert np.all(np.abs(q[m] - v) <= 0.5 + 128 * 2.0 ** -22)
+        assert np.all((np.sign(q[m]) == np.sign(v)) | (q[m] == 0))
+        # the scale is a/127 to within half an fp32 ulp
+        assert abs(float(s[m]) - a[m] / 127.0) <= 2.0 ** -24 * a[m] / 127.0
+
+
+# ---------------------------------------------------------------- format
+
+def test_unpack_golden_word(orc):
+    g = read_golden("packed_word.txt")
+    packed = np.array([int(v, 16) for v in g["BYTES"]], np.uint8)
+    t = orc.unpack(packed, 1, 16)
+    assert t[0].tolist() == [int(v) for v in g["T"]]
+
+
+def test_unpack_exhaustive_bytes(orc):
+    # every byte value at every byte position of a word: exactly the 81 bytes
+    # whose four fields are all < 3 decode; the other 175 are rejected.
+    for pos in range(4):
+        valid = 0
+        for byte in range(256):
+            word = np.full(4, 0x55, np.uint8)  # 0x55 = four zero-valued codes
+            word[pos] = byte
+            try:
+                t = orc.unpack(word, 1, 16)
+            except ValueError:
+                continue
+            valid += 1
+            # only the 4 elements held by this byte may be nonzero
+            nz = set(np.nonzero(t[0])[0].tolist())
+            assert nz <= {pos, pos + 4, pos + 8, pos + 12}
+        assert valid == 81
+
+
+def test_unpack_bad_shapes(orc):
+    with pytest.raises(ValueError):
+        orc.unpack(np.zeros(3, np.uint8), 1, 12)
+
+
+# ---------------------------------------------------------------- dequant
+
+def test_dequant_exact_product(orc):
+    rng = np.random.default_rng(2)
+    acc = rng.integers(-10 ** 6, 10 ** 6, size=(3, 5)).astype(np.int32)
+    acc[0, 0] = 0
+    s = rng.random(3).astype(np.float32)
+    g = rng.random(5).astype(np.float32)
+    y = orc.dequant(acc, s, g)
+    assert y[0, 0] == 0.0
+    for m in range(3):
+        for n in range(5):
+            exact = Fraction(int(acc[m, n])) * Fraction(float(s[m])) * Fraction(float(g[n]))
+            if exact == 0:
+                assert y[m, n] == 0
+            else:
+                assert abs(Fraction(y[m, n]) - exact) <= abs(exact) * Fraction(1, 2 ** 51)
+
+
+# ---------------------------------------------------------------- end to end
+
+def test_hand_worked_example(orc):
+    g = read_golden("hand_case_k16.txt")
+    W = np.array([[float(v) for v in g["W0"]], [float(v) for v in g["W1"]]], np.float32)
+    x = f32_to_bf16_bits(np.array([[float(v) for v in g["X0"]]], np.float32))
+    r = orc.forward(W, (2,), x)
+    assert r["gammas"] == [float(g["gamma"][0])]
+    assert r["t"][0].tolist() == [int(v) for v in g["T0"]]
+    assert r["t"][1].tolist() == [int(v) for v in g["T1"]]
+    assert r["q"][0].tolist() == [int(v) for v in g["Q0"]]
+    assert float(r["scale"][0]) == float(g["scale"][0])
+    assert r["acc"][0].tolist() == [int(v) for v in g["ACC0"]]
+    assert r["y"][0].tolist() == [float(v) for v in g["Y0"]]
+    packed = np.array([[int(v, 16) for v in g["PACKED0"]],
+                       [int(v, 16) for v in g["PACKED1"]]], np.uint8)
+    np.testing.assert_array_equal(orc.unpack(packed, 2, 16), r["t"])
+
+
+def test_segments_concatenate(orc):
+    rng = np.random.default_rng(4)
+    W = rng.standard_normal((48, 64), dtype=np.float32)
+    W[32:] *= 5.0
+    t, gammas, grow = orc.ternarize_segments(W, (32, 16))
+    t0, g0 = orc.ternarize_absmean(W[:32])
+    t1, g1 = orc.ternarize_absmean(W[32:])
+    assert gammas == [g0, g1] and g1 > 4 * g0
+    np.testing.assert_array_equal(t, np.concatenate([t0, t1]))
+    assert np.all(grow[:32] == g0) and np.all(grow[32:] == g1)
