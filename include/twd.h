@@ -1,0 +1,164 @@
+/*
+ * twd.h -- C ABI of the MI355X (gfx950) W2A8 ternary linear library.
+ *
+ * The library computes the packed W2A8 linear layer that BitMTP's
+ * width-specialized low-bit execution runs at the narrow token widths that
+ * block-parallel multi-token prediction produces (page "BitMTP: When
+ * Multi-Token Prediction Meets Low-Bit Large Language Models", ai.info AI
+ * summary): M = 1 for autoregressive steps, M = 2..16 for drafted-block
+ * verification ("Methodology in Plain English", paragraphs 2-3: the verifier
+ * runs the anchor plus the whole draft through the model; M1 picks packed
+ * low-bit operators by replay width and input/output dimensions).  Weights
+ * are ternary (BitNet b1.58, "What This Paper Is About"); the setting is W2A8:
+ * 2-bit weights, 8-bit activations ("Main Findings", first bullet).
+ *
+ * Conventions for every call:
+ *   - W is [N][K] (output rows x input columns), x is [M][K], y = x W^T.
+ *   - The caller owns every buffer; the library keeps no pointer after a call
+ *     returns and allocates nothing.  Device calls are asynchronous on
+ *     `stream` (a hipStream_t; NULL means the null stream): buffers must stay
+ *     alive until that stream's work completes.  Device calls neither
+ *     synchronize nor read device memory on the host, so they may be
+ *     captured into a HIP graph.
+ *   - Arguments are checked before anything is launched.  On a non-OK status
+ *     nothing was launched (or, for TWD_ERR_HIP, the launch failed) and
+ *     twd_last_error() returns a message for the calling thread.
+ *   - Integer results are deterministic: two calls on the same inputs give
+ *     the same bits.
+ */
+#ifndef TWD_H
+#define TWD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TWD_OK = 0,
+    TWD_ERR_INVALID_ARG = 1, /* null pointer, negative size, misaligned buffer */
+    TWD_ERR_UNSUPPORTED = 2, /* shape outside what the kernels handle */
+    TWD_ERR_BAD_CODE = 3,    /* weight code outside {-1, 0, +1} or field == 3 */
+    TWD_ERR_HIP = 4          /* the HIP runtime reported an error */
+} twd_status;
+
+/* Limits of the device kernels. */
+#define TWD_MAX_M 16          /* token rows per call */
+#define TWD_MAX_K 8192        /* input width (activation rows are staged in LDS) */
+#define TWD_MAX_SEGMENTS 4    /* independently scaled row segments (fused) */
+
+/* Kernel families of the linear; TWD_KERNEL_AUTO lets the width dispatch
+ * choose (M1's "select by replay width and input/output dimensions"). */
+typedef enum {
+    TWD_KERNEL_AUTO = 0,
+    TWD_KERNEL_DOT = 1,  /* VALU: 2-bit decode in registers + v_dot4 int8 */
+    TWD_KERNEL_MFMA = 2  /* matrix cores: v_mfma_i32_16x16x64_i8 */
+} twd_kernel;
+
+/* Library version string; never NULL. */
+const char *twd_version(void);
+
+/* Message for the last non-OK status returned on the calling thread. */
+const char *twd_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Weight format (host, offline).
+ *
+ * Ternary code c = t + 1 (0, 1, 2; 3 is invalid), two bits per weight.  Row
+ * n occupies K/4 bytes; rows are contiguous.  Its K/16 little-endian 32-bit
+ * words each hold sixteen weights k = 16 i + e with e = 4 j + b (j, b in
+ * 0..3): the code of element e sits at bit 8 b + 2 j.  So masking a word
+ * with 0x03030303 << 2j yields four byte lanes holding the codes of
+ * elements 4j .. 4j+3, which line up with one 32-bit word of int8
+ * activations.  The pages call the execution "packed W2A8" ("Methodology in
+ * Plain English", last paragraph) but give no layout; this one is chosen
+ * for byte-wise dot products and matrix-core operands.
+ * ---------------------------------------------------------------------- */
+
+/* Absmean ternarization of one tensor W[N][K] (fp32, host memory):
+ * gamma = mean |W| (summed in double in row-major order, rounded once to
+ * fp32), codes = clamp(rint(W / gamma), -1, 1) with an fp32 division and
+ * ties to even; gamma == 0 gives all-zero codes.  BitNet b1.58's rule; the
+ * pages name the model but not the formula.  codes: host int8 [N][K].
+ * Errors: INVALID_ARG for null pointers, negative sizes or a non-finite W. */
+twd_status twd_ternarize_absmean(const float *W, int64_t N, int64_t K,
+                                 int8_t *codes, float *gamma);
+
+/* Pack host codes int8 [N][K] in {-1, 0, +1} into host bytes [N][K/4].
+ * Errors: INVALID_ARG (null, N < 0, K < 0, K % 16 != 0), BAD_CODE. */
+twd_status twd_pack_ternary(const int8_t *codes, int64_t N, int64_t K,
+                            uint8_t *packed);
+
+/* Inverse of twd_pack_ternary.  Errors: INVALID_ARG, BAD_CODE on a field
+ * holding the invalid code 3. */
+twd_status twd_unpack_ternary(const uint8_t *packed, int64_t N, int64_t K,
+                              int8_t *codes);
+
+/* ------------------------------------------------------------------------
+ * Device calls.
+ * ---------------------------------------------------------------------- */
+
+/* Per-token absmax int8 quantization ("Main Findings": 8-bit activations).
+ * x_bf16: device bf16 bit patterns [M][K]; xq: device int8 [M][K];
+ * xscale: device fp32 [M].  For each row: a = max |x|, inv = 127 / a (fp32,
+ * correctly rounded), xq = clamp(rint(x * inv), -127, 127), xscale = a / 127;
+ * a == 0 gives xq = 0 and xscale = 0.  Non-finite x is outside the contract.
+ * Shapes: 0 <= M (M == 0 is a no-op), 1 <= K <= 65536, K % 8 == 0.
+ * Alignment: x_bf16 and xq 16-byte aligned. */
+twd_status twd_quantize_act(const uint16_t *x_bf16, int64_t M, int64_t K,
+                            int8_t *xq, float *xscale, void *stream);
+
+/* W2A8 ternary linear: acc[m][n] = sum_k xq[m][k] * t[n][k] in int32
+ * (exact), y[m][n] = acc[m][n] * xscale[m] * gamma in fp32.
+ * wpacked: device packed weights [N][K/4] (format above); xq, xscale: the
+ * outputs of twd_quantize_act; acc (int32 [M][N]) and y (fp32 [M][N]) are
+ * device outputs, either may be NULL (not both).
+ * Shapes: 0 <= M <= 16 (M == 0 is a no-op), N >= 0 (N == 0 is a no-op),
+ * 64 <= K <= TWD_MAX_K with K % 64 == 0.  Alignment: wpacked and xq 16 bytes,
+ * acc and y 4 bytes.  The kernel is chosen by (M, K, N). */
+twd_status twd_ternary_linear(const uint8_t *wpacked, float gamma,
+                              const int8_t *xq, const float *xscale,
+                              int64_t M, int64_t K, int64_t N,
+                              int32_t *acc, float *y, void *stream);
+
+/* Fused projections (Q/K/V, gate/up): one launch over the concatenated
+ * output rows.  seg_rows / seg_gamma are HOST arrays of nseg (1..4) entries:
+ * segment s covers the next seg_rows[s] rows and is dequantized with
+ * seg_gamma[s].  They are copied into the kernel arguments, so a captured
+ * graph keeps them.  N = sum of seg_rows; other arguments as above. */
+twd_status twd_ternary_linear_fused(const uint8_t *wpacked, int nseg,
+                                    const int64_t *seg_rows,
+                                    const float *seg_gamma,
+                                    const int8_t *xq, const float *xscale,
+                                    int64_t M, int64_t K,
+                                    int32_t *acc, float *y, void *stream);
+
+/* As twd_ternary_linear_fused with the kernel family forced (tests and
+ * measurement of the width crossover).  kernel = TWD_KERNEL_AUTO behaves
+ * exactly like twd_ternary_linear_fused. */
+twd_status twd_ternary_linear_fused_kernel(const uint8_t *wpacked, int nseg,
+                                           const int64_t *seg_rows,
+                                           const float *seg_gamma,
+                                           const int8_t *xq,
+                                           const float *xscale, int64_t M,
+                                           int64_t K, int32_t *acc, float *y,
+                                           int kernel, void *stream);
+
+/* The kernel family the width dispatch picks for (M, K, N), without
+ * launching anything.  Returns TWD_KERNEL_DOT or TWD_KERNEL_MFMA, or -1 if
+ * the shape is unsupported. */
+int twd_select_kernel(int64_t M, int64_t K, int64_t N);
+
+/* Measurement helper: a plain streaming read of `bytes` device bytes
+ * (16-byte aligned, bytes % 16 == 0) that stores nothing but a guard word
+ * into sink (device, >= 1024 bytes).  Its launch duration is the
+ * achievable-bandwidth reference for a kernel moving the same bytes. */
+twd_status twd_stream_read(const void *buf, int64_t bytes, uint32_t *sink,
+                           void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TWD_H */

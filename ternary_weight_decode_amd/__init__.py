@@ -1,0 +1,256 @@
+"""Python binding of libtwd, the gfx950 W2A8 ternary linear library.
+
+Argument marshalling only: every step runs in the C/HIP library
+(``libtwd.so``, built in-tree by ``build.py``).  PyTorch supplies device
+memory and the current HIP stream.  Importing this package without the built
+library raises ``ImportError`` -- there is no fallback implementation.
+
+Names follow the C ABI in ``include/twd.h``: ``quantize_act``,
+``ternary_linear``, ``ternary_linear_fused``, ``pack_ternary``,
+``unpack_ternary``, ``ternarize_absmean``, ``select_kernel``,
+``stream_read``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtwd.so")
+
+TWD_OK = 0
+KERNEL_AUTO, KERNEL_DOT, KERNEL_MFMA = 0, 1, 2
+KERNEL_NAMES = {KERNEL_DOT: "dot", KERNEL_MFMA: "mfma"}
+MAX_M, MAX_K, MAX_SEGMENTS = 16, 8192, 4
+_STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "BAD_CODE", 4: "HIP"}
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; "
+        "g.build()'` (hipcc --offload-arch=gfx950)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_p, _i64, _int, _f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+
+
+def _sig(name, args, res=ctypes.c_int):
+    f = getattr(_lib, name)
+    f.argtypes = args
+    f.restype = res
+    return f
+
+
+_lib_version = _sig("twd_version", [], ctypes.c_char_p)
+_lib_last_error = _sig("twd_last_error", [], ctypes.c_char_p)
+_lib_ternarize = _sig("twd_ternarize_absmean", [_p, _i64, _i64, _p, _p])
+_lib_pack = _sig("twd_pack_ternary", [_p, _i64, _i64, _p])
+_lib_unpack = _sig("twd_unpack_ternary", [_p, _i64, _i64, _p])
+_lib_quantize = _sig("twd_quantize_act", [_p, _i64, _i64, _p, _p, _p])
+_lib_linear = _sig("twd_ternary_linear", [_p, _f32, _p, _p, _i64, _i64, _i64, _p, _p, _p])
+_lib_fused = _sig("twd_ternary_linear_fused",
+                  [_p, _int, _p, _p, _p, _p, _i64, _i64, _p, _p, _p])
+_lib_fused_kernel = _sig("twd_ternary_linear_fused_kernel",
+                         [_p, _int, _p, _p, _p, _p, _i64, _i64, _p, _p, _int, _p])
+_lib_select = _sig("twd_select_kernel", [_i64, _i64, _i64])
+_lib_stream_read = _sig("twd_stream_read", [_p, _i64, _p, _p])
+
+EXPORTS = ("twd_version", "twd_last_error", "twd_ternarize_absmean",
+           "twd_pack_ternary", "twd_unpack_ternary", "twd_quantize_act",
+           "twd_ternary_linear", "twd_ternary_linear_fused",
+           "twd_ternary_linear_fused_kernel", "twd_select_kernel",
+           "twd_stream_read")
+
+
+class TwdError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"twd {_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def _check(status: int):
+    if status != TWD_OK:
+        raise TwdError(status, _lib_last_error().decode(errors="replace"))
+
+
+def version() -> str:
+    return _lib_version().decode()
+
+
+# ----------------------------------------------------------------- host side
+
+def _np_ptr(a: np.ndarray):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def ternarize_absmean(W: np.ndarray):
+    """Absmean ternarization of one fp32 tensor [N, K] -> (int8 codes, gamma)."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    N, K = W.shape
+    codes = np.empty((N, K), np.int8)
+    g = np.zeros(1, np.float32)
+    _check(_lib_ternarize(_np_ptr(W), N, K, _np_ptr(codes), _np_ptr(g)))
+    return codes, float(g[0])
+
+
+def pack_ternary(codes: np.ndarray) -> np.ndarray:
+    """int8 codes [N, K] in {-1, 0, 1} -> packed uint8 [N, K/4]."""
+    codes = np.ascontiguousarray(codes, dtype=np.int8)
+    N, K = codes.shape
+    out = np.empty((N, K // 4), np.uint8)
+    _check(_lib_pack(_np_ptr(codes), N, K, _np_ptr(out)))
+    return out
+
+
+def unpack_ternary(packed: np.ndarray, N: int, K: int) -> np.ndarray:
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    if packed.size != N * K // 4:
+        raise ValueError("packed size does not match N*K/4")
+    codes = np.empty((N, K), np.int8)
+    _check(_lib_unpack(_np_ptr(packed), N, K, _np_ptr(codes)))
+    return codes
+
+
+def prepare_weights(W: np.ndarray, seg_rows=None):
+    """Offline weight preparation of a (fused) projection: each row segment
+    is ternarized with its own gamma, then the whole matrix is packed.
+    Returns (packed uint8 [N, K/4], [gamma per segment])."""
+    N, K = W.shape
+    seg_rows = tuple(seg_rows) if seg_rows is not None else (N,)
+    if sum(seg_rows) != N:
+        raise ValueError("segments do not cover N")
+    codes = np.empty((N, K), np.int8)
+    gammas = []
+    r0 = 0
+    for rows in seg_rows:
+        c, g = ternarize_absmean(W[r0:r0 + rows])
+        codes[r0:r0 + rows] = c
+        gammas.append(g)
+        r0 += rows
+    return pack_ternary(codes), gammas
+
+
+# --------------------------------------------------------------- device side
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev_ptr(t, name, dtypes=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def quantize_act(x, xq=None, xscale=None, stream=None):
+    """Per-token absmax int8 quantization of a bf16 [M, K] device tensor.
+    Returns (xq int8 [M, K], xscale fp32 [M])."""
+    torch = _torch()
+    _need(x.dim() == 2, "x must be [M, K]")
+    M, K = x.shape
+    _need(xq is None or tuple(xq.shape) == (M, K), "xq must be [M, K]")
+    _need(xscale is None or xscale.numel() >= M, "xscale must hold M values")
+    if xq is None:
+        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if xscale is None:
+        xscale = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _check(_lib_quantize(_dev_ptr(x, "x", (torch.bfloat16, torch.int16)), M, K,
+                         _dev_ptr(xq, "xq", (torch.int8,)),
+                         _dev_ptr(xscale, "xscale", (torch.float32,)),
+                         _stream(stream)))
+    return xq, xscale
+
+
+def _outputs(M, N, device, acc, y, want_acc, want_y):
+    torch = _torch()
+    _need(acc is None or tuple(acc.shape) == (M, N), "acc must be [M, N]")
+    _need(y is None or tuple(y.shape) == (M, N), "y must be [M, N]")
+    if acc is None and want_acc:
+        acc = torch.empty((M, N), dtype=torch.int32, device=device)
+    if y is None and want_y:
+        y = torch.empty((M, N), dtype=torch.float32, device=device)
+    return acc, y
+
+
+def ternary_linear(wpacked, gamma, xq, xscale, N, acc=None, y=None,
+                   want_acc=True, want_y=True, stream=None):
+    """acc = xq . t^T (int32), y = acc * xscale[m] * gamma (fp32).
+    wpacked: uint8 device tensor of N*K/4 bytes.  Returns (acc, y)."""
+    torch = _torch()
+    _need(xq.dim() == 2, "xq must be [M, K]")
+    M, K = xq.shape
+    _need(_nbytes(wpacked) >= N * K // 4, "wpacked holds fewer than N*K/4 bytes")
+    _need(xscale.numel() >= M, "xscale must hold M values")
+    acc, y = _outputs(M, N, xq.device, acc, y, want_acc, want_y)
+    _check(_lib_linear(_dev_ptr(wpacked, "wpacked", (torch.uint8,)), float(gamma),
+                       _dev_ptr(xq, "xq", (torch.int8,)),
+                       _dev_ptr(xscale, "xscale", (torch.float32,)), M, K, N,
+                       _dev_ptr(acc, "acc", (torch.int32,)),
+                       _dev_ptr(y, "y", (torch.float32,)), _stream(stream)))
+    return acc, y
+
+
+def ternary_linear_fused(wpacked, seg_rows, seg_gamma, xq, xscale, acc=None,
+                         y=None, want_acc=True, want_y=True, kernel=KERNEL_AUTO,
+                         stream=None):
+    """One launch over concatenated row segments (fused Q/K/V or gate/up),
+    each dequantized with its own gamma.  Returns (acc, y)."""
+    torch = _torch()
+    _need(xq.dim() == 2, "xq must be [M, K]")
+    M, K = xq.shape
+    seg_rows = [int(r) for r in seg_rows]
+    nseg = len(seg_rows)
+    _need(len(seg_gamma) == nseg, "one gamma per segment")
+    N = int(sum(seg_rows))
+    _need(_nbytes(wpacked) >= N * K // 4, "wpacked holds fewer than N*K/4 bytes")
+    _need(xscale.numel() >= M, "xscale must hold M values")
+    rows = (ctypes.c_int64 * max(nseg, 1))(*seg_rows)
+    gam = (ctypes.c_float * max(nseg, 1))(*[float(g) for g in seg_gamma])
+    acc, y = _outputs(M, N, xq.device, acc, y, want_acc, want_y)
+    args = (_dev_ptr(wpacked, "wpacked", (torch.uint8,)), nseg, rows, gam,
+            _dev_ptr(xq, "xq", (torch.int8,)),
+            _dev_ptr(xscale, "xscale", (torch.float32,)), M, K,
+            _dev_ptr(acc, "acc", (torch.int32,)), _dev_ptr(y, "y", (torch.float32,)))
+    if kernel == KERNEL_AUTO:
+        _check(_lib_fused(*args, _stream(stream)))
+    else:
+        _check(_lib_fused_kernel(*args, int(kernel), _stream(stream)))
+    return acc, y
+
+
+def select_kernel(M: int, K: int, N: int) -> int:
+    """Kernel family the width dispatch picks (KERNEL_DOT / KERNEL_MFMA),
+    or -1 for an unsupported shape."""
+    return int(_lib_select(M, K, N))
+
+
+def stream_read(buf, nbytes: int, sink, stream=None):
+    """Launch the plain streaming-read reference kernel over nbytes of buf."""
+    _need(_nbytes(buf) >= nbytes, "buf smaller than nbytes")
+    _need(_nbytes(sink) >= 1024, "sink needs 1024 bytes")
+    _check(_lib_stream_read(_dev_ptr(buf, "buf"), int(nbytes), _dev_ptr(sink, "sink"),
+                            _stream(stream)))

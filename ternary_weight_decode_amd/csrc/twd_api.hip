@@ -1,0 +1,186 @@
+// C-ABI entry points: argument checks, the width dispatch, launches.
+// Nothing here allocates, synchronizes or reads device memory, so every
+// device call can be recorded into a HIP graph.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "twd_internal.h"
+
+namespace twd {
+
+namespace {
+thread_local char g_error[512] = "";
+
+bool aligned(const void *p, uintptr_t a) {
+    return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
+
+twd_status hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess)
+        return TWD_OK;
+    return set_error(TWD_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxN = int64_t(1) << 30;
+
+// Shared checks of the linear entry points; fills segs and N.
+twd_status check_linear(const uint8_t *wpacked, int nseg,
+                        const int64_t *seg_rows, const float *seg_gamma,
+                        const int8_t *xq, const float *xscale, int64_t M,
+                        int64_t K, const int32_t *acc, const float *y,
+                        Segments *segs, int64_t *N_out) {
+    if (nseg < 1 || nseg > TWD_MAX_SEGMENTS)
+        return set_error(TWD_ERR_INVALID_ARG, "linear: nseg=%d outside 1..%d",
+                         nseg, TWD_MAX_SEGMENTS);
+    if (!seg_rows || !seg_gamma)
+        return set_error(TWD_ERR_INVALID_ARG, "linear: null segment table");
+    int64_t N = 0;
+    segs->nseg = nseg;
+    for (int s = 0; s < TWD_MAX_SEGMENTS; ++s) {
+        segs->bound[s] = 0;
+        segs->gamma[s] = 0.0f;
+    }
+    for (int s = 0; s < nseg; ++s) {
+        if (seg_rows[s] < 0)
+            return set_error(TWD_ERR_INVALID_ARG, "linear: seg_rows[%d] < 0", s);
+        N += seg_rows[s];
+        if (N > kMaxN)
+            return set_error(TWD_ERR_UNSUPPORTED, "linear: N > 2^30");
+        segs->bound[s] = static_cast<int>(N);
+        segs->gamma[s] = seg_gamma[s];
+    }
+    *N_out = N;
+    if (M < 0 || M > TWD_MAX_M)
+        return set_error(TWD_ERR_UNSUPPORTED, "linear: M=%lld outside 0..%d",
+                         (long long)M, TWD_MAX_M);
+    if (K < 64 || K > TWD_MAX_K || K % 64 != 0)
+        return set_error(TWD_ERR_UNSUPPORTED,
+                         "linear: K=%lld must be a multiple of 64 in 64..%d",
+                         (long long)K, TWD_MAX_K);
+    if (M == 0 || N == 0)
+        return TWD_OK;
+    if (!wpacked || !xq || !xscale)
+        return set_error(TWD_ERR_INVALID_ARG, "linear: null input pointer");
+    if (!acc && !y)
+        return set_error(TWD_ERR_INVALID_ARG, "linear: acc and y are both NULL");
+    if (!aligned(wpacked, 16) || !aligned(xq, 16))
+        return set_error(TWD_ERR_INVALID_ARG,
+                         "linear: wpacked and xq must be 16-byte aligned");
+    if (!aligned(xscale, 4) || (acc && !aligned(acc, 4)) || (y && !aligned(y, 4)))
+        return set_error(TWD_ERR_INVALID_ARG,
+                         "linear: xscale, acc and y must be 4-byte aligned");
+    return TWD_OK;
+}
+
+}  // namespace
+
+twd_status set_error(twd_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_error, sizeof g_error, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+}  // namespace twd
+
+using namespace twd;
+
+extern "C" const char *twd_version(void) { return "twd 0.1.0 (gfx950)"; }
+
+extern "C" const char *twd_last_error(void) { return g_error; }
+
+extern "C" twd_status twd_quantize_act(const uint16_t *x_bf16, int64_t M,
+                                       int64_t K, int8_t *xq, float *xscale,
+                                       void *stream) {
+    if (M < 0)
+        return set_error(TWD_ERR_INVALID_ARG, "quantize_act: M < 0");
+    if (K < 8 || K > 65536 || K % 8 != 0)
+        return set_error(TWD_ERR_UNSUPPORTED,
+                         "quantize_act: K=%lld must be a multiple of 8 in 8..65536",
+                         (long long)K);
+    if (M > 65535)
+        return set_error(TWD_ERR_UNSUPPORTED, "quantize_act: M > 65535");
+    if (M == 0)
+        return TWD_OK;
+    if (!x_bf16 || !xq || !xscale)
+        return set_error(TWD_ERR_INVALID_ARG, "quantize_act: null pointer");
+    if (!aligned(x_bf16, 16) || !aligned(xq, 16) || !aligned(xscale, 4))
+        return set_error(TWD_ERR_INVALID_ARG,
+                         "quantize_act: x and xq must be 16-byte aligned");
+    return hip_status(launch_quantize_act(x_bf16, static_cast<int>(M),
+                                          static_cast<int>(K), xq, xscale,
+                                          as_stream(stream)),
+                      "quantize_act launch");
+}
+
+extern "C" twd_status twd_ternary_linear_fused_kernel(
+    const uint8_t *wpacked, int nseg, const int64_t *seg_rows,
+    const float *seg_gamma, const int8_t *xq, const float *xscale, int64_t M,
+    int64_t K, int32_t *acc, float *y, int kernel, void *stream) {
+    if (kernel != TWD_KERNEL_AUTO && kernel != TWD_KERNEL_DOT &&
+        kernel != TWD_KERNEL_MFMA)
+        return set_error(TWD_ERR_INVALID_ARG, "linear: unknown kernel %d", kernel);
+    Segments segs;
+    int64_t N = 0;
+    twd_status st = check_linear(wpacked, nseg, seg_rows, seg_gamma, xq, xscale,
+                                 M, K, acc, y, &segs, &N);
+    if (st != TWD_OK || M == 0 || N == 0)
+        return st;
+    if (kernel == TWD_KERNEL_DOT && M > 8)
+        return set_error(TWD_ERR_UNSUPPORTED, "linear: the dot kernel takes M <= 8");
+    const LinearPlan plan = plan_linear(static_cast<int>(M), static_cast<int>(K),
+                                        static_cast<int>(N), kernel);
+    return hip_status(launch_linear(plan, wpacked, xq, xscale, static_cast<int>(M),
+                                    static_cast<int>(K), static_cast<int>(N),
+                                    segs, acc, y, as_stream(stream)),
+                      "linear launch");
+}
+
+extern "C" twd_status twd_ternary_linear_fused(
+    const uint8_t *wpacked, int nseg, const int64_t *seg_rows,
+    const float *seg_gamma, const int8_t *xq, const float *xscale, int64_t M,
+    int64_t K, int32_t *acc, float *y, void *stream) {
+    return twd_ternary_linear_fused_kernel(wpacked, nseg, seg_rows, seg_gamma,
+                                           xq, xscale, M, K, acc, y,
+                                           TWD_KERNEL_AUTO, stream);
+}
+
+extern "C" twd_status twd_ternary_linear(const uint8_t *wpacked, float gamma,
+                                         const int8_t *xq, const float *xscale,
+                                         int64_t M, int64_t K, int64_t N,
+                                         int32_t *acc, float *y, void *stream) {
+    if (N < 0)
+        return set_error(TWD_ERR_INVALID_ARG, "linear: N < 0");
+    const int64_t rows[1] = {N};
+    const float gam[1] = {gamma};
+    return twd_ternary_linear_fused_kernel(wpacked, 1, rows, gam, xq, xscale, M,
+                                           K, acc, y, TWD_KERNEL_AUTO, stream);
+}
+
+extern "C" int twd_select_kernel(int64_t M, int64_t K, int64_t N) {
+    if (M < 1 || M > TWD_MAX_M || K < 64 || K > TWD_MAX_K || K % 64 != 0 ||
+        N < 1 || N > kMaxN)
+        return -1;
+    return plan_linear(static_cast<int>(M), static_cast<int>(K),
+                       static_cast<int>(N), TWD_KERNEL_AUTO)
+        .kernel;
+}
+
+extern "C" twd_status twd_stream_read(const void *buf, int64_t bytes,
+                                      uint32_t *sink, void *stream) {
+    if (bytes < 0 || bytes % 16 != 0)
+        return set_error(TWD_ERR_INVALID_ARG,
+                         "stream_read: bytes must be a non-negative multiple of 16");
+    if (bytes == 0)
+        return TWD_OK;
+    if (!buf || !sink || !aligned(buf, 16))
+        return set_error(TWD_ERR_INVALID_ARG, "stream_read: bad pointer");
+    if (bytes / 16 / 1024 >= (int64_t(1) << 31))
+        return set_error(TWD_ERR_UNSUPPORTED, "stream_read: too large");
+    return hip_status(launch_stream_read(buf, bytes, sink, as_stream(stream)),
+                      "stream_read launch");
+}

@@ -1,0 +1,43 @@
+// Internal declarations shared by the C-ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "twd.h"
+
+namespace twd {
+
+// Per-launch description of the fused row segments.  bound[s] is the first
+// row after segment s (cumulative), gamma[s] its weight scale.  Passed by
+// value as a kernel argument.
+struct Segments {
+    int nseg;
+    int bound[TWD_MAX_SEGMENTS];
+    float gamma[TWD_MAX_SEGMENTS];
+};
+
+// Launch parameters the width dispatch chose for one linear call.
+struct LinearPlan {
+    int kernel;       // TWD_KERNEL_DOT or TWD_KERNEL_MFMA
+    int tiles;        // 16-row tiles per workgroup
+    int64_t grid;     // workgroups
+};
+
+// Thread-local error message; returns `st` for convenient chaining.
+twd_status set_error(twd_status st, const char *fmt, ...);
+
+LinearPlan plan_linear(int M, int K, int N, int forced_kernel);
+
+hipError_t launch_quantize_act(const uint16_t *x, int M, int K, int8_t *xq,
+                               float *xscale, hipStream_t stream);
+
+hipError_t launch_linear(const LinearPlan &plan, const uint8_t *w,
+                         const int8_t *xq, const float *xscale, int M, int K,
+                         int N, const Segments &segs, int32_t *acc, float *y,
+                         hipStream_t stream);
+
+hipError_t launch_stream_read(const void *buf, int64_t bytes, uint32_t *sink,
+                              hipStream_t stream);
+
+}  // namespace twd

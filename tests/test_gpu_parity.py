@@ -1,0 +1,279 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: quantized activations, scales and int32 accumulators bit-exact; fp32
+outputs within 1e-6 relative of the oracle's double-precision value, per
+element.  Cases span several 16-row tiles, partial 256-wide K slices and
+ragged N tails, every width M = 1..16 for the matrix-core kernel and 1..8 for
+the VALU kernel, fused segments, the single-linear workload and full-size
+2B / 4B projections.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+REL_TOL = 1e-6
+
+
+@pytest.fixture(scope="module")
+def env():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import oracle
+    import ternary_weight_decode_amd as twd
+    oracle.build(force=False)
+    return torch, twd, oracle
+
+
+def log(msg):
+    sys.stdout.write(msg + "\n")
+    sys.stdout.flush()
+
+
+def to_dev_bf16(torch, x_bits):
+    return torch.from_numpy(x_bits.view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def check_y(y, yref):
+    y = np.asarray(y, dtype=np.float64)
+    err = np.abs(y - yref)
+    bad = err > REL_TOL * np.abs(yref)
+    assert not bad.any(), f"{bad.sum()} y values outside 1e-6 relative, worst {err[bad].max()}"
+
+
+_prep_cache = {}
+
+
+def prepared(twd, torch, W, segs, key):
+    if key not in _prep_cache:
+        packed, gammas = twd.prepare_weights(W, segs)
+        _prep_cache.clear()
+        _prep_cache[key] = (torch.from_numpy(packed).cuda(), gammas)
+    return _prep_cache[key]
+
+
+def run_case(env, W, segs, x, kernel, key, ref=None):
+    torch, twd, orc = env
+    wp, gammas = prepared(twd, torch, W, segs, key)
+    M, K = x.shape
+    log(f"case {key} M={M} K={K} N={W.shape[0]} segs={segs} kernel={kernel}")
+    xq, xs = twd.quantize_act(to_dev_bf16(torch, x))
+    acc, y = twd.ternary_linear_fused(wp, segs, gammas, xq, xs, kernel=kernel)
+    torch.cuda.synchronize()
+    if ref is None:
+        ref = orc.forward(W, segs, x)
+    assert gammas == ref["gammas"]
+    np.testing.assert_array_equal(xq.cpu().numpy(), ref["q"])
+    np.testing.assert_array_equal(xs.cpu().numpy().view(np.uint32),
+                                  ref["scale"].view(np.uint32))
+    np.testing.assert_array_equal(acc.cpu().numpy(), ref["acc"])
+    check_y(y.cpu().numpy(), ref["y"])
+    return acc, y
+
+
+# ------------------------------------------------------------ quantize_act
+
+@pytest.mark.parametrize("M,K", [(1, 256), (3, 2560), (16, 6912), (16, 8192), (2, 8),
+                                 (5, 65536), (300, 64)])
+def test_quantize_act_bit_exact(env, M, K):
+    torch, twd, orc = env
+    rng = np.random.default_rng([M, K])
+    xf = rng.standard_normal((M, K), dtype=np.float32)
+    if M > 2:
+        xf[1] = 0.0                       # all-zero row
+        xf[2, :: max(K // 50, 1)] *= 20  # outlier channels
+    x = wl.f32_to_bf16_bits(xf)
+    log(f"quantize M={M} K={K}")
+    xq, xs = twd.quantize_act(to_dev_bf16(torch, x))
+    torch.cuda.synchronize()
+    q, s = orc.quantize_act(x)
+    np.testing.assert_array_equal(xq.cpu().numpy(), q)
+    np.testing.assert_array_equal(xs.cpu().numpy().view(np.uint32), s.view(np.uint32))
+
+
+def test_quantize_act_ties(env):
+    torch, twd, orc = env
+    row = np.zeros((1, 64), np.float32)
+    row[0, :6] = [127, 62.5, -62.5, 0.5, 1.5, 2.5]
+    x = wl.f32_to_bf16_bits(row)
+    xq, xs = twd.quantize_act(to_dev_bf16(torch, x))
+    torch.cuda.synchronize()
+    assert xq.cpu().numpy()[0, :6].tolist() == [127, 62, -62, 0, 2, 2]
+    assert float(xs.cpu()[0]) == 1.0
+
+
+# ------------------------------------------------------------------- linear
+
+SMALL_SHAPES = [
+    (64, (1,)),           # one partial super chunk, one row
+    (320, (17,)),         # partial last super chunk, ragged tile
+    (2560, (130,)),       # ten full super chunks, ragged tail
+    (1536, (64, 33, 33)),  # three segments, ragged
+    (768, (50, 50)),      # two segments
+]
+
+
+@pytest.mark.parametrize("K,segs", SMALL_SHAPES)
+@pytest.mark.parametrize("M", list(range(1, 17)))
+def test_mfma_kernel_parity(env, M, K, segs):
+    torch, twd, orc = env
+    W, segs, x = wl.random_case(seed=1, M=M, K=K, seg_rows=segs)
+    run_case(env, W, segs, x, twd.KERNEL_MFMA, ("rand", 1, K, segs))
+
+
+@pytest.mark.parametrize("K,segs", SMALL_SHAPES)
+@pytest.mark.parametrize("M", list(range(1, 9)))
+def test_dot_kernel_parity(env, M, K, segs):
+    torch, twd, orc = env
+    W, segs, x = wl.random_case(seed=1, M=M, K=K, seg_rows=segs)
+    run_case(env, W, segs, x, twd.KERNEL_DOT, ("rand", 1, K, segs))
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 5, 8, 16])
+def test_auto_dispatch_parity_and_determinism(env, M):
+    torch, twd, orc = env
+    W, segs, x = wl.random_case(seed=2, M=M, K=1024, seg_rows=(200,))
+    a1, y1 = run_case(env, W, segs, x, twd.KERNEL_AUTO, ("rand", 2, 1024, segs))
+    a2, y2 = run_case(env, W, segs, x, twd.KERNEL_AUTO, ("rand", 2, 1024, segs))
+    assert torch.equal(a1, a2) and torch.equal(y1, y2)
+
+
+def test_single_linear_workload(env):
+    """The single-linear case: M=1, K=256, N=512, seed 0."""
+    torch, twd, orc = env
+    W, segs, x = wl.single_case(seed=0)
+    for kernel in (twd.KERNEL_AUTO, twd.KERNEL_DOT, twd.KERNEL_MFMA):
+        run_case(env, W, segs, x, kernel, ("single", 0))
+
+
+def test_width_invariance(env):
+    """Row m of an M-wide call equals the 1-wide call on that row."""
+    torch, twd, orc = env
+    W, segs, x = wl.random_case(seed=3, M=16, K=2560, seg_rows=(96,))
+    wp, gammas = prepared(twd, torch, W, segs, ("rand", 3))
+    xq, xs = twd.quantize_act(to_dev_bf16(torch, x))
+    full = {}
+    for kernel in (twd.KERNEL_MFMA, twd.KERNEL_DOT):
+        for M in (16, 8, 4, 1) if kernel == twd.KERNEL_MFMA else (8, 4, 1):
+            acc, _ = twd.ternary_linear_fused(wp, segs, gammas, xq[:M].contiguous(),
+                                              xs[:M].contiguous(), kernel=kernel)
+            full[(kernel, M)] = acc
+    torch.cuda.synchronize()
+    ref = full[(twd.KERNEL_MFMA, 16)]
+    for (kernel, M), acc in full.items():
+        assert torch.equal(acc, ref[:M]), (kernel, M)
+
+
+def test_fused_equals_separate_calls(env):
+    torch, twd, orc = env
+    W, segs, x = wl.random_case(seed=4, M=4, K=512, seg_rows=(48, 16, 16))
+    wp, gammas = prepared(twd, torch, W, segs, ("rand", 4))
+    xq, xs = twd.quantize_act(to_dev_bf16(torch, x))
+    acc, y = twd.ternary_linear_fused(wp, segs, gammas, xq, xs)
+    r0 = 0
+    for rows, g in zip(segs, gammas):
+        part = wp.view(-1)[r0 * 512 // 4:(r0 + rows) * 512 // 4]
+        a2, y2 = twd.ternary_linear(part, g, xq, xs, rows)
+        torch.cuda.synchronize()
+        assert torch.equal(acc[:, r0:r0 + rows], a2)
+        assert torch.equal(y[:, r0:r0 + rows], y2)
+        r0 += rows
+
+
+def test_timing_mode_outputs_optional(env):
+    torch, twd, orc = env
+    W, segs, x = wl.random_case(seed=5, M=2, K=256, seg_rows=(40,))
+    wp, gammas = prepared(twd, torch, W, segs, ("rand", 5))
+    xq, xs = twd.quantize_act(to_dev_bf16(torch, x))
+    acc, y = twd.ternary_linear_fused(wp, segs, gammas, xq, xs)
+    a_only, none_y = twd.ternary_linear_fused(wp, segs, gammas, xq, xs, want_y=False)
+    none_a, y_only = twd.ternary_linear_fused(wp, segs, gammas, xq, xs, want_acc=False)
+    torch.cuda.synchronize()
+    assert none_y is None and none_a is None
+    assert torch.equal(acc, a_only) and torch.equal(y, y_only)
+
+
+def test_invariants_on_gpu(env):
+    """Zero weights give zero; an all-+1 row gives the activation row sum."""
+    torch, twd, orc = env
+    M, K, N = 3, 512, 20
+    x = wl.f32_to_bf16_bits(np.random.default_rng(6).standard_normal((M, K),
+                                                                     dtype=np.float32))
+    codes = np.zeros((N, K), np.int8)
+    codes[1] = 1
+    codes[2] = -1
+    wp = torch.from_numpy(twd.pack_ternary(codes)).cuda()
+    xq, xs = twd.quantize_act(to_dev_bf16(torch, x))
+    for kernel in (twd.KERNEL_DOT, twd.KERNEL_MFMA):
+        acc, y = twd.ternary_linear_fused(wp, (N,), (1.0,), xq, xs, kernel=kernel)
+        torch.cuda.synchronize()
+        a = acc.cpu().numpy()
+        rowsum = xq.cpu().numpy().astype(np.int64).sum(axis=1)
+        assert not a[:, 0].any() and not a[:, 3:].any()
+        np.testing.assert_array_equal(a[:, 1], rowsum)
+        np.testing.assert_array_equal(a[:, 2], -rowsum)
+        assert not y.cpu().numpy()[:, 0].any()
+
+
+def test_extreme_values(env):
+    """|acc| at its maximum: q = +-127 everywhere, every weight +-1, K = 8192."""
+    torch, twd, orc = env
+    M, K, N = 16, 8192, 32
+    xf = np.full((M, K), 1.0, np.float32)
+    xf[1::2] = -1.0
+    x = wl.f32_to_bf16_bits(xf)
+    W = np.ones((N, K), np.float32)
+    W[::3] = -1.0
+    for kernel in (twd.KERNEL_MFMA, twd.KERNEL_DOT):
+        xs_ = x if kernel == twd.KERNEL_MFMA else x[:8]
+        acc, _ = run_case(env, W, (N,), xs_, kernel, ("extreme",))
+        assert abs(int(acc.abs().max())) == 127 * K
+
+
+# ---------------------------------------------------------- full-size layers
+
+@pytest.mark.parametrize("set_name,workload,layer,M", [
+    ("2b", "2b_decode", 0, 1),
+    ("2b", "2b_decode", 29, 1),
+    ("2b", "2b_verify", 7, 4),
+    ("2b", "2b_verify", 7, 8),
+    ("2b", "2b_sweep_outlier", 3, 13),
+    ("4b", "4b_stack", 35, 1),
+    ("4b", "4b_stack", 0, 16),
+])
+def test_full_size_layer(env, set_name, workload, layer, M):
+    """Every projection of one full-size layer, in the dispatch the benchmark
+    times, compared element by element."""
+    torch, twd, orc = env
+    ls = wl.LAYER_SETS[set_name]
+    for pi, proj in enumerate(ls.projs):
+        W = wl.layer_weights(ls, layer, pi)
+        x = wl.layer_activations(workload, proj.K, M, layer, pi,
+                                 outliers=workload == "2b_sweep_outlier")
+        run_case(env, W, proj.segs, x, twd.KERNEL_AUTO, (set_name, layer, pi))
+
+
+# ------------------------------------------------------------- error paths
+
+def test_errors_on_gpu(env):
+    torch, twd, orc = env
+    xq = torch.zeros((17, 256), dtype=torch.int8, device="cuda")
+    xs = torch.ones(17, device="cuda")
+    wp = torch.zeros(64 * 64, dtype=torch.uint8, device="cuda")
+    with pytest.raises(twd.TwdError) as e:
+        twd.ternary_linear(wp, 1.0, xq, xs, 64)
+    assert e.value.status == 2
+    with pytest.raises(twd.TwdError) as e:
+        twd.ternary_linear(wp, 1.0, xq[:4, :100].contiguous(), xs[:4], 64)
+    assert e.value.status == 2
+    with pytest.raises(twd.TwdError) as e:
+        twd.ternary_linear(wp[1:], 1.0, xq[:4], xs[:4], 32)  # misaligned weights
+    assert e.value.status == 1
+    # empty width: no launch, outputs untouched
+    acc, y = twd.ternary_linear(wp, 1.0, xq[:0], xs[:0], 64)
+    assert acc.shape == (0, 64)

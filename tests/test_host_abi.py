@@ -1,0 +1,167 @@
+"""CPU tests of the C ABI: every symbol the header declares is exported, the
+host-side weight preparation matches the oracle bit for bit, and argument
+checks reject bad calls before anything is launched (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from conftest import ROOT, read_golden
+import workloads as wl
+
+
+@pytest.fixture(scope="module")
+def twd():
+    from ternary_weight_decode_amd import build as libbuild
+    if not os.path.exists(libbuild.LIB):
+        libbuild.build()
+    import ternary_weight_decode_amd as twd
+    return twd
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "twd.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(twd_\w+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(twd):
+    names = header_functions()
+    assert len(names) >= 10
+    lib = ctypes.CDLL(twd.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+    assert set(names) == set(twd.EXPORTS)
+
+
+def test_version(twd):
+    assert "gfx950" in twd.version()
+
+
+# ------------------------------------------------------------- pack / unpack
+
+@pytest.mark.parametrize("N,K", [(1, 16), (3, 64), (17, 256), (5, 2560), (2, 8192)])
+def test_pack_roundtrip_against_oracle_unpack(twd, orc, N, K):
+    rng = np.random.default_rng([N, K])
+    codes = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    packed = twd.pack_ternary(codes)
+    assert packed.shape == (N, K // 4)
+    np.testing.assert_array_equal(orc.unpack(packed, N, K), codes)
+    np.testing.assert_array_equal(twd.unpack_ternary(packed, N, K), codes)
+
+
+def test_pack_golden(twd):
+    g = read_golden("packed_word.txt")
+    codes = np.array([[int(v) for v in g["T"]]], np.int8)
+    assert twd.pack_ternary(codes)[0].tolist() == [int(v, 16) for v in g["BYTES"]]
+    h = read_golden("hand_case_k16.txt")
+    codes = np.array([[int(v) for v in h["T0"]], [int(v) for v in h["T1"]]], np.int8)
+    packed = twd.pack_ternary(codes)
+    assert packed[0].tolist() == [int(v, 16) for v in h["PACKED0"]]
+    assert packed[1].tolist() == [int(v, 16) for v in h["PACKED1"]]
+
+
+def test_pack_rejects_bad_codes(twd):
+    codes = np.zeros((2, 32), np.int8)
+    codes[1, 5] = 2
+    with pytest.raises(twd.TwdError) as e:
+        twd.pack_ternary(codes)
+    assert e.value.status == 3
+    with pytest.raises(twd.TwdError) as e:
+        twd.pack_ternary(np.zeros((2, 24), np.int8))
+    assert e.value.status == 1
+
+
+def test_unpack_rejects_code3_everywhere(twd):
+    base = twd.pack_ternary(np.zeros((1, 16), np.int8))
+    for byte in range(4):
+        for field in range(4):
+            p = base.copy()
+            p[0, byte] |= np.uint8(3 << (2 * field))
+            with pytest.raises(twd.TwdError) as e:
+                twd.unpack_ternary(p, 1, 16)
+            assert e.value.status == 3
+
+
+# ------------------------------------------------------------------ ternarize
+
+@pytest.mark.parametrize("shape,sigma", [((512, 256), 1.0), ((640, 2560), 0.02),
+                                         ((7, 48), 3.0), ((1, 16), 1.0)])
+def test_ternarize_bit_exact_vs_oracle(twd, orc, shape, sigma):
+    rng = np.random.default_rng(list(shape))
+    W = rng.standard_normal(shape, dtype=np.float32) * np.float32(sigma)
+    c1, g1 = twd.ternarize_absmean(W)
+    c2, g2 = orc.ternarize_absmean(W)
+    assert np.float32(g1).view(np.uint32) == np.float32(g2).view(np.uint32)
+    np.testing.assert_array_equal(c1, c2)
+
+
+def test_ternarize_ties_zero_and_nonfinite(twd):
+    c, g = twd.ternarize_absmean(np.array([[1, 7, 0, 0]], np.float32))
+    assert g == 2.0 and c.tolist() == [[0, 1, 0, 0]]
+    c, g = twd.ternarize_absmean(np.zeros((4, 16), np.float32))
+    assert g == 0.0 and not c.any()
+    W = np.ones((2, 16), np.float32)
+    W[0, 0] = np.nan
+    with pytest.raises(twd.TwdError):
+        twd.ternarize_absmean(W)
+
+
+def test_prepare_weights_segments_vs_oracle(twd, orc):
+    W = wl.layer_weights(wl.SET_2B, 0, 0)[:, :256]  # qkv segments, narrowed K
+    segs = wl.SET_2B.projs[0].segs
+    packed, gammas = twd.prepare_weights(W, segs)
+    t, og, _ = orc.ternarize_segments(W, segs)
+    assert gammas == og
+    np.testing.assert_array_equal(orc.unpack(packed, W.shape[0], W.shape[1]), t)
+
+
+# ---------------------------------------------------- argument checks (no GPU)
+
+def _fused(twd, wp=0x1000, nseg=1, rows=(64,), gam=(1.0,), xq=0x2000, xs=0x3000,
+           M=1, K=256, acc=0x4000, y=0x5000, kernel=0):
+    r = (ctypes.c_int64 * 4)(*rows)
+    g = (ctypes.c_float * 4)(*gam)
+    return twd._lib_fused_kernel(wp, nseg, r, g, xq, xs, M, K, acc, y, kernel, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=17), 2), (dict(M=-1), 2), (dict(K=100), 2), (dict(K=0), 2),
+    (dict(K=8256), 2), (dict(nseg=0), 1), (dict(nseg=5), 1),
+    (dict(rows=(-1,)), 1), (dict(wp=None), 1), (dict(xq=None), 1),
+    (dict(xs=None), 1), (dict(acc=None, y=None), 1), (dict(wp=0x1008), 1),
+    (dict(xq=0x2004), 1), (dict(y=0x5002), 1), (dict(kernel=7), 1),
+    (dict(kernel=1, M=9), 2),
+])
+def test_linear_rejects_before_launch(twd, kw, status):
+    assert _fused(twd, **kw) == status
+    assert twd._lib_last_error()
+
+
+def test_linear_empty_is_noop(twd):
+    # M == 0 or N == 0: nothing to compute, nothing launched, even with
+    # placeholder pointers
+    assert _fused(twd, M=0) == 0
+    assert _fused(twd, rows=(0,)) == 0
+
+
+def test_quantize_rejects_before_launch(twd):
+    q = twd._lib_quantize
+    assert q(0x1000, 1, 12, 0x2000, 0x3000, None) == 2       # K % 8
+    assert q(0x1000, 1, 0, 0x2000, 0x3000, None) == 2        # K == 0
+    assert q(0x1000, -1, 64, 0x2000, 0x3000, None) == 1      # M < 0
+    assert q(None, 1, 64, 0x2000, 0x3000, None) == 1         # null
+    assert q(0x1008, 1, 64, 0x2000, 0x3000, None) == 1       # alignment
+    assert q(0x1000, 0, 64, None, None, None) == 0           # empty
+
+
+def test_select_kernel(twd):
+    assert twd.select_kernel(1, 2560, 2560) == twd.KERNEL_DOT
+    assert twd.select_kernel(16, 2560, 2560) == twd.KERNEL_MFMA
+    for M in range(1, 17):
+        assert twd.select_kernel(M, 2560, 13824) in (twd.KERNEL_DOT, twd.KERNEL_MFMA)
+    assert twd.select_kernel(17, 2560, 2560) == -1
+    assert twd.select_kernel(1, 100, 2560) == -1
+    assert twd.select_kernel(1, 2560, 0) == -1

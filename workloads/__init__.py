@@ -146,10 +146,11 @@ def layer_activations(workload: str, K: int, M: int, layer: int, proj_index: int
 def random_case(seed: int, M: int, K: int, seg_rows, w_sigma: float = 1.0,
                 x_sigma: float = 1.0):
     """A generic seeded case of any shape (parity tests over tile edges and
-    ragged tails)."""
-    rng = np.random.default_rng([77, seed, M, K, len(seg_rows)])
-    W = (rng.standard_normal((int(sum(seg_rows)), K), dtype=np.float32)
-         * np.float32(w_sigma))
+    ragged tails).  W depends on (seed, K, segments) only, x on (seed, M, K)."""
+    N = int(sum(seg_rows))
+    rng = np.random.default_rng([77, seed, K, N, len(seg_rows)])
+    W = rng.standard_normal((N, K), dtype=np.float32) * np.float32(w_sigma)
+    rng = np.random.default_rng([78, seed, M, K])
     x = rng.standard_normal((M, K), dtype=np.float32) * np.float32(x_sigma)
     return W, tuple(seg_rows), f32_to_bf16_bits(x)
 
