@@ -1,0 +1,371 @@
+#!/usr/bin/env python3
+"""Benchmark of the W2A8 ternary linear hot path on one MI355X.
+
+A step is one pass of the whole hot path over the 2B-class decode layer set
+(30 layers x {fused QKV 2560->3840, O 2560->2560, fused gate/up
+2560->13824, down 6912->2560}) at width M: per projection, the per-token
+int8 quantization of a fresh bf16 activation block followed by the fused
+ternary linear with its dequant epilogue.  All weights (521 MB packed, more
+than the 256 MB Infinity Cache, so every projection streams cold weights)
+and activations are resident in HBM before timing starts.  The step is
+recorded once into a HIP graph and replayed.
+
+Output: one JSON line.  `value` is packed-weight bytes per second over the
+timed steps (wall clock between two synchronizations).  `roofline` rates the
+dominant kernel -- the ternary linear -- from two events around
+back-to-back replays of a graph holding only its launches (average launch
+duration = elapsed / launches), against MI355X's 8 TB/s HBM peak.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same work.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads as wl  # noqa: E402
+
+METRIC = "ternary_linear weight-stream GB/s and % HBM roofline at M=1,2,4,8,16"
+HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def host_threads():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+class LayerSetOnDevice:
+    """Packed weights of every projection, uploaded once."""
+
+    def __init__(self, twd, torch, ls, layers):
+        self.ls = ls
+        self.layers = layers
+        self.w = {}
+        self.gammas = {}
+
+        def prep(key):
+            layer, pi = key
+            W = wl.layer_weights(ls, layer, pi)
+            return key, twd.prepare_weights(W, ls.projs[pi].segs)
+
+        keys = [(l, p) for l in range(layers) for p in range(len(ls.projs))]
+        with ThreadPoolExecutor(max_workers=host_threads()) as ex:
+            for (layer, pi), (packed, gammas) in ex.map(prep, keys):
+                self.w[(layer, pi)] = torch.from_numpy(packed).cuda()
+                self.gammas[(layer, pi)] = gammas
+        torch.cuda.synchronize()
+
+    @property
+    def bytes_per_sweep(self):
+        return self.layers * self.ls.packed_bytes_per_layer
+
+
+class Step:
+    """Inputs, outputs and launches of one step at width M."""
+
+    def __init__(self, twd, torch, dev_set, workload, M, kernel, outliers=False):
+        self.twd, self.torch, self.ds = twd, torch, dev_set
+        self.M, self.kernel = M, kernel
+        ls = dev_set.ls
+        self.x, self.xq, self.xs, self.y = {}, {}, {}, {}
+        for layer in range(dev_set.layers):
+            for pi, p in enumerate(ls.projs):
+                xb = wl.layer_activations(workload, p.K, M, layer, pi, outliers=outliers)
+                self.x[(layer, pi)] = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16)
+                self.xq[(layer, pi)] = torch.empty((M, p.K), dtype=torch.int8, device="cuda")
+                self.xs[(layer, pi)] = torch.empty((M,), dtype=torch.float32, device="cuda")
+                self.y[(layer, pi)] = torch.empty((M, p.N), dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+
+    def keys(self):
+        return [(l, p) for l in range(self.ds.layers) for p in range(len(self.ds.ls.projs))]
+
+    def quantize(self, key):
+        self.twd.quantize_act(self.x[key], self.xq[key], self.xs[key])
+
+    def linear(self, key):
+        p = self.ds.ls.projs[key[1]]
+        self.twd.ternary_linear_fused(self.ds.w[key], p.segs, self.ds.gammas[key],
+                                      self.xq[key], self.xs[key], y=self.y[key],
+                                      want_acc=False, kernel=self.kernel)
+
+    def full(self):
+        for k in self.keys():
+            self.quantize(k)
+            self.linear(k)
+
+    def linear_only(self):
+        for k in self.keys():
+            self.linear(k)
+
+    def quantize_only(self):
+        for k in self.keys():
+            self.quantize(k)
+
+
+def capture(torch, fn):
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # eager warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_replays(torch, g, reps):
+    """Wall seconds and event seconds for `reps` back-to-back replays."""
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(reps):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return t1 - t0, start.elapsed_time(end) * 1e-3
+
+
+def stream_read_reference(twd, torch, dev_set, reps):
+    """The plain streaming-read kernel over each projection's weight buffer,
+    launched back to back in the same order as the linear sweep."""
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+    keys = [(l, p) for l in range(dev_set.layers) for p in range(len(dev_set.ls.projs))]
+
+    def sweep():
+        for k in keys:
+            w = dev_set.w[k]
+            twd.stream_read(w, w.numel(), sink)
+
+    g = capture(torch, sweep)
+    g.replay()
+    _, sec = time_replays(torch, g, reps)
+    return dev_set.bytes_per_sweep * reps / sec / 1e9, sec / (reps * len(keys))
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "ternary_weight_decode_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(workload, M, launches_bytes):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel sources; else None."""
+    path = os.path.join(PROFILES, f"ternary_linear_counters_{workload}_m{M}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(ls, workload, M, outliers, budget_s):
+    """The CPU oracle (quantize, int8 x ternary loops, dequant) on the layers
+    of the set, in order, until its compute time passes budget_s; timed on
+    the host's cores.  Setup (weight generation and the oracle's own
+    ternarization, a few layers ahead in a thread pool) is not timed."""
+    import oracle
+    oracle.build(force=False)
+    threads = host_threads()
+
+    def prep(key):
+        layer, pi = key
+        p = ls.projs[pi]
+        W = wl.layer_weights(ls, layer, pi)
+        t, _, grow = oracle.ternarize_segments(W, p.segs)
+        x = wl.layer_activations(workload, p.K, M, layer, pi, outliers=outliers)
+        return p, t, grow, x
+
+    done_bytes, spent, layers = 0, 0.0, 0
+    keys = [(l, p) for l in range(ls.layers) for p in range(len(ls.projs))]
+    chunk = 4 * len(ls.projs)
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        for c0 in range(0, len(keys), chunk):
+            for p, t, grow, x in ex.map(prep, keys[c0:c0 + chunk]):
+                t0 = time.perf_counter()
+                q, s = oracle.quantize_act(x)
+                acc = oracle.linear(q, t, threads)
+                oracle.dequant(acc, s, grow)
+                spent += time.perf_counter() - t0
+                done_bytes += p.packed_bytes
+            layers = min(ls.layers, (c0 + chunk) // len(ls.projs))
+            if spent >= budget_s:
+                break
+    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{layers} of {ls.layers} layers of the {ls.name.upper()} set at M={M} "
+                      f"(all 4 projections each: quantize + int32 contraction + dequant; "
+                      f"{spent:.2f} s of CPU time; throughput in packed-weight bytes/s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="2b_decode",
+                    choices=["2b_decode", "2b_verify", "2b_sweep_outlier", "4b_stack"])
+    ap.add_argument("--M", type=int, default=None, help="width (default: the workload's first)")
+    ap.add_argument("--kernel", default="auto", choices=["auto", "dot", "mfma"])
+    ap.add_argument("--widths", default="1,2,4,8,16",
+                    help="widths for the per-width linear table ('' to skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="CPU oracle budget (0 skips the CPU baseline)")
+    ap.add_argument("--check", action="store_true", default=True)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the "
+              "ternary linear is measured on a single MI355X; the multi-GPU sharding is a "
+              "design note, not a measured path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import ternary_weight_decode_amd as twd
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    kernel = {"auto": twd.KERNEL_AUTO, "dot": twd.KERNEL_DOT, "mfma": twd.KERNEL_MFMA}[args.kernel]
+    set_name = "4b" if args.workload.startswith("4b") else "2b"
+    ls = wl.LAYER_SETS[set_name]
+    M = args.M or wl.workload_widths(args.workload)[0]
+    outliers = args.workload == "2b_sweep_outlier"
+
+    t_setup = time.perf_counter()
+    dev_set = LayerSetOnDevice(twd, torch, ls, ls.layers)
+    log(f"weights ready: {dev_set.bytes_per_sweep / 1e6:.1f} MB packed in "
+        f"{time.perf_counter() - t_setup:.1f} s")
+
+    step = Step(twd, torch, dev_set, args.workload, M, kernel, outliers)
+    nlaunch = len(step.keys())
+    g_full = capture(torch, step.full)
+    g_lin = capture(torch, step.linear_only)
+    g_q = capture(torch, step.quantize_only)
+
+    # graph replays must equal eager results (every replay is checked)
+    if args.check:
+        step.full()
+        torch.cuda.synchronize()
+        eager = {k: v.clone() for k, v in step.y.items()}
+        for _ in range(2):
+            for v in step.y.values():
+                v.zero_()
+            g_full.replay()
+            torch.cuda.synchronize()
+            for k in step.keys():
+                if not torch.equal(step.y[k], eager[k]):
+                    raise SystemExit(f"graph replay differs from eager at {k}")
+
+    for _ in range(args.warmup):
+        g_full.replay()
+    wall, _ = time_replays(torch, g_full, args.steps)
+    bytes_step = dev_set.bytes_per_sweep
+    value = bytes_step * args.steps / wall / 1e9
+
+    # dominant kernel: the ternary linear alone, back-to-back launches
+    reps = max(args.steps, 20)
+    g_lin.replay()
+    _, lin_sec = time_replays(torch, g_lin, reps)
+    lin_dur = lin_sec / (reps * nlaunch)
+    lin_gbs = bytes_step * reps / lin_sec / 1e9
+    g_q.replay()
+    _, q_sec = time_replays(torch, g_q, reps)
+    ref_gbs, ref_dur = stream_read_reference(twd, torch, dev_set, reps)
+    traffic = counter_traffic(args.workload, M, bytes_step / nlaunch)
+    kname = twd.KERNEL_NAMES[twd.select_kernel(M, ls.hidden, ls.projs[2].N)] \
+        if kernel == twd.KERNEL_AUTO else args.kernel
+
+    widths = {}
+    if args.widths:
+        for Mw in [int(v) for v in args.widths.split(",") if v]:
+            st = step if Mw == M else Step(twd, torch, dev_set, args.workload, Mw, kernel, outliers)
+            g = g_lin if Mw == M else capture(torch, st.linear_only)
+            g.replay()
+            _, sec = time_replays(torch, g, max(10, args.steps // 2))
+            gbs = bytes_step * max(10, args.steps // 2) / sec / 1e9
+            widths[str(Mw)] = {"gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                               "us_per_launch": round(sec / (max(10, args.steps // 2) * nlaunch) * 1e6, 3),
+                               "kernel": twd.KERNEL_NAMES[twd.select_kernel(Mw, ls.hidden, ls.projs[2].N)]
+                               if kernel == twd.KERNEL_AUTO else args.kernel}
+            if st is not step:
+                del st, g
+                torch.cuda.empty_cache()
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(ls, args.workload, M, outliers, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic (seeded N(0,0.02) weights, absmean-ternarized; N(0,1) bf16 activations)",
+        "config": {
+            "workload": args.workload,
+            "layer_set": f"{ls.name.upper()}-class, hidden {ls.hidden}, {ls.layers} layers",
+            "M": M,
+            "packed_weight_bytes_per_step": bytes_step,
+            "launches_per_step": 2 * nlaunch,
+            "hip_graph": True,
+            "kernel": kname,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(lin_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(lin_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": f"ternary linear ({kname})",
+            "avg_launch_us": round(lin_dur * 1e6, 3),
+            "launches_timed": reps * nlaunch,
+        },
+        "stream_read_ref": {"gbs": round(ref_gbs, 1), "avg_launch_us": round(ref_dur * 1e6, 3),
+                            "linear_over_ref": round(lin_gbs / ref_gbs, 4)},
+        "quantize_act_avg_launch_us": round(q_sec / (reps * nlaunch) * 1e6, 3),
+        "widths": widths,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -32,6 +32,8 @@
 //   MFMA (matrix cores): the four planes of a lane's four words form the A
 //        operands of four 16x16x64 int8 MFMAs; tokens fill the 16 B columns
 //        (zero beyond M).
+#include <atomic>
+
 #include "twd_internal.h"
 
 namespace twd {
@@ -299,6 +301,9 @@ __global__ __launch_bounds__(kThreads) void linear_kernel(
     }
 }
 
+constexpr int kMaxKernels = 2 * 3 * 16;  // families x tile counts x widths
+constexpr int kMaxLds = 160 * 1024;
+
 using LinearFn = void (*)(const uint4 *, const int8_t *, const float *, int,
                           int, Segments, int32_t *, float *);
 
@@ -364,11 +369,31 @@ hipError_t launch_linear(const LinearPlan &plan, const uint8_t *w,
     if (!fn)
         return hipErrorInvalidValue;
     if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           lds);
-        if (e != hipSuccess)
-            return e;
+        // Raise the dynamic-LDS limit to the largest size any call can need,
+        // once per kernel (not a stream operation; safe under capture).
+        static std::atomic<const void *> raised[kMaxKernels];
+        const void *key = reinterpret_cast<const void *>(fn);
+        bool done = false;
+        int slot = 0;
+        for (; slot < kMaxKernels; ++slot) {
+            const void *v = raised[slot].load(std::memory_order_acquire);
+            if (v == key) {
+                done = true;
+                break;
+            }
+            if (v == nullptr)
+                break;
+        }
+        if (!done) {
+            hipError_t e = hipFuncSetAttribute(key, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               kMaxLds);
+            if (e != hipSuccess)
+                return e;
+            if (slot < kMaxKernels) {
+                const void *expected = nullptr;
+                raised[slot].compare_exchange_strong(expected, key);
+            }
+        }
     }
     hipLaunchKernelGGL(fn, dim3(static_cast<uint32_t>(plan.grid)), dim3(kThreads),
                        lds, stream, reinterpret_cast<const uint4 *>(w), xq,
