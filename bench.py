@@ -3,19 +3,21 @@
 
 A step is one pass of the whole hot path over the 2B-class decode layer set
 (30 layers x {fused QKV 2560->3840, O 2560->2560, fused gate/up
-2560->13824, down 6912->2560}) at width M: per projection, the per-token
-int8 quantization of a fresh bf16 activation block followed by the fused
-ternary linear with its dequant epilogue.  All weights (521 MB packed, more
-than the 256 MB Infinity Cache, so every projection streams cold weights)
-and activations are resident in HBM before timing starts.  The step is
-recorded once into a HIP graph and replayed.
+2560->13824, down 6912->2560}) at width M: per projection, one launch that
+quantizes a fresh bf16 activation block per token to int8 and runs the
+fused ternary linear with its dequant epilogue.  All weights (521 MB packed,
+more than the 256 MB Infinity Cache, so every projection streams cold
+weights) and activations are resident in HBM before timing starts.  The step
+is recorded once into a HIP graph and replayed.
 
 Output: one JSON line.  `value` is packed-weight bytes per second over the
-timed steps (wall clock between two synchronizations).  `roofline` rates the
-dominant kernel -- the ternary linear -- from two events around
-back-to-back replays of a graph holding only its launches (average launch
-duration = elapsed / launches), against MI355X's 8 TB/s HBM peak.
-`cpu_baseline` times the CPU oracle on a bounded sample of the same work.
+timed steps (wall clock between two synchronizations).  The timed graph
+holds only the ternary linear launches, back to back, so two events around
+the timed replays give that kernel's average launch duration (elapsed /
+launches), from which `roofline` rates it against MI355X's 8 TB/s HBM peak.
+Also reported: the two-launch form (stand-alone quantizer + linear), a plain
+streaming read of the same buffers, the per-width table, and `cpu_baseline`,
+the CPU oracle timed on a bounded sample of the same work.
 """
 from __future__ import annotations
 
@@ -98,27 +100,21 @@ class Step:
     def keys(self):
         return [(l, p) for l in range(self.ds.layers) for p in range(len(self.ds.ls.projs))]
 
-    def quantize(self, key):
-        self.twd.quantize_act(self.x[key], self.xq[key], self.xs[key])
-
-    def linear(self, key):
-        p = self.ds.ls.projs[key[1]]
-        self.twd.ternary_linear_fused(self.ds.w[key], p.segs, self.ds.gammas[key],
-                                      self.xq[key], self.xs[key], y=self.y[key],
-                                      want_acc=False, kernel=self.kernel)
-
-    def full(self):
+    def fused(self):
+        """The step: one launch per projection (quantize + linear)."""
         for k in self.keys():
-            self.quantize(k)
-            self.linear(k)
+            p = self.ds.ls.projs[k[1]]
+            self.twd.ternary_linear_bf16(self.ds.w[k], p.segs, self.ds.gammas[k], self.x[k],
+                                         y=self.y[k], want_acc=False, kernel=self.kernel)
 
-    def linear_only(self):
+    def two_launch(self):
+        """Stand-alone quantizer, then the pre-quantized linear."""
         for k in self.keys():
-            self.linear(k)
-
-    def quantize_only(self):
-        for k in self.keys():
-            self.quantize(k)
+            p = self.ds.ls.projs[k[1]]
+            self.twd.quantize_act(self.x[k], self.xq[k], self.xs[k])
+            self.twd.ternary_linear_fused(self.ds.w[k], p.segs, self.ds.gammas[k],
+                                          self.xq[k], self.xs[k], y=self.y[k],
+                                          want_acc=False, kernel=self.kernel)
 
 
 def capture(torch, fn):
@@ -268,58 +264,59 @@ def main():
 
     step = Step(twd, torch, dev_set, args.workload, M, kernel, outliers)
     nlaunch = len(step.keys())
-    g_full = capture(torch, step.full)
-    g_lin = capture(torch, step.linear_only)
-    g_q = capture(torch, step.quantize_only)
+    g_step = capture(torch, step.fused)
+    g_two = capture(torch, step.two_launch)
 
-    # graph replays must equal eager results (every replay is checked)
+    # graph replays must equal eager results (every replay is checked), and
+    # the one-launch and two-launch forms must agree bit for bit
     if args.check:
-        step.full()
+        step.two_launch()
         torch.cuda.synchronize()
         eager = {k: v.clone() for k, v in step.y.items()}
-        for _ in range(2):
+        for g in (g_step, g_step, g_two):
             for v in step.y.values():
                 v.zero_()
-            g_full.replay()
+            g.replay()
             torch.cuda.synchronize()
             for k in step.keys():
                 if not torch.equal(step.y[k], eager[k]):
                     raise SystemExit(f"graph replay differs from eager at {k}")
 
     for _ in range(args.warmup):
-        g_full.replay()
-    wall, _ = time_replays(torch, g_full, args.steps)
+        g_step.replay()
+    wall, ev_sec = time_replays(torch, g_step, args.steps)
     bytes_step = dev_set.bytes_per_sweep
     value = bytes_step * args.steps / wall / 1e9
+    lin_dur = ev_sec / (args.steps * nlaunch)
+    lin_gbs = bytes_step * args.steps / ev_sec / 1e9
 
-    # dominant kernel: the ternary linear alone, back-to-back launches
-    reps = max(args.steps, 20)
-    g_lin.replay()
-    _, lin_sec = time_replays(torch, g_lin, reps)
-    lin_dur = lin_sec / (reps * nlaunch)
-    lin_gbs = bytes_step * reps / lin_sec / 1e9
-    g_q.replay()
-    _, q_sec = time_replays(torch, g_q, reps)
+    reps = max(10, args.steps // 2)
+    g_two.replay()
+    two_wall, _ = time_replays(torch, g_two, reps)
     ref_gbs, ref_dur = stream_read_reference(twd, torch, dev_set, reps)
     traffic = counter_traffic(args.workload, M, bytes_step / nlaunch)
     kname = twd.KERNEL_NAMES[twd.select_kernel(M, ls.hidden, ls.projs[2].N)] \
         if kernel == twd.KERNEL_AUTO else args.kernel
+    del g_two
 
     widths = {}
     if args.widths:
         for Mw in [int(v) for v in args.widths.split(",") if v]:
-            st = step if Mw == M else Step(twd, torch, dev_set, args.workload, Mw, kernel, outliers)
-            g = g_lin if Mw == M else capture(torch, st.linear_only)
+            if Mw == M:
+                widths[str(Mw)] = {"gbs": round(lin_gbs, 1), "frac": round(lin_gbs / HBM_PEAK_GBS, 4),
+                                   "us_per_launch": round(lin_dur * 1e6, 3), "kernel": kname}
+                continue
+            st = Step(twd, torch, dev_set, args.workload, Mw, kernel, outliers)
+            g = capture(torch, st.fused)
             g.replay()
-            _, sec = time_replays(torch, g, max(10, args.steps // 2))
-            gbs = bytes_step * max(10, args.steps // 2) / sec / 1e9
+            _, sec = time_replays(torch, g, reps)
+            gbs = bytes_step * reps / sec / 1e9
             widths[str(Mw)] = {"gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
-                               "us_per_launch": round(sec / (max(10, args.steps // 2) * nlaunch) * 1e6, 3),
+                               "us_per_launch": round(sec / (reps * nlaunch) * 1e6, 3),
                                "kernel": twd.KERNEL_NAMES[twd.select_kernel(Mw, ls.hidden, ls.projs[2].N)]
                                if kernel == twd.KERNEL_AUTO else args.kernel}
-            if st is not step:
-                del st, g
-                torch.cuda.empty_cache()
+            del st, g
+            torch.cuda.empty_cache()
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -343,7 +340,7 @@ def main():
             "layer_set": f"{ls.name.upper()}-class, hidden {ls.hidden}, {ls.layers} layers",
             "M": M,
             "packed_weight_bytes_per_step": bytes_step,
-            "launches_per_step": 2 * nlaunch,
+            "launches_per_step": nlaunch,
             "hip_graph": True,
             "kernel": kname,
         },
@@ -354,13 +351,13 @@ def main():
             "unit": "GB/s",
             "frac": round(lin_gbs / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": f"ternary linear ({kname})",
+            "kernel": f"ternary linear, activation quantization fused ({kname})",
             "avg_launch_us": round(lin_dur * 1e6, 3),
-            "launches_timed": reps * nlaunch,
+            "launches_timed": args.steps * nlaunch,
         },
         "stream_read_ref": {"gbs": round(ref_gbs, 1), "avg_launch_us": round(ref_dur * 1e6, 3),
                             "linear_over_ref": round(lin_gbs / ref_gbs, 4)},
-        "quantize_act_avg_launch_us": round(q_sec / (reps * nlaunch) * 1e6, 3),
+        "two_launch_step_gbs": round(bytes_step * reps / two_wall / 1e9, 1),
         "widths": widths,
         "cpu_baseline": cpu,
     }

@@ -104,7 +104,7 @@ twd_status twd_unpack_ternary(const uint8_t *packed, int64_t N, int64_t K,
  * xscale: device fp32 [M].  For each row: a = max |x|, inv = 127 / a (fp32,
  * correctly rounded), xq = clamp(rint(x * inv), -127, 127), xscale = a / 127;
  * a == 0 gives xq = 0 and xscale = 0.  Non-finite x is outside the contract.
- * Shapes: 0 <= M (M == 0 is a no-op), 1 <= K <= 65536, K % 8 == 0.
+ * Shapes: 0 <= M <= 65535 (M == 0 is a no-op), 8 <= K <= 65536, K % 8 == 0.
  * Alignment: x_bf16 and xq 16-byte aligned. */
 twd_status twd_quantize_act(const uint16_t *x_bf16, int64_t M, int64_t K,
                             int8_t *xq, float *xscale, void *stream);
@@ -144,6 +144,21 @@ twd_status twd_ternary_linear_fused_kernel(const uint8_t *wpacked, int nseg,
                                            const float *xscale, int64_t M,
                                            int64_t K, int32_t *acc, float *y,
                                            int kernel, void *stream);
+
+/* One launch for a whole projection: the per-token absmax int8
+ * quantization of bf16 activations x_bf16 (device [M][K], 16-byte aligned),
+ * with exactly the arithmetic of twd_quantize_act, fused into the ternary
+ * linear over nseg row segments.  acc / y and the segment tables as in
+ * twd_ternary_linear_fused; kernel as in twd_ternary_linear_fused_kernel.
+ * Reading of the pages: BitNet b1.58 quantizes activations inside every
+ * ternary layer ("What This Paper Is About" names the backbone), so the
+ * quantizer belongs to the layer's launch. */
+twd_status twd_ternary_linear_bf16(const uint8_t *wpacked, int nseg,
+                                   const int64_t *seg_rows,
+                                   const float *seg_gamma,
+                                   const uint16_t *x_bf16, int64_t M,
+                                   int64_t K, int32_t *acc, float *y,
+                                   int kernel, void *stream);
 
 /* The kernel family the width dispatch picks for (M, K, N), without
  * launching anything.  Returns TWD_KERNEL_DOT or TWD_KERNEL_MFMA, or -1 if

@@ -6,7 +6,8 @@ memory and the current HIP stream.  Importing this package without the built
 library raises ``ImportError`` -- there is no fallback implementation.
 
 Names follow the C ABI in ``include/twd.h``: ``quantize_act``,
-``ternary_linear``, ``ternary_linear_fused``, ``pack_ternary``,
+``ternary_linear``, ``ternary_linear_fused``, ``ternary_linear_bf16``,
+``pack_ternary``,
 ``unpack_ternary``, ``ternarize_absmean``, ``select_kernel``,
 ``stream_read``.
 """
@@ -31,6 +32,14 @@ if not os.path.exists(LIB_PATH):
         f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; "
         "g.build()'` (hipcc --offload-arch=gfx950)")
 
+# PyTorch ships its own HIP runtime with the same soname as ROCm's; loading
+# torch first makes libtwd bind to that one, so a process never holds two
+# HIP runtimes (device tensors come from torch).
+try:
+    import torch  # noqa: F401
+except ImportError:  # host-side functions still work without torch
+    pass
+
 _lib = ctypes.CDLL(LIB_PATH)
 _p, _i64, _int, _f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
 
@@ -53,13 +62,16 @@ _lib_fused = _sig("twd_ternary_linear_fused",
                   [_p, _int, _p, _p, _p, _p, _i64, _i64, _p, _p, _p])
 _lib_fused_kernel = _sig("twd_ternary_linear_fused_kernel",
                          [_p, _int, _p, _p, _p, _p, _i64, _i64, _p, _p, _int, _p])
+_lib_bf16 = _sig("twd_ternary_linear_bf16",
+                 [_p, _int, _p, _p, _p, _i64, _i64, _p, _p, _int, _p])
 _lib_select = _sig("twd_select_kernel", [_i64, _i64, _i64])
 _lib_stream_read = _sig("twd_stream_read", [_p, _i64, _p, _p])
 
 EXPORTS = ("twd_version", "twd_last_error", "twd_ternarize_absmean",
            "twd_pack_ternary", "twd_unpack_ternary", "twd_quantize_act",
            "twd_ternary_linear", "twd_ternary_linear_fused",
-           "twd_ternary_linear_fused_kernel", "twd_select_kernel",
+           "twd_ternary_linear_fused_kernel", "twd_ternary_linear_bf16",
+           "twd_select_kernel",
            "twd_stream_read")
 
 
@@ -239,6 +251,29 @@ def ternary_linear_fused(wpacked, seg_rows, seg_gamma, xq, xscale, acc=None,
         _check(_lib_fused(*args, _stream(stream)))
     else:
         _check(_lib_fused_kernel(*args, int(kernel), _stream(stream)))
+    return acc, y
+
+
+def ternary_linear_bf16(wpacked, seg_rows, seg_gamma, x, acc=None, y=None,
+                        want_acc=True, want_y=True, kernel=KERNEL_AUTO, stream=None):
+    """Whole projection in one launch: bf16 activations x [M, K] are
+    quantized per token inside the kernel, then contracted with the packed
+    ternary weights over the row segments.  Returns (acc, y)."""
+    torch = _torch()
+    _need(x.dim() == 2, "x must be [M, K]")
+    M, K = x.shape
+    seg_rows = [int(r) for r in seg_rows]
+    nseg = len(seg_rows)
+    _need(len(seg_gamma) == nseg, "one gamma per segment")
+    N = int(sum(seg_rows))
+    _need(_nbytes(wpacked) >= N * K // 4, "wpacked holds fewer than N*K/4 bytes")
+    rows = (ctypes.c_int64 * max(nseg, 1))(*seg_rows)
+    gam = (ctypes.c_float * max(nseg, 1))(*[float(g) for g in seg_gamma])
+    acc, y = _outputs(M, N, x.device, acc, y, want_acc, want_y)
+    _check(_lib_bf16(_dev_ptr(wpacked, "wpacked", (torch.uint8,)), nseg, rows, gam,
+                     _dev_ptr(x, "x", (torch.bfloat16, torch.int16)), M, K,
+                     _dev_ptr(acc, "acc", (torch.int32,)), _dev_ptr(y, "y", (torch.float32,)),
+                     int(kernel), _stream(stream)))
     return acc, y
 
 

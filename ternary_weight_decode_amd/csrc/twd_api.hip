@@ -26,12 +26,17 @@ twd_status hip_status(hipError_t e, const char *what) {
 
 constexpr int64_t kMaxN = int64_t(1) << 30;
 
-// Shared checks of the linear entry points; fills segs and N.
+// Shared checks of the linear entry points; fills segs and N.  xscale is
+// only required for the pre-quantized form (fused == false).
 twd_status check_linear(const uint8_t *wpacked, int nseg,
                         const int64_t *seg_rows, const float *seg_gamma,
-                        const int8_t *xq, const float *xscale, int64_t M,
-                        int64_t K, const int32_t *acc, const float *y,
-                        Segments *segs, int64_t *N_out) {
+                        const void *act, bool fused, const float *xscale,
+                        int64_t M, int64_t K, const int32_t *acc,
+                        const float *y, int kernel, Segments *segs,
+                        int64_t *N_out) {
+    if (kernel != TWD_KERNEL_AUTO && kernel != TWD_KERNEL_DOT &&
+        kernel != TWD_KERNEL_MFMA)
+        return set_error(TWD_ERR_INVALID_ARG, "linear: unknown kernel %d", kernel);
     if (nseg < 1 || nseg > TWD_MAX_SEGMENTS)
         return set_error(TWD_ERR_INVALID_ARG, "linear: nseg=%d outside 1..%d",
                          nseg, TWD_MAX_SEGMENTS);
@@ -60,16 +65,19 @@ twd_status check_linear(const uint8_t *wpacked, int nseg,
         return set_error(TWD_ERR_UNSUPPORTED,
                          "linear: K=%lld must be a multiple of 64 in 64..%d",
                          (long long)K, TWD_MAX_K);
+    if (kernel == TWD_KERNEL_DOT && M > 4)
+        return set_error(TWD_ERR_UNSUPPORTED, "linear: the dot kernel takes M <= 4");
     if (M == 0 || N == 0)
         return TWD_OK;
-    if (!wpacked || !xq || !xscale)
+    if (!wpacked || !act || (!fused && !xscale))
         return set_error(TWD_ERR_INVALID_ARG, "linear: null input pointer");
     if (!acc && !y)
         return set_error(TWD_ERR_INVALID_ARG, "linear: acc and y are both NULL");
-    if (!aligned(wpacked, 16) || !aligned(xq, 16))
+    if (!aligned(wpacked, 16) || !aligned(act, 16))
         return set_error(TWD_ERR_INVALID_ARG,
-                         "linear: wpacked and xq must be 16-byte aligned");
-    if (!aligned(xscale, 4) || (acc && !aligned(acc, 4)) || (y && !aligned(y, 4)))
+                         "linear: wpacked and the activations must be 16-byte aligned");
+    if ((!fused && !aligned(xscale, 4)) || (acc && !aligned(acc, 4)) ||
+        (y && !aligned(y, 4)))
         return set_error(TWD_ERR_INVALID_ARG,
                          "linear: xscale, acc and y must be 4-byte aligned");
     return TWD_OK;
@@ -117,27 +125,43 @@ extern "C" twd_status twd_quantize_act(const uint16_t *x_bf16, int64_t M,
                       "quantize_act launch");
 }
 
+namespace {
+
+twd_status run_linear(const uint8_t *wpacked, int nseg, const int64_t *seg_rows,
+                      const float *seg_gamma, const void *act, bool fused,
+                      const float *xscale, int64_t M, int64_t K, int32_t *acc,
+                      float *y, int kernel, void *stream) {
+    Segments segs;
+    int64_t N = 0;
+    twd_status st = check_linear(wpacked, nseg, seg_rows, seg_gamma, act, fused,
+                                 xscale, M, K, acc, y, kernel, &segs, &N);
+    if (st != TWD_OK || M == 0 || N == 0)
+        return st;
+    const LinearPlan plan = plan_linear(static_cast<int>(M), static_cast<int>(K),
+                                        static_cast<int>(N), kernel);
+    return hip_status(launch_linear(plan, wpacked, act, fused, xscale,
+                                    static_cast<int>(M), static_cast<int>(K),
+                                    static_cast<int>(N), segs, acc, y,
+                                    as_stream(stream)),
+                      "linear launch");
+}
+
+}  // namespace
+
 extern "C" twd_status twd_ternary_linear_fused_kernel(
     const uint8_t *wpacked, int nseg, const int64_t *seg_rows,
     const float *seg_gamma, const int8_t *xq, const float *xscale, int64_t M,
     int64_t K, int32_t *acc, float *y, int kernel, void *stream) {
-    if (kernel != TWD_KERNEL_AUTO && kernel != TWD_KERNEL_DOT &&
-        kernel != TWD_KERNEL_MFMA)
-        return set_error(TWD_ERR_INVALID_ARG, "linear: unknown kernel %d", kernel);
-    Segments segs;
-    int64_t N = 0;
-    twd_status st = check_linear(wpacked, nseg, seg_rows, seg_gamma, xq, xscale,
-                                 M, K, acc, y, &segs, &N);
-    if (st != TWD_OK || M == 0 || N == 0)
-        return st;
-    if (kernel == TWD_KERNEL_DOT && M > 8)
-        return set_error(TWD_ERR_UNSUPPORTED, "linear: the dot kernel takes M <= 8");
-    const LinearPlan plan = plan_linear(static_cast<int>(M), static_cast<int>(K),
-                                        static_cast<int>(N), kernel);
-    return hip_status(launch_linear(plan, wpacked, xq, xscale, static_cast<int>(M),
-                                    static_cast<int>(K), static_cast<int>(N),
-                                    segs, acc, y, as_stream(stream)),
-                      "linear launch");
+    return run_linear(wpacked, nseg, seg_rows, seg_gamma, xq, false, xscale, M,
+                      K, acc, y, kernel, stream);
+}
+
+extern "C" twd_status twd_ternary_linear_bf16(
+    const uint8_t *wpacked, int nseg, const int64_t *seg_rows,
+    const float *seg_gamma, const uint16_t *x_bf16, int64_t M, int64_t K,
+    int32_t *acc, float *y, int kernel, void *stream) {
+    return run_linear(wpacked, nseg, seg_rows, seg_gamma, x_bf16, true, nullptr,
+                      M, K, acc, y, kernel, stream);
 }
 
 extern "C" twd_status twd_ternary_linear_fused(

@@ -19,9 +19,8 @@ struct Segments {
 
 // Launch parameters the width dispatch chose for one linear call.
 struct LinearPlan {
-    int kernel;       // TWD_KERNEL_DOT or TWD_KERNEL_MFMA
-    int tiles;        // 16-row tiles per workgroup
-    int64_t grid;     // workgroups
+    int kernel;  // TWD_KERNEL_DOT or TWD_KERNEL_MFMA
+    int tiles;   // 16-row tiles per workgroup
 };
 
 // Thread-local error message; returns `st` for convenient chaining.
@@ -32,10 +31,23 @@ LinearPlan plan_linear(int M, int K, int N, int forced_kernel);
 hipError_t launch_quantize_act(const uint16_t *x, int M, int K, int8_t *xq,
                                float *xscale, hipStream_t stream);
 
+// act is int8 xq [M][K] with its scales xscale, or, when fused, bf16 x
+// [M][K] quantized inside the kernel (xscale unused).
 hipError_t launch_linear(const LinearPlan &plan, const uint8_t *w,
-                         const int8_t *xq, const float *xscale, int M, int K,
-                         int N, const Segments &segs, int32_t *acc, float *y,
-                         hipStream_t stream);
+                         const void *act, bool fused, const float *xscale,
+                         int M, int K, int N, const Segments &segs,
+                         int32_t *acc, float *y, hipStream_t stream);
+
+// The two kernel families (ternary_dot.hip: M <= 4; ternary_mfma.hip:
+// M <= 16).  tiles = 16-row tiles per workgroup.
+hipError_t launch_dot(int tiles, const uint8_t *w, const void *act, bool fused,
+                      const float *xscale, int M, int K, int N,
+                      const Segments &segs, int32_t *acc, float *y,
+                      hipStream_t stream);
+hipError_t launch_mfma(int tiles, const uint8_t *w, const void *act, bool fused,
+                       const float *xscale, int M, int K, int N,
+                       const Segments &segs, int32_t *acc, float *y,
+                       hipStream_t stream);
 
 hipError_t launch_stream_read(const void *buf, int64_t bytes, uint32_t *sink,
                               hipStream_t stream);

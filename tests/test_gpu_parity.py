@@ -3,7 +3,7 @@
 Bar: quantized activations, scales and int32 accumulators bit-exact; fp32
 outputs within 1e-6 relative of the oracle's double-precision value, per
 element.  Cases span several 16-row tiles, partial 256-wide K slices and
-ragged N tails, every width M = 1..16 for the matrix-core kernel and 1..8 for
+ragged N tails, every width M = 1..16 for the matrix-core kernel and 1..4 for
 the VALU kernel, fused segments, the single-linear workload and full-size
 2B / 4B projections.
 """
@@ -57,20 +57,27 @@ def prepared(twd, torch, W, segs, key):
     return _prep_cache[key]
 
 
-def run_case(env, W, segs, x, kernel, key, ref=None):
+def run_case(env, W, segs, x, kernel, key, ref=None, fused=False):
+    """Run one case through the C ABI and compare with the oracle.  fused:
+    the one-launch bf16 entry point instead of quantize_act + linear."""
     torch, twd, orc = env
     wp, gammas = prepared(twd, torch, W, segs, key)
     M, K = x.shape
-    log(f"case {key} M={M} K={K} N={W.shape[0]} segs={segs} kernel={kernel}")
-    xq, xs = twd.quantize_act(to_dev_bf16(torch, x))
-    acc, y = twd.ternary_linear_fused(wp, segs, gammas, xq, xs, kernel=kernel)
-    torch.cuda.synchronize()
+    log(f"case {key} M={M} K={K} N={W.shape[0]} segs={segs} kernel={kernel} fused={fused}")
     if ref is None:
         ref = orc.forward(W, segs, x)
     assert gammas == ref["gammas"]
-    np.testing.assert_array_equal(xq.cpu().numpy(), ref["q"])
-    np.testing.assert_array_equal(xs.cpu().numpy().view(np.uint32),
-                                  ref["scale"].view(np.uint32))
+    xd = to_dev_bf16(torch, x)
+    if fused:
+        acc, y = twd.ternary_linear_bf16(wp, segs, gammas, xd, kernel=kernel)
+        torch.cuda.synchronize()
+    else:
+        xq, xs = twd.quantize_act(xd)
+        acc, y = twd.ternary_linear_fused(wp, segs, gammas, xq, xs, kernel=kernel)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(xq.cpu().numpy(), ref["q"])
+        np.testing.assert_array_equal(xs.cpu().numpy().view(np.uint32),
+                                      ref["scale"].view(np.uint32))
     np.testing.assert_array_equal(acc.cpu().numpy(), ref["acc"])
     check_y(y.cpu().numpy(), ref["y"])
     return acc, y
@@ -127,11 +134,42 @@ def test_mfma_kernel_parity(env, M, K, segs):
 
 
 @pytest.mark.parametrize("K,segs", SMALL_SHAPES)
-@pytest.mark.parametrize("M", list(range(1, 9)))
+@pytest.mark.parametrize("M", list(range(1, 5)))
 def test_dot_kernel_parity(env, M, K, segs):
     torch, twd, orc = env
     W, segs, x = wl.random_case(seed=1, M=M, K=K, seg_rows=segs)
     run_case(env, W, segs, x, twd.KERNEL_DOT, ("rand", 1, K, segs))
+
+
+@pytest.mark.parametrize("K,segs", SMALL_SHAPES)
+@pytest.mark.parametrize("M", list(range(1, 17)))
+def test_fused_bf16_mfma_parity(env, M, K, segs):
+    torch, twd, orc = env
+    W, segs, x = wl.random_case(seed=1, M=M, K=K, seg_rows=segs)
+    run_case(env, W, segs, x, twd.KERNEL_MFMA, ("rand", 1, K, segs), fused=True)
+
+
+@pytest.mark.parametrize("K,segs", SMALL_SHAPES)
+@pytest.mark.parametrize("M", list(range(1, 5)))
+def test_fused_bf16_dot_parity(env, M, K, segs):
+    torch, twd, orc = env
+    W, segs, x = wl.random_case(seed=1, M=M, K=K, seg_rows=segs)
+    run_case(env, W, segs, x, twd.KERNEL_DOT, ("rand", 1, K, segs), fused=True)
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 8, 16])
+def test_fused_bf16_zero_rows_and_outliers(env, M):
+    """All-zero token rows (scale 0, output 0) and x20 outlier channels."""
+    torch, twd, orc = env
+    W, segs, x = wl.random_case(seed=7, M=M, K=2560, seg_rows=(48,))
+    xf = wl.bf16_bits_to_f32(x).copy()
+    xf[0] = 0.0
+    if M > 1:
+        xf[1, ::97] *= 20.0
+    x = wl.f32_to_bf16_bits(xf)
+    for kernel in (twd.KERNEL_MFMA, twd.KERNEL_DOT) if M <= 4 else (twd.KERNEL_MFMA,):
+        acc, y = run_case(env, W, segs, x, kernel, ("rand", 7), fused=True)
+        assert not acc[0].any() and not y[0].any()
 
 
 @pytest.mark.parametrize("M", [1, 2, 4, 5, 8, 16])
@@ -148,7 +186,8 @@ def test_single_linear_workload(env):
     torch, twd, orc = env
     W, segs, x = wl.single_case(seed=0)
     for kernel in (twd.KERNEL_AUTO, twd.KERNEL_DOT, twd.KERNEL_MFMA):
-        run_case(env, W, segs, x, kernel, ("single", 0))
+        for fused in (False, True):
+            run_case(env, W, segs, x, kernel, ("single", 0), fused=fused)
 
 
 def test_width_invariance(env):
@@ -159,7 +198,7 @@ def test_width_invariance(env):
     xq, xs = twd.quantize_act(to_dev_bf16(torch, x))
     full = {}
     for kernel in (twd.KERNEL_MFMA, twd.KERNEL_DOT):
-        for M in (16, 8, 4, 1) if kernel == twd.KERNEL_MFMA else (8, 4, 1):
+        for M in (16, 8, 4, 1) if kernel == twd.KERNEL_MFMA else (4, 2, 1):
             acc, _ = twd.ternary_linear_fused(wp, segs, gammas, xq[:M].contiguous(),
                                               xs[:M].contiguous(), kernel=kernel)
             full[(kernel, M)] = acc
@@ -230,7 +269,7 @@ def test_extreme_values(env):
     W = np.ones((N, K), np.float32)
     W[::3] = -1.0
     for kernel in (twd.KERNEL_MFMA, twd.KERNEL_DOT):
-        xs_ = x if kernel == twd.KERNEL_MFMA else x[:8]
+        xs_ = x if kernel == twd.KERNEL_MFMA else x[:4]
         acc, _ = run_case(env, W, (N,), xs_, kernel, ("extreme",))
         assert abs(int(acc.abs().max())) == 127 * K
 
@@ -255,10 +294,29 @@ def test_full_size_layer(env, set_name, workload, layer, M):
         W = wl.layer_weights(ls, layer, pi)
         x = wl.layer_activations(workload, proj.K, M, layer, pi,
                                  outliers=workload == "2b_sweep_outlier")
-        run_case(env, W, proj.segs, x, twd.KERNEL_AUTO, (set_name, layer, pi))
+        ref = orc.forward(W, proj.segs, x)
+        run_case(env, W, proj.segs, x, twd.KERNEL_AUTO, (set_name, layer, pi), ref=ref)
+        run_case(env, W, proj.segs, x, twd.KERNEL_AUTO, (set_name, layer, pi), ref=ref,
+                 fused=True)
 
 
 # ------------------------------------------------------------- error paths
+
+def test_fused_errors_on_gpu(env):
+    torch, twd, orc = env
+    x = torch.zeros((4, 256), dtype=torch.bfloat16, device="cuda")
+    wp = torch.zeros(64 * 64, dtype=torch.uint8, device="cuda")
+    with pytest.raises(twd.TwdError) as e:
+        twd.ternary_linear_bf16(wp, (64,), (1.0,),
+                                torch.zeros((4, 100), dtype=torch.bfloat16, device="cuda"))
+    assert e.value.status == 2
+    with pytest.raises(twd.TwdError) as e:
+        twd.ternary_linear_bf16(wp, (64,), (1.0,), torch.zeros((5, 256), dtype=torch.bfloat16,
+                                                               device="cuda"), kernel=twd.KERNEL_DOT)
+    assert e.value.status == 2
+    acc, y = twd.ternary_linear_bf16(wp, (64,), (1.0,), x[:0])
+    assert acc.shape == (0, 64)
+
 
 def test_errors_on_gpu(env):
     torch, twd, orc = env

@@ -133,11 +133,23 @@ def _fused(twd, wp=0x1000, nseg=1, rows=(64,), gam=(1.0,), xq=0x2000, xs=0x3000,
     (dict(rows=(-1,)), 1), (dict(wp=None), 1), (dict(xq=None), 1),
     (dict(xs=None), 1), (dict(acc=None, y=None), 1), (dict(wp=0x1008), 1),
     (dict(xq=0x2004), 1), (dict(y=0x5002), 1), (dict(kernel=7), 1),
-    (dict(kernel=1, M=9), 2),
+    (dict(kernel=1, M=5), 2),
 ])
 def test_linear_rejects_before_launch(twd, kw, status):
     assert _fused(twd, **kw) == status
     assert twd._lib_last_error()
+
+
+def test_bf16_linear_rejects_before_launch(twd):
+    f = twd._lib_bf16
+    r = (ctypes.c_int64 * 1)(64)
+    g = (ctypes.c_float * 1)(1.0)
+    assert f(0x1000, 1, r, g, 0x2000, 17, 256, 0x4000, 0x5000, 0, None) == 2
+    assert f(0x1000, 1, r, g, 0x2000, 1, 96, 0x4000, 0x5000, 0, None) == 2
+    assert f(0x1000, 1, r, g, None, 1, 256, 0x4000, 0x5000, 0, None) == 1
+    assert f(0x1000, 1, r, g, 0x2008, 1, 256, 0x4000, 0x5000, 0, None) == 1
+    assert f(0x1000, 1, r, g, 0x2000, 5, 256, 0x4000, 0x5000, 1, None) == 2
+    assert f(0x1000, 1, r, g, 0x2000, 0, 256, 0x4000, 0x5000, 0, None) == 0
 
 
 def test_linear_empty_is_noop(twd):
