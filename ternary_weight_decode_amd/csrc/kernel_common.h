@@ -55,27 +55,45 @@ __device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
     return max(a, b);
 }
 
-__device__ __forceinline__ uint32_t absbits8(const uint4 v) {
-    // |bf16| pairs widened to fp32 bit patterns; max over the eight
-    const uint32_t m0 = max(v.x << 16 & 0x7FFF0000u, v.x & 0x7FFF0000u);
-    const uint32_t m1 = max(v.y << 16 & 0x7FFF0000u, v.y & 0x7FFF0000u);
-    const uint32_t m2 = max(v.z << 16 & 0x7FFF0000u, v.z & 0x7FFF0000u);
-    const uint32_t m3 = max(v.w << 16 & 0x7FFF0000u, v.w & 0x7FFF0000u);
-    return max(max(m0, m1), max(m2, m3));
-}
+// Per-token int8 quantization, q = rint(x * inv), bit-exact with a plain
+// fp32 implementation (rint rounds half to even):
+//   * the product x * inv is rounded to fp32 on its own (__fmul_rn: never
+//     contracted into an fma), then 1.5 * 2^23 is added (__fadd_rn): the
+//     sum's ulp is 1, so the FPU's round-to-nearest-even performs rint and
+//     the integer lands in the low mantissa bits, whose low byte is q in
+//     two's complement;
+//   * no clamp is needed: |x| <= a and inv = RN(127 / a) <= (127 / a)(1 +
+//     2^-24) give |x * inv| < 127.5, so |q| <= 127 always.
+constexpr float kRoundMagic = 12582912.0f;  // 1.5 * 2^23
 
-__device__ __forceinline__ uint32_t q8(float x, float inv) {
-    float r = __builtin_rintf(x * inv);
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    return static_cast<uint32_t>(static_cast<int>(r)) & 0xFFu;
+__device__ __forceinline__ uint32_t q8bits(float x, float inv) {
+    return __float_as_uint(__fadd_rn(__fmul_rn(x, inv), kRoundMagic));
 }
 
 // Quantize two bf16 pairs (one 32-bit word each) into four int8 lanes.
 __device__ __forceinline__ uint32_t quant4(uint32_t lo, uint32_t hi, float inv) {
-    return q8(__uint_as_float(lo << 16), inv) |
-           q8(__uint_as_float(lo & 0xFFFF0000u), inv) << 8 |
-           q8(__uint_as_float(hi << 16), inv) << 16 |
-           q8(__uint_as_float(hi & 0xFFFF0000u), inv) << 24;
+    const uint32_t b0 = q8bits(__uint_as_float(lo << 16), inv);
+    const uint32_t b1 = q8bits(__uint_as_float(lo & 0xFFFF0000u), inv);
+    const uint32_t b2 = q8bits(__uint_as_float(hi << 16), inv);
+    const uint32_t b3 = q8bits(__uint_as_float(hi & 0xFFFF0000u), inv);
+    // gather the four low bytes (v_perm_b32: selector bytes 0-3 pick the
+    // second operand's bytes, 4-7 the first's, 0x0c gives zero)
+    const uint32_t lo2 = __builtin_amdgcn_perm(b1, b0, 0x0C0C0400u);
+    const uint32_t hi2 = __builtin_amdgcn_perm(b3, b2, 0x04000C0Cu);
+    return lo2 | hi2;
+}
+
+// Running max of |bf16| over pairs packed in 32-bit words: the magnitude of
+// a bf16 orders like its low 15 bits, so a packed 16-bit max does it.
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u16x2 absmax_pair(u16x2 m, uint32_t v) {
+    return __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, v & 0x7FFF7FFFu));
+}
+
+// The fp32 bit pattern of the larger of the two halves.
+__device__ __forceinline__ uint32_t absmax_bits(u16x2 m) {
+    return static_cast<uint32_t>(m.x > m.y ? m.x : m.y) << 16;
 }
 
 __device__ __forceinline__ float row_gamma(const Segments &sg, int n) {

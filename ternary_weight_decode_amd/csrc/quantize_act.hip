@@ -1,76 +1,72 @@
 // Per-token absmax int8 activation quantizer for gfx950 (BitMTP page,
 // ai.info AI summary, "Main Findings": W2A8 uses 8-bit activations).  One
-// workgroup per token row: a max-reduction of |x| over the row, one
-// correctly rounded fp32 division for 127/a, then q = clamp(rint(x * inv))
-// written eight at a time.
-#include "twd_internal.h"
+// workgroup per token row: every 16-byte chunk of the row is loaded at once
+// (up to 16384 elements stay in registers), a max-reduction of |x| (packed
+// 16-bit max, DPP, one LDS exchange), one correctly rounded fp32 division for
+// 127/a, then q = rint(x * inv) written eight at a time.  The rounding
+// arithmetic is shared with the fused linear kernels, so both produce the
+// same bytes.
+#include "kernel_common.h"
 
 namespace twd {
 namespace {
 
-constexpr int kThreads = 256;
+using namespace kern;
 
-__device__ inline float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
-__device__ inline float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+constexpr int kQThreads = 256;
+constexpr int kHold = 8;  // chunks of 8 elements held per thread
 
-__device__ inline float absmax8(const uint4 v) {
-    float a = fabsf(bf16_lo(v.x));
-    a = fmaxf(a, fabsf(bf16_hi(v.x)));
-    a = fmaxf(a, fabsf(bf16_lo(v.y)));
-    a = fmaxf(a, fabsf(bf16_hi(v.y)));
-    a = fmaxf(a, fabsf(bf16_lo(v.z)));
-    a = fmaxf(a, fabsf(bf16_hi(v.z)));
-    a = fmaxf(a, fabsf(bf16_lo(v.w)));
-    a = fmaxf(a, fabsf(bf16_hi(v.w)));
-    return a;
-}
-
-__device__ inline uint32_t q8(float x, float inv) {
-    float r = __builtin_rintf(x * inv);
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    return static_cast<uint32_t>(static_cast<int>(r)) & 0xFFu;
-}
-
-__device__ inline uint32_t quant4(uint32_t lo, uint32_t hi, float inv) {
-    return q8(bf16_lo(lo), inv) | q8(bf16_hi(lo), inv) << 8 |
-           q8(bf16_lo(hi), inv) << 16 | q8(bf16_hi(hi), inv) << 24;
-}
-
-__global__ __launch_bounds__(kThreads) void quantize_act_kernel(
+__global__ __launch_bounds__(kQThreads) void quantize_act_kernel(
     const uint16_t *__restrict__ x, int K, int8_t *__restrict__ xq,
     float *__restrict__ xscale) {
-    __shared__ float wave_max[kThreads / 64];
+    __shared__ uint32_t wave_max[kQThreads / 64];
     const int m = blockIdx.x;
+    const int tid = threadIdx.x;
     const uint4 *row = reinterpret_cast<const uint4 *>(x + static_cast<int64_t>(m) * K);
     uint2 *out = reinterpret_cast<uint2 *>(xq + static_cast<int64_t>(m) * K);
     const int n8 = K / 8;
 
-    float a = 0.0f;
-    for (int i = threadIdx.x; i < n8; i += kThreads)
-        a = fmaxf(a, absmax8(row[i]));
+    uint4 v[kHold];
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1)
-        a = fmaxf(a, __shfl_xor(a, off, 64));
-    if ((threadIdx.x & 63) == 0)
-        wave_max[threadIdx.x >> 6] = a;
+    for (int j = 0; j < kHold; ++j) {
+        const int c = tid + kQThreads * j;
+        v[j] = c < n8 ? row[c] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    u16x2 am2 = {0, 0};
+#pragma unroll
+    for (int j = 0; j < kHold; ++j) {
+        am2 = absmax_pair(am2, v[j].x);
+        am2 = absmax_pair(am2, v[j].y);
+        am2 = absmax_pair(am2, v[j].z);
+        am2 = absmax_pair(am2, v[j].w);
+    }
+    // rows longer than the held part (K > 16384)
+    for (int c = tid + kQThreads * kHold; c < n8; c += kQThreads) {
+        const uint4 w = row[c];
+        am2 = absmax_pair(am2, w.x);
+        am2 = absmax_pair(am2, w.y);
+        am2 = absmax_pair(am2, w.z);
+        am2 = absmax_pair(am2, w.w);
+    }
+    const uint32_t wm = wave_umax(absmax_bits(am2));
+    if ((tid & 63) == 0)
+        wave_max[tid >> 6] = wm;
     __syncthreads();
-    a = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
-
-    if (a == 0.0f) {
-        for (int i = threadIdx.x; i < n8; i += kThreads)
-            out[i] = make_uint2(0u, 0u);
-        if (threadIdx.x == 0)
-            xscale[m] = 0.0f;
-        return;
+    const uint32_t ab = max(max(wave_max[0], wave_max[1]), max(wave_max[2], wave_max[3]));
+    const float a = __uint_as_float(ab);
+    // correctly rounded fp32 division (build flag); all-zero row -> zeros
+    const float inv = a > 0.0f ? 127.0f / a : 0.0f;
+#pragma unroll
+    for (int j = 0; j < kHold; ++j) {
+        const int c = tid + kQThreads * j;
+        if (c < n8)
+            out[c] = make_uint2(quant4(v[j].x, v[j].y, inv), quant4(v[j].z, v[j].w, inv));
     }
-    // IEEE division (the library is built with correctly rounded fp32
-    // division), then one rounded multiply per element.
-    const float inv = 127.0f / a;
-    for (int i = threadIdx.x; i < n8; i += kThreads) {
-        const uint4 v = row[i];
-        out[i] = make_uint2(quant4(v.x, v.y, inv), quant4(v.z, v.w, inv));
+    for (int c = tid + kQThreads * kHold; c < n8; c += kQThreads) {
+        const uint4 w = row[c];
+        out[c] = make_uint2(quant4(w.x, w.y, inv), quant4(w.z, w.w, inv));
     }
-    if (threadIdx.x == 0)
+    if (tid == 0)
         xscale[m] = a / 127.0f;
 }
 
@@ -78,7 +74,7 @@ __global__ __launch_bounds__(kThreads) void quantize_act_kernel(
 
 hipError_t launch_quantize_act(const uint16_t *x, int M, int K, int8_t *xq,
                                float *xscale, hipStream_t stream) {
-    hipLaunchKernelGGL(quantize_act_kernel, dim3(M), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL(quantize_act_kernel, dim3(M), dim3(kQThreads), 0, stream,
                        x, K, xq, xscale);
     return hipGetLastError();
 }

@@ -51,11 +51,6 @@ __host__ __device__ constexpr int lds_bytes() {
     return act_bytes<M, U, TW>() + red_bytes<M, U, TW>() + 2 * kWaves * M * 4;
 }
 
-__device__ __forceinline__ uint32_t absbits4(const uint2 v) {
-    return max(max(v.x << 16 & 0x7FFF0000u, v.x & 0x7FFF0000u),
-               max(v.y << 16 & 0x7FFF0000u, v.y & 0x7FFF0000u));
-}
-
 template <int M, int U, int TW, bool FUSED>
 __global__ __launch_bounds__(kThreads) void dot_kernel(
     const uint4 *__restrict__ W, const void *__restrict__ act,
@@ -122,11 +117,13 @@ __global__ __launch_bounds__(kThreads) void dot_kernel(
     if constexpr (FUSED) {
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-            uint32_t am = 0;
+            u16x2 am2 = {0, 0};
 #pragma unroll
-            for (int u = 0; u < U; ++u)
-                am = max(am, xok[u] ? absbits4(xb[m][u]) : 0u);
-            am = wave_umax(am);
+            for (int u = 0; u < U; ++u) {
+                am2 = absmax_pair(am2, xok[u] ? xb[m][u].x : 0u);
+                am2 = absmax_pair(am2, xok[u] ? xb[m][u].y : 0u);
+            }
+            const uint32_t am = wave_umax(absmax_bits(am2));
             if (lane == 0)
                 st_max[wave * M + m] = am;
         }

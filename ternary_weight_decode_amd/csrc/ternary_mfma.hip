@@ -67,12 +67,16 @@ __device__ __forceinline__ void stage_row(const void *__restrict__ act,
     }
     int part = 0;
     if constexpr (FUSED) {
-        uint32_t am = 0;
+        u16x2 am2 = {0, 0};
 #pragma unroll
         for (int j = 0; j < kMax; ++j)
-            if (lane + 64 * j < cpr)
-                am = max(am, absbits8(v[j]));
-        const float a = __uint_as_float(wave_umax(am));
+            if (lane + 64 * j < cpr) {
+                am2 = absmax_pair(am2, v[j].x);
+                am2 = absmax_pair(am2, v[j].y);
+                am2 = absmax_pair(am2, v[j].z);
+                am2 = absmax_pair(am2, v[j].w);
+            }
+        const float a = __uint_as_float(wave_umax(absmax_bits(am2)));
         // correctly rounded fp32 division (build flag), as in the
         // stand-alone quantizer; an all-zero row quantizes to zeros
         const float inv = a > 0.0f ? 127.0f / a : 0.0f;
