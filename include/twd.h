@@ -52,8 +52,14 @@ typedef enum {
  * choose (M1's "select by replay width and input/output dimensions"). */
 typedef enum {
     TWD_KERNEL_AUTO = 0,
-    TWD_KERNEL_DOT = 1,  /* VALU: 2-bit decode in registers + v_dot4 int8 */
-    TWD_KERNEL_MFMA = 2  /* matrix cores: v_mfma_i32_16x16x64_i8 */
+    /* straight-line VALU kernel: 2-bit decode in registers + v_dot4 int8;
+     * M <= 4 and M * ceil(K / 1024) <= 32 */
+    TWD_KERNEL_DOT = 1,
+    /* straight-line matrix-core kernel (v_mfma_i32_16x16x64_i8) where
+     * M * ceil(K / 1024) <= 32, else the staged one */
+    TWD_KERNEL_MFMA = 2,
+    /* matrix cores with separate activation-staging waves: any M, K */
+    TWD_KERNEL_MFMA_STAGED = 3
 } twd_kernel;
 
 /* Library version string; never NULL. */
@@ -161,8 +167,8 @@ twd_status twd_ternary_linear_bf16(const uint8_t *wpacked, int nseg,
                                    int kernel, void *stream);
 
 /* The kernel family the width dispatch picks for (M, K, N), without
- * launching anything.  Returns TWD_KERNEL_DOT or TWD_KERNEL_MFMA, or -1 if
- * the shape is unsupported. */
+ * launching anything.  Returns TWD_KERNEL_DOT, TWD_KERNEL_MFMA or
+ * TWD_KERNEL_MFMA_STAGED, or -1 if the shape is unsupported. */
 int twd_select_kernel(int64_t M, int64_t K, int64_t N);
 
 /* Measurement helper: a plain streaming read of `bytes` device bytes

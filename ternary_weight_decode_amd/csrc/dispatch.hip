@@ -1,20 +1,25 @@
 // Width dispatch -- M1's choice of "packed low-bit operators by replay width
 // and input/output dimensions" (BitMTP page, ai.info AI summary,
-// "Methodology in Plain English", paragraph 3): the VALU dot kernel for the
-// narrowest widths, the matrix-core kernel for the wider verification
-// widths, and the number of 16-row tiles per workgroup from the output size.
+// "Methodology in Plain English", paragraph 3): the straight-line kernels
+// while each wave's activation slices fit in registers (VALU dot for the
+// narrowest widths, matrix cores above), the staged matrix-core kernel
+// otherwise, and its 16-row tiles per workgroup from the output size.
 #include "twd_internal.h"
 
 namespace twd {
 
 LinearPlan plan_linear(int M, int K, int N, int forced_kernel) {
-    (void)K;
     LinearPlan p;
-    p.kernel = forced_kernel != TWD_KERNEL_AUTO
-                   ? forced_kernel
-                   : (M <= 4 ? TWD_KERNEL_DOT : TWD_KERNEL_MFMA);
-    const int tiles = (N + 15) / 16;
-    p.tiles = (p.kernel == TWD_KERNEL_MFMA && tiles >= 512) ? 2 : 1;
+    p.tiles = 1;
+    int k = forced_kernel;
+    if (k == TWD_KERNEL_AUTO)
+        k = (M <= 4 && narrow_supported(TWD_KERNEL_DOT, M, K)) ? TWD_KERNEL_DOT
+                                                                : TWD_KERNEL_MFMA;
+    if (k == TWD_KERNEL_MFMA && !narrow_supported(TWD_KERNEL_MFMA, M, K))
+        k = TWD_KERNEL_MFMA_STAGED;
+    p.kernel = k;
+    if (k == TWD_KERNEL_MFMA_STAGED && (N + 15) / 16 >= 512)
+        p.tiles = 2;
     return p;
 }
 
@@ -22,11 +27,11 @@ hipError_t launch_linear(const LinearPlan &plan, const uint8_t *w,
                          const void *act, bool fused, const float *xscale,
                          int M, int K, int N, const Segments &segs,
                          int32_t *acc, float *y, hipStream_t stream) {
-    if (plan.kernel == TWD_KERNEL_DOT)
-        return launch_dot(plan.tiles, w, act, fused, xscale, M, K, N, segs, acc, y,
-                          stream);
-    return launch_mfma(plan.tiles, w, act, fused, xscale, M, K, N, segs, acc, y,
-                       stream);
+    if (plan.kernel == TWD_KERNEL_MFMA_STAGED)
+        return launch_staged(plan.tiles, w, act, fused, xscale, M, K, N, segs, acc, y,
+                             stream);
+    return launch_narrow(plan.kernel, w, act, fused, xscale, M, K, N, segs, acc, y,
+                         stream);
 }
 
 }  // namespace twd

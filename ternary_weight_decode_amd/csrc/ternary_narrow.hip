@@ -1,0 +1,363 @@
+// Straight-line kernels of the W2A8 ternary linear, gfx950: one pass over the
+// weights with every load issued up front, for autoregressive steps (M = 1)
+// and drafted blocks whose activations fit in registers.
+//
+// What they compute (BitMTP page, ai.info AI summary): ternary BitNet b1.58
+// weights ("What This Paper Is About"), 8-bit activations ("Main Findings":
+// W2A8), and the packed low-bit operator M1 picks by replay width
+// ("Methodology in Plain English", paragraph 3):
+// acc[m][n] = sum_k q[m][k] t[n][k] in int32, y = acc * s_m * gamma(n).
+// With FUSED the per-token absmax int8 quantization of the bf16 activations
+// (same arithmetic as the stand-alone quantizer) happens inside.
+//
+// Work split.  A workgroup of four waves owns 16 weight rows and all of K.
+// Wave w takes the 256-wide K slices w, w + 4, ..., exactly U of them (U is a
+// compile-time count, so every load is straight-line code; a wave with one
+// slice fewer loads a slice whose activations are zero).  All loads are
+// buffer loads: 32-bit offsets against a descriptor whose size bound makes
+// out-of-range reads return zero, so rows past N and activations past K need
+// no clamping.  They are issued in order -- this wave's activation slices
+// first, then its weights -- so the wave waits for the activations alone
+// before staging them, and for each weight slice only when it is consumed:
+// quantization and decode overlap the weight stream.
+//
+// In one slice, lane l loads 16 bytes (64 weights) of row l % 16 at K offset
+// 256 s + 64 (l / 16); the wave covers 16 rows x 256 weights.  Each wave
+// stages the int8 activations of its own slices in a private LDS region, so
+// the only cross-wave synchronization is the row absmax (FUSED) and the
+// final sum.
+//
+// Decode.  A 32-bit word holds 16 codes c = t + 1; masking with 0x03030303,
+// 0x0C0C0C0C, 0x30303030 gives byte planes holding c, 4c, 16c for elements
+// 4j..4j+3 (j = 0, 1, 2) and (w >> 6) & 0x03030303 gives plane 3.  Each plane
+// pairs with one activation word; the planes scaled by 4 and 16 have their
+// own accumulators, shifted back exactly at the end; sum q t = sum q c -
+// sum q.
+//   DOT:  v_dot4 of each plane with the activation word, per token.
+//   MFMA: plane j of the lane's four words is the A operand of a
+//         16x16x64 int8 MFMA (row = lane % 16, K group = lane / 16); the
+//         tokens fill the B columns, a zero block beyond M.  The staged
+//         activations are stored permuted within each 16-word group so that
+//         one 16-byte LDS read yields a B operand.
+#include "kernel_common.h"
+
+namespace twd {
+namespace {
+
+using namespace kern;
+
+// Buffer resource word 3 for raw (untyped) loads on CDNA: 32-bit data format.
+constexpr int kRawBufferFlags = 0x00020000;
+// An offset past every buffer bound: the load returns zeros.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+template <int KIND>
+__host__ __device__ constexpr int parts() { return KIND == TWD_KERNEL_DOT ? 16 : kWaves; }
+
+// Per-wave LDS region: M x U staged slices, then (MFMA) a zero block.
+template <int M, int U>
+__host__ __device__ constexpr int wave_bytes() { return M * U * 256 + 64; }
+
+// LDS: per-wave regions | partials [M][16 rows][parts] | absmax partials
+// [wave][M] | row-sum partials [wave][M].
+template <int KIND, int M, int U>
+__host__ __device__ constexpr int lds_bytes() {
+    return kWaves * wave_bytes<M, U>() + M * 16 * parts<KIND>() * 4 + 2 * kWaves * M * 4;
+}
+
+// Where lane l's activation word (elements 4l..4l+3 of the slice) is staged.
+// MFMA: word 16g + 4d + j goes to 16g + 4j + d, so the four words of plane j
+// of K group g are contiguous.
+template <int KIND>
+__device__ __forceinline__ int staged_word(int lane) {
+    if constexpr (KIND == TWD_KERNEL_DOT)
+        return lane;
+    return (lane & 48) | ((lane & 3) << 2) | ((lane >> 2) & 3);
+}
+
+template <int KIND, int M, int U, bool FUSED>
+__global__ __launch_bounds__(kThreads) void narrow_kernel(
+    const uint8_t *__restrict__ W, const void *__restrict__ act,
+    const float *__restrict__ xscale, int K, int N, Segments segs,
+    int32_t *__restrict__ acc, float *__restrict__ y) {
+    constexpr int P = parts<KIND>();
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 15;
+    const int g = lane >> 4;
+    const int n0 = blockIdx.x * 16;
+    const int row_bytes = K >> 2;
+
+    uint8_t *own = smem + wave * wave_bytes<M, U>();
+    int32_t *red = reinterpret_cast<int32_t *>(smem + kWaves * wave_bytes<M, U>());
+    uint32_t *st_max = reinterpret_cast<uint32_t *>(red + M * 16 * P);
+    int32_t *st_sum = reinterpret_cast<int32_t *>(st_max + kWaves * M);
+
+    // 1. activation loads: lane l takes elements 256 s + 4 l .. + 3 of each
+    //    row for this wave's slices s = wave + 4 u (zeros past K)
+    constexpr int kEl = FUSED ? 2 : 1;  // bytes per element
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void *>(act), 0, M * K * kEl, kRawBufferFlags);
+    uint2 xb[FUSED ? M : 1][U];
+    uint32_t xi[FUSED ? 1 : M][U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int k0 = 256 * (wave + kWaves * u) + 4 * lane;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const uint32_t off =
+                k0 < K ? static_cast<uint32_t>((m * K + k0) * kEl) : kOutOfRange;
+            if constexpr (FUSED) {
+                const auto v = __builtin_amdgcn_raw_buffer_load_b64(xr, off, 0, 0);
+                xb[m][u] = make_uint2(v[0], v[1]);
+            } else {
+                xi[m][u] = __builtin_amdgcn_raw_buffer_load_b32(xr, off, 0, 0);
+            }
+        }
+    }
+
+    // 2. weight loads against this workgroup's 16 rows; rows past N fall
+    //    outside the descriptor (zeros, never stored), K groups past the
+    //    row end read the next row (their activations are zero)
+    const int rows = min(16, N - n0);
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(W + static_cast<int64_t>(n0) * row_bytes), 0,
+        rows * row_bytes, kRawBufferFlags);
+    const uint32_t wbase = static_cast<uint32_t>(r * row_bytes + 16 * g);
+    uint4 a[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(
+            wr, wbase + 64u * static_cast<uint32_t>(wave + kWaves * u), 0, 0);
+        a[u] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+    // keep every load issued before any use (the scheduler would otherwise
+    // hoist activation math, and its wait, above the weight loads)
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 3. own activation slices -> LDS as int8, with this wave's row sums
+    const int slot = 4 * staged_word<KIND>(lane);
+    int sq[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+        sq[m] = 0;
+    if constexpr (FUSED) {
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            u16x2 am2 = {0, 0};
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                am2 = absmax_pair(am2, xb[m][u].x);
+                am2 = absmax_pair(am2, xb[m][u].y);
+            }
+            const uint32_t am = wave_umax(absmax_bits(am2));
+            if (lane == 0)
+                st_max[wave * M + m] = am;
+        }
+        __syncthreads();  // row absmax partials (LDS only)
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            uint32_t am = st_max[m];
+#pragma unroll
+            for (int w = 1; w < kWaves; ++w)
+                am = max(am, st_max[w * M + m]);
+            const float a_m = __uint_as_float(am);
+            // correctly rounded fp32 division (build flag), as in the
+            // stand-alone quantizer; an all-zero row quantizes to zeros
+            const float inv = a_m > 0.0f ? 127.0f / a_m : 0.0f;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t q = quant4(xb[m][u].x, xb[m][u].y, inv);
+                *reinterpret_cast<uint32_t *>(own + (m * U + u) * 256 + slot) = q;
+                sq[m] = sdot4(q, kOnes, sq[m]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                *reinterpret_cast<uint32_t *>(own + (m * U + u) * 256 + slot) = xi[m][u];
+                sq[m] = sdot4(xi[m][u], kOnes, sq[m]);
+            }
+    }
+    if constexpr (KIND == TWD_KERNEL_MFMA) {
+        if (lane < 4)  // zero block behind the token columns past M
+            *reinterpret_cast<uint4 *>(own + M * U * 256 + 16 * lane) = make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const int s = wave_sum(sq[m]);
+        if (lane == 0)
+            st_sum[wave * M + m] = s;
+    }
+    // the wave reads back only its own LDS region: its writes are ordered
+    // before its reads, no workgroup barrier needed
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // 4. decode + multiply-accumulate, one slice at a time as it arrives
+    if constexpr (KIND == TWD_KERNEL_DOT) {
+        int d1[M], d4[M], d16[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+            d1[m] = d4[m] = d16[m] = 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int dw = 0; dw < 4; ++dw) {
+                uint4 x[M];
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+                    x[m] = *reinterpret_cast<const uint4 *>(own + (m * U + u) * 256 + 64 * g + 16 * dw);
+                const uint32_t w = dw == 0 ? a[u].x : dw == 1 ? a[u].y : dw == 2 ? a[u].z : a[u].w;
+                const uint32_t p0 = w & kPlane0;
+                const uint32_t p1 = w & kPlane1;
+                const uint32_t p2 = w & kPlane2;
+                const uint32_t p3 = (w >> 6) & kPlane0;
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    d1[m] = sdot4(p0, x[m].x, d1[m]);
+                    d4[m] = sdot4(p1, x[m].y, d4[m]);
+                    d16[m] = sdot4(p2, x[m].z, d16[m]);
+                    d1[m] = sdot4(p3, x[m].w, d1[m]);
+                }
+            }
+        }
+        // partials [M][16 rows][wave, K group]
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+            red[(m * 16 + r) * P + wave * 4 + g] = d1[m] + (d4[m] >> 2) + (d16[m] >> 4);
+    } else {
+        v4i c0 = {0, 0, 0, 0}, c3 = c0, c4 = c0, c16 = c0;
+        // B operand of plane j: token r's K group g; columns past M read
+        // the zero block
+        const uint8_t *bsrc = r < M ? own + r * (U * 256) + 64 * g : own + M * U * 256;
+        const int ustep = r < M ? 256 : 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint8_t *bu = bsrc + u * ustep;
+            const v4i b0 = *reinterpret_cast<const v4i *>(bu);
+            const v4i b1 = *reinterpret_cast<const v4i *>(bu + 16);
+            const v4i b2 = *reinterpret_cast<const v4i *>(bu + 32);
+            const v4i b3 = *reinterpret_cast<const v4i *>(bu + 48);
+            const v4i w = {static_cast<int>(a[u].x), static_cast<int>(a[u].y),
+                           static_cast<int>(a[u].z), static_cast<int>(a[u].w)};
+            const v4i p0 = w & static_cast<int>(kPlane0);
+            const v4i p1 = w & static_cast<int>(kPlane1);
+            const v4i p2 = w & static_cast<int>(kPlane2);
+            const v4i p3 = (w >> 6) & static_cast<int>(kPlane0);
+            c0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(p0, b0, c0, 0, 0, 0);
+            c4 = __builtin_amdgcn_mfma_i32_16x16x64_i8(p1, b1, c4, 0, 0, 0);
+            c16 = __builtin_amdgcn_mfma_i32_16x16x64_i8(p2, b2, c16, 0, 0, 0);
+            c3 = __builtin_amdgcn_mfma_i32_16x16x64_i8(p3, b3, c3, 0, 0, 0);
+        }
+        // lane (r, g) holds rows 4g .. 4g+3 of token r: partials [M][16][wave]
+        const v4i c = c0 + c3 + (c4 >> 2) + (c16 >> 4);
+        if (r < M) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                red[(r * 16 + 4 * g + i) * P + wave] = c[i];
+        }
+    }
+
+    // 5. one thread per output adds its partials, takes off the row sum and
+    //    dequantizes
+    __syncthreads();
+    for (int idx = tid; idx < M * 16; idx += kThreads) {
+        const int m = idx >> 4;
+        const int n = n0 + (idx & 15);
+        if (n >= N)
+            continue;
+        int total = 0;
+#pragma unroll
+        for (int p = 0; p < P; p += 4) {
+            const int4 v = *reinterpret_cast<const int4 *>(red + idx * P + p);
+            total += v.x + v.y + v.z + v.w;
+        }
+        float scale;
+        if constexpr (FUSED) {
+            uint32_t am = st_max[m];
+#pragma unroll
+            for (int w = 1; w < kWaves; ++w)
+                am = max(am, st_max[w * M + m]);
+            scale = __uint_as_float(am) / 127.0f;
+        } else {
+            scale = xscale[m];
+        }
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w)
+            total -= st_sum[w * M + m];
+        const int64_t o = static_cast<int64_t>(m) * N + n;
+        if (acc)
+            acc[o] = total;
+        if (y)
+            y[o] = static_cast<float>(total) * scale * row_gamma(segs, n);
+    }
+}
+
+using Fn = void (*)(const uint8_t *, const void *, const float *, int, int, Segments,
+                    int32_t *, float *);
+
+template <int KIND, int M, bool FUSED, int... Us>
+bool pick_u(int U, Fn *fn, int *lds) {
+    bool found = false;
+    auto take = [&](auto uc) {
+        constexpr int Uc = decltype(uc)::value;
+        if constexpr (narrow_fits(M, Uc)) {
+            *fn = &narrow_kernel<KIND, M, Uc, FUSED>;
+            *lds = lds_bytes<KIND, M, Uc>();
+            found = true;
+        }
+    };
+    ((U == Us ? (take(std::integral_constant<int, Us>{}), 0) : 0), ...);
+    return found;
+}
+
+template <int KIND, bool FUSED, int... Ms>
+bool pick_m(int M, int U, Fn *fn, int *lds) {
+    bool found = false;
+    ((M == Ms ? (found = pick_u<KIND, Ms, FUSED, 1, 2, 3, 4, 5, 6, 7, 8>(U, fn, lds)) : false),
+     ...);
+    return found;
+}
+
+}  // namespace
+
+bool narrow_supported(int kernel, int M, int K) {
+    const int U = (K + 1023) / 1024;
+    if (kernel == TWD_KERNEL_DOT)
+        return M >= 1 && M <= 4 && narrow_fits(M, U);
+    return M >= 1 && M <= TWD_MAX_M && narrow_fits(M, U);
+}
+
+hipError_t launch_narrow(int kernel, const uint8_t *w, const void *act, bool fused,
+                         const float *xscale, int M, int K, int N,
+                         const Segments &segs, int32_t *acc, float *y,
+                         hipStream_t stream) {
+    const int U = (K + 1023) / 1024;  // 256-wide slices per wave
+    Fn fn = nullptr;
+    int lds = 0;
+    bool ok = false;
+    if (kernel == TWD_KERNEL_DOT)
+        ok = fused ? pick_m<TWD_KERNEL_DOT, true, 1, 2, 3, 4>(M, U, &fn, &lds)
+                   : pick_m<TWD_KERNEL_DOT, false, 1, 2, 3, 4>(M, U, &fn, &lds);
+    else
+        ok = fused ? pick_m<TWD_KERNEL_MFMA, true, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12,
+                            13, 14, 15, 16>(M, U, &fn, &lds)
+                   : pick_m<TWD_KERNEL_MFMA, false, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12,
+                            13, 14, 15, 16>(M, U, &fn, &lds);
+    if (!ok)
+        return hipErrorInvalidValue;
+    hipError_t e = ensure_lds_limit(reinterpret_cast<const void *>(fn), lds);
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(fn, dim3((N + 15) / 16), dim3(kThreads), lds, stream, w, act,
+                       xscale, K, N, segs, acc, y);
+    return hipGetLastError();
+}
+
+}  // namespace twd

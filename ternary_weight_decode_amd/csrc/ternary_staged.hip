@@ -272,7 +272,7 @@ using Widths = Table<TW, FUSED, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 1
 
 }  // namespace
 
-hipError_t launch_mfma(int tiles, const uint8_t *w, const void *act, bool fused,
+hipError_t launch_staged(int tiles, const uint8_t *w, const void *act, bool fused,
                        const float *xscale, int M, int K, int N,
                        const Segments &segs, int32_t *acc, float *y,
                        hipStream_t stream) {

@@ -19,9 +19,13 @@ struct Segments {
 
 // Launch parameters the width dispatch chose for one linear call.
 struct LinearPlan {
-    int kernel;  // TWD_KERNEL_DOT or TWD_KERNEL_MFMA
-    int tiles;   // 16-row tiles per workgroup
+    int kernel;  // TWD_KERNEL_DOT, TWD_KERNEL_MFMA or TWD_KERNEL_MFMA_STAGED
+    int tiles;   // 16-row tiles per workgroup (staged kernel)
 };
+
+// The straight-line kernels hold each wave's activation slices in registers
+// (M x U words, U = 256-wide K slices per wave): they exist for M * U <= 32.
+constexpr bool narrow_fits(int M, int U) { return U >= 1 && U <= 8 && M * U <= 32; }
 
 // Thread-local error message; returns `st` for convenient chaining.
 twd_status set_error(twd_status st, const char *fmt, ...);
@@ -38,13 +42,15 @@ hipError_t launch_linear(const LinearPlan &plan, const uint8_t *w,
                          int M, int K, int N, const Segments &segs,
                          int32_t *acc, float *y, hipStream_t stream);
 
-// The two kernel families (ternary_dot.hip: M <= 4; ternary_mfma.hip:
-// M <= 16).  tiles = 16-row tiles per workgroup.
-hipError_t launch_dot(int tiles, const uint8_t *w, const void *act, bool fused,
-                      const float *xscale, int M, int K, int N,
-                      const Segments &segs, int32_t *acc, float *y,
-                      hipStream_t stream);
-hipError_t launch_mfma(int tiles, const uint8_t *w, const void *act, bool fused,
+// Straight-line kernels (ternary_narrow.hip), kernel = TWD_KERNEL_DOT
+// (M <= 4) or TWD_KERNEL_MFMA, for the (M, K) narrow_supported accepts.
+bool narrow_supported(int kernel, int M, int K);
+hipError_t launch_narrow(int kernel, const uint8_t *w, const void *act, bool fused,
+                         const float *xscale, int M, int K, int N,
+                         const Segments &segs, int32_t *acc, float *y,
+                         hipStream_t stream);
+// Staged matrix-core kernel (ternary_staged.hip): any M <= 16 and K.
+hipError_t launch_staged(int tiles, const uint8_t *w, const void *act, bool fused,
                        const float *xscale, int M, int K, int N,
                        const Segments &segs, int32_t *acc, float *y,
                        hipStream_t stream);

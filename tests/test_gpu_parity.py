@@ -117,44 +117,35 @@ def test_quantize_act_ties(env):
 # ------------------------------------------------------------------- linear
 
 SMALL_SHAPES = [
-    (64, (1,)),           # one partial super chunk, one row
-    (320, (17,)),         # partial last super chunk, ragged tile
-    (2560, (130,)),       # ten full super chunks, ragged tail
+    (64, (1,)),            # one partial slice, one row; three waves idle
+    (320, (17,)),          # partial last slice, ragged tile
+    (2560, (130,)),        # ten full slices, ragged tail
     (1536, (64, 33, 33)),  # three segments, ragged
-    (768, (50, 50)),      # two segments
+    (768, (50, 50)),       # two segments
+    (6912, (33,)),         # 27 slices: seven per wave, one wave a slice short
+    (8192, (20,)),         # the largest K
 ]
 
+# (kernel family, widest M it takes); KERNEL_MFMA runs the straight-line
+# matrix-core kernel where its registers allow and the staged one otherwise
+FAMILIES = [("dot", 4), ("mfma", 16), ("mfma_staged", 16)]
 
+
+def family(twd, name):
+    return {"dot": twd.KERNEL_DOT, "mfma": twd.KERNEL_MFMA,
+            "mfma_staged": twd.KERNEL_MFMA_STAGED}[name]
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["int8", "bf16"])
 @pytest.mark.parametrize("K,segs", SMALL_SHAPES)
 @pytest.mark.parametrize("M", list(range(1, 17)))
-def test_mfma_kernel_parity(env, M, K, segs):
+@pytest.mark.parametrize("fam,max_m", FAMILIES)
+def test_kernel_parity(env, fam, max_m, M, K, segs, fused):
+    if M > max_m:
+        pytest.skip(f"{fam} takes M <= {max_m}")
     torch, twd, orc = env
     W, segs, x = wl.random_case(seed=1, M=M, K=K, seg_rows=segs)
-    run_case(env, W, segs, x, twd.KERNEL_MFMA, ("rand", 1, K, segs))
-
-
-@pytest.mark.parametrize("K,segs", SMALL_SHAPES)
-@pytest.mark.parametrize("M", list(range(1, 5)))
-def test_dot_kernel_parity(env, M, K, segs):
-    torch, twd, orc = env
-    W, segs, x = wl.random_case(seed=1, M=M, K=K, seg_rows=segs)
-    run_case(env, W, segs, x, twd.KERNEL_DOT, ("rand", 1, K, segs))
-
-
-@pytest.mark.parametrize("K,segs", SMALL_SHAPES)
-@pytest.mark.parametrize("M", list(range(1, 17)))
-def test_fused_bf16_mfma_parity(env, M, K, segs):
-    torch, twd, orc = env
-    W, segs, x = wl.random_case(seed=1, M=M, K=K, seg_rows=segs)
-    run_case(env, W, segs, x, twd.KERNEL_MFMA, ("rand", 1, K, segs), fused=True)
-
-
-@pytest.mark.parametrize("K,segs", SMALL_SHAPES)
-@pytest.mark.parametrize("M", list(range(1, 5)))
-def test_fused_bf16_dot_parity(env, M, K, segs):
-    torch, twd, orc = env
-    W, segs, x = wl.random_case(seed=1, M=M, K=K, seg_rows=segs)
-    run_case(env, W, segs, x, twd.KERNEL_DOT, ("rand", 1, K, segs), fused=True)
+    run_case(env, W, segs, x, family(twd, fam), ("rand", 1, K, segs), fused=fused)
 
 
 @pytest.mark.parametrize("M", [1, 2, 3, 8, 16])
@@ -167,7 +158,8 @@ def test_fused_bf16_zero_rows_and_outliers(env, M):
     if M > 1:
         xf[1, ::97] *= 20.0
     x = wl.f32_to_bf16_bits(xf)
-    for kernel in (twd.KERNEL_MFMA, twd.KERNEL_DOT) if M <= 4 else (twd.KERNEL_MFMA,):
+    for kernel in ((twd.KERNEL_MFMA, twd.KERNEL_MFMA_STAGED, twd.KERNEL_DOT) if M <= 4
+                   else (twd.KERNEL_MFMA, twd.KERNEL_MFMA_STAGED)):
         acc, y = run_case(env, W, segs, x, kernel, ("rand", 7), fused=True)
         assert not acc[0].any() and not y[0].any()
 
@@ -185,7 +177,7 @@ def test_single_linear_workload(env):
     """The single-linear case: M=1, K=256, N=512, seed 0."""
     torch, twd, orc = env
     W, segs, x = wl.single_case(seed=0)
-    for kernel in (twd.KERNEL_AUTO, twd.KERNEL_DOT, twd.KERNEL_MFMA):
+    for kernel in (twd.KERNEL_AUTO, twd.KERNEL_DOT, twd.KERNEL_MFMA, twd.KERNEL_MFMA_STAGED):
         for fused in (False, True):
             run_case(env, W, segs, x, kernel, ("single", 0), fused=fused)
 
@@ -197,13 +189,13 @@ def test_width_invariance(env):
     wp, gammas = prepared(twd, torch, W, segs, ("rand", 3))
     xq, xs = twd.quantize_act(to_dev_bf16(torch, x))
     full = {}
-    for kernel in (twd.KERNEL_MFMA, twd.KERNEL_DOT):
-        for M in (16, 8, 4, 1) if kernel == twd.KERNEL_MFMA else (4, 2, 1):
+    for kernel in (twd.KERNEL_MFMA_STAGED, twd.KERNEL_MFMA, twd.KERNEL_DOT):
+        for M in (4, 2, 1) if kernel == twd.KERNEL_DOT else (16, 10, 8, 4, 1):
             acc, _ = twd.ternary_linear_fused(wp, segs, gammas, xq[:M].contiguous(),
                                               xs[:M].contiguous(), kernel=kernel)
             full[(kernel, M)] = acc
     torch.cuda.synchronize()
-    ref = full[(twd.KERNEL_MFMA, 16)]
+    ref = full[(twd.KERNEL_MFMA_STAGED, 16)]
     for (kernel, M), acc in full.items():
         assert torch.equal(acc, ref[:M]), (kernel, M)
 
@@ -248,7 +240,7 @@ def test_invariants_on_gpu(env):
     codes[2] = -1
     wp = torch.from_numpy(twd.pack_ternary(codes)).cuda()
     xq, xs = twd.quantize_act(to_dev_bf16(torch, x))
-    for kernel in (twd.KERNEL_DOT, twd.KERNEL_MFMA):
+    for kernel in (twd.KERNEL_DOT, twd.KERNEL_MFMA, twd.KERNEL_MFMA_STAGED):
         acc, y = twd.ternary_linear_fused(wp, (N,), (1.0,), xq, xs, kernel=kernel)
         torch.cuda.synchronize()
         a = acc.cpu().numpy()
@@ -268,8 +260,8 @@ def test_extreme_values(env):
     x = wl.f32_to_bf16_bits(xf)
     W = np.ones((N, K), np.float32)
     W[::3] = -1.0
-    for kernel in (twd.KERNEL_MFMA, twd.KERNEL_DOT):
-        xs_ = x if kernel == twd.KERNEL_MFMA else x[:4]
+    for kernel in (twd.KERNEL_MFMA_STAGED, twd.KERNEL_MFMA, twd.KERNEL_DOT):
+        xs_ = x[:4] if kernel == twd.KERNEL_DOT else x
         acc, _ = run_case(env, W, (N,), xs_, kernel, ("extreme",))
         assert abs(int(acc.abs().max())) == 127 * K
 
