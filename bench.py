@@ -163,6 +163,74 @@ def stream_read_reference(twd, torch, dev_set, reps):
     return dev_set.bytes_per_sweep * reps / sec / 1e9, sec / (reps * len(keys))
 
 
+def kernel_map(twd, ls, M, kernel):
+    """Kernel family each projection of the set runs at width M (a forced
+    KERNEL_MFMA runs the staged form where the straight-line one does not
+    fit: M * ceil(K / 1024) > 32)."""
+    out = {}
+    for p in ls.projs:
+        if kernel == twd.KERNEL_AUTO:
+            k = twd.select_kernel(M, p.K, p.N)
+        elif kernel == twd.KERNEL_MFMA and M * (-(-p.K // 1024)) > 32:
+            k = twd.KERNEL_MFMA_STAGED
+        else:
+            k = kernel
+        out[p.name] = twd.KERNEL_NAMES[k]
+    return out
+
+
+def per_projection(twd, torch, ls, M, kernel, reps, target_bytes=640 << 20):
+    """Each projection shape on its own, cold: one graph cycles through
+    enough distinct weight buffers (random packed bytes; the kernels' timing
+    does not depend on the codes) to exceed the 256 MB Infinity Cache.  The
+    plain streaming read over the same buffers is timed beside it."""
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    table = {}
+    for p in ls.projs:
+        nbytes = p.N * p.K // 4
+        copies = max(8, -(-target_bytes // nbytes))
+        ws = [torch.randint(0, 256, (p.N, p.K // 4), dtype=torch.uint8, device="cuda",
+                            generator=gen) for _ in range(copies)]
+        x = torch.randn((M, p.K), device="cuda", generator=gen).to(torch.bfloat16)
+        y = torch.empty((M, p.N), dtype=torch.float32, device="cuda")
+        gam = [1.0] * len(p.segs)
+
+        def lin():
+            for w in ws:
+                twd.ternary_linear_bf16(w, p.segs, gam, x, y=y, want_acc=False, kernel=kernel)
+
+        def ref():
+            for w in ws:
+                twd.stream_read(w, nbytes, sink)
+
+        row = {"K": p.K, "N": p.N, "bytes": nbytes}
+        for name, fn in (("linear", lin), ("stream_read", ref)):
+            g = capture(torch, fn)
+            g.replay()
+            _, sec = time_replays(torch, g, reps)
+            per = sec / (reps * copies)
+            row[f"{name}_us"] = round(per * 1e6, 3)
+            row[f"{name}_gbs"] = round(nbytes / per / 1e9, 1)
+            del g
+        table[p.name] = row
+        del ws
+        torch.cuda.empty_cache()
+    return table
+
+
+def copy_calibration(twd, torch, nbytes=256 << 20, reps=3):
+    """Plain copies of known size, for the HBM byte-counter calibration."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    for _ in range(reps):
+        twd.stream_copy(src, dst, nbytes)
+    torch.cuda.synchronize()
+    return nbytes
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "ternary_weight_decode_amd", "csrc")
@@ -186,10 +254,11 @@ def counter_traffic(workload, M, launches_bytes):
 
 
 def cpu_baseline(ls, workload, M, outliers, budget_s):
-    """The CPU oracle (quantize, int8 x ternary loops, dequant) on the layers
-    of the set, in order, until its compute time passes budget_s; timed on
-    the host's cores.  Setup (weight generation and the oracle's own
-    ternarization, a few layers ahead in a thread pool) is not timed."""
+    """The CPU oracle (quantize, int8 x ternary loops, dequant) over the
+    layers of the set in order, repeating whole passes until its compute time
+    reaches budget_s; timed on the host's cores.  Setup (weight generation and
+    the oracle's own ternarization, in a thread pool, all before timing) is
+    not timed."""
     import oracle
     oracle.build(force=False)
     threads = host_threads()
@@ -202,26 +271,177 @@ def cpu_baseline(ls, workload, M, outliers, budget_s):
         x = wl.layer_activations(workload, p.K, M, layer, pi, outliers=outliers)
         return p, t, grow, x
 
-    done_bytes, spent, layers = 0, 0.0, 0
     keys = [(l, p) for l in range(ls.layers) for p in range(len(ls.projs))]
-    chunk = 4 * len(ls.projs)
+    done_bytes, spent, passes = 0, 0.0, 0
+
+    def run(item):
+        nonlocal done_bytes, spent
+        p, t, grow, x = item
+        t0 = time.perf_counter()
+        q, s = oracle.quantize_act(x)
+        acc = oracle.linear(q, t, threads)
+        oracle.dequant(acc, s, grow)
+        spent += time.perf_counter() - t0
+        done_bytes += p.packed_bytes
+
     with ThreadPoolExecutor(max_workers=threads) as ex:
-        for c0 in range(0, len(keys), chunk):
-            for p, t, grow, x in ex.map(prep, keys[c0:c0 + chunk]):
-                t0 = time.perf_counter()
-                q, s = oracle.quantize_act(x)
-                acc = oracle.linear(q, t, threads)
-                oracle.dequant(acc, s, grow)
-                spent += time.perf_counter() - t0
-                done_bytes += p.packed_bytes
-            layers = min(ls.layers, (c0 + chunk) // len(ls.projs))
-            if spent >= budget_s:
-                break
+        prepared = list(ex.map(prep, keys))
+    while passes == 0 or spent < budget_s:
+        for item in prepared:
+            run(item)
+        passes += 1
     return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{layers} of {ls.layers} layers of the {ls.name.upper()} set at M={M} "
-                      f"(all 4 projections each: quantize + int32 contraction + dequant; "
-                      f"{spent:.2f} s of CPU time; throughput in packed-weight bytes/s)"}
+            "sample": f"{passes} pass(es) over all {ls.layers} layers of the {ls.name.upper()} set "
+                      f"at M={M} (4 projections each: quantize + int32 contraction + dequant; "
+                      f"{spent:.1f} s of CPU time; throughput in packed-weight bytes/s)"}
+
+
+# --------------------------------------------------------------------------
+# rocprofv3 summaries (no GPU): CSV output of this script under
+# `rocprofv3 --kernel-trace --stats -f csv` and two `--pmc` passes
+# (FETCH_SIZE, WRITE_SIZE) -> short text summaries plus the counter record
+# counter_traffic() reads.
+
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    paths = sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+    if not paths:
+        raise SystemExit(f"no *{suffix} under {d}")
+    rows = []
+    for path in paths:
+        with open(path, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def _col(row, *names):
+    low = {k.lower(): v for k, v in row.items()}
+    for n in names:
+        if n.lower() in low:
+            return low[n.lower()]
+    raise KeyError(f"none of {names} in {list(row)}")
+
+
+def _short(name):
+    return (name.replace("void ", "").replace("twd::(anonymous namespace)::", "")
+            .split("(")[0].strip())
+
+
+def _linear_fused(name):
+    """The one-launch (fused quantization) instances of the linear kernels."""
+    short = _short(name)
+    return (short.startswith(("narrow_kernel<", "staged_kernel<"))
+            and short.endswith("true>"))
+
+
+def summarize_profiles(args):
+    trace_dir, fetch_dir, write_dir = args.summarize_profile
+    cmds = args.profile_commands or ("?", "?", "?")
+    ls = wl.LAYER_SETS["4b" if args.workload.startswith("4b") else "2b"]
+    M = args.M or wl.workload_widths(args.workload)[0]
+    nproj = len(ls.projs)
+    out_dir = args.profile_out
+    os.makedirs(out_dir, exist_ok=True)
+    tag = f"{args.workload}_m{M}"
+
+    # kernel trace: the timed steps are the last steps x launches dispatches
+    # of the fused linear kernels (nothing else launches them afterwards)
+    stats = _csv_rows(trace_dir, "kernel_stats.csv")
+    trace = _csv_rows(trace_dir, "kernel_trace.csv")
+    lin = [r for r in trace if _linear_fused(_col(r, "Kernel_Name"))]
+    lin.sort(key=lambda r: int(_col(r, "Start_Timestamp")))
+    timed = lin[-args.steps * ls.layers * nproj:]
+    durs = [int(_col(r, "End_Timestamp")) - int(_col(r, "Start_Timestamp")) for r in timed]
+    avg_ns = sum(durs) / len(durs)
+    span_ns = int(_col(timed[-1], "End_Timestamp")) - int(_col(timed[0], "Start_Timestamp"))
+    lines = [f"# ternary linear, {args.workload}, M={M}: rocprofv3 kernel trace", "",
+             "Command (from the repository root):", "", "    " + cmds[0], "",
+             "## Kernel statistics (rocprofv3 --stats)", "",
+             "| kernel | calls | total us | average us | min us | max us |",
+             "|---|---|---|---|---|---|"]
+    stats.sort(key=lambda r: -float(_col(r, "TotalDurationNs")))
+    for r in stats[:12]:
+        lines.append(f"| `{_short(_col(r, 'Name'))}` | {_col(r, 'Calls')} | "
+                     f"{float(_col(r, 'TotalDurationNs')) / 1e3:.1f} | "
+                     f"{float(_col(r, 'AverageNs')) / 1e3:.3f} | {float(_col(r, 'MinNs')) / 1e3:.3f} | "
+                     f"{float(_col(r, 'MaxNs')) / 1e3:.3f} |")
+    lines += ["", f"## The timed region: the last {len(timed)} fused linear dispatches "
+              f"({args.steps} steps x {ls.layers * nproj} launches)", "",
+              "| projection | K | N | dispatches | average us | GB/s (K*N/4 bytes) |",
+              "|---|---|---|---|---|---|"]
+    # within a step the launches go layer by layer, projections in set order
+    for pi, p in enumerate(ls.projs):
+        ent = durs[pi::nproj]
+        a = sum(ent) / len(ent)
+        lines.append(f"| {p.name} | {p.K} | {p.N} | {len(ent)} | {a / 1e3:.3f} | "
+                     f"{p.packed_bytes / a:.1f} |")
+    lines += ["", f"Average duration over the timed dispatches: **{avg_ns / 1e3:.3f} us** "
+              f"(algorithmic bytes per launch {ls.packed_bytes_per_layer / nproj / 1e6:.3f} MB "
+              f"-> {ls.packed_bytes_per_layer / nproj / avg_ns:.1f} GB/s); first start to "
+              f"last end {span_ns / 1e3:.1f} us.", ""]
+    trace_path = os.path.join(out_dir, f"ternary_linear_{tag}_kernel_trace.md")
+    with open(trace_path, "w") as f:
+        f.write("\n".join(lines))
+
+    # counters: KiB per dispatch, scaled by the copy kernel's reading
+    def per_kernel(d, counter):
+        rows = [r for r in _csv_rows(d, "counter_collection.csv")
+                if _col(r, "Counter_Name") == counter]
+        agg = {}
+        for r in rows:
+            name = _col(r, "Kernel_Name")
+            g = int(_col(r, "Grid_Size", "Grid_Size_X", "grid_size"))
+            agg.setdefault((name, g), []).append(float(_col(r, "Counter_Value")))
+        return agg
+
+    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
+    write = per_kernel(write_dir, "WRITE_SIZE")
+    copy_bytes = 256 << 20
+
+    def copy_factor(agg):
+        vals = [v for (n, _), vs in agg.items() if "stream_copy_kernel" in n for v in vs]
+        return copy_bytes / (sum(vals) / len(vals) * 1024.0), sum(vals) / len(vals)
+
+    f_fetch, copy_fetch_kib = copy_factor(fetch)
+    f_write, copy_write_kib = copy_factor(write)
+
+    def lin_mean(agg):
+        vals = [v for (n, _), vs in agg.items() if _linear_fused(n) for v in vs]
+        return sum(vals) / len(vals), len(vals)
+
+    lf, nf = lin_mean(fetch)
+    lw, nw = lin_mean(write)
+    hbm = lf * 1024 * f_fetch + lw * 1024 * f_write
+    alg = ls.packed_bytes_per_layer / nproj
+    lines = [f"# ternary linear, {args.workload}, M={M}: HBM bytes from rocprofv3 counters", "",
+             "Commands (from the repository root), one counter per run:", "",
+             "    " + cmds[1], "", "    " + cmds[2], "",
+             f"Calibration: the plain copy kernel (`stream_copy_kernel`) moves {copy_bytes} bytes "
+             f"each way per dispatch; FETCH_SIZE reads {copy_fetch_kib:.1f} KiB -> factor "
+             f"{f_fetch:.4f}; WRITE_SIZE reads {copy_write_kib:.1f} KiB -> factor {f_write:.4f}.", "",
+             "| kernel | grid WGs | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (calibrated) |",
+             "|---|---|---|---|---|---|"]
+    for (n, g), vs in sorted(fetch.items(), key=lambda kv: _short(kv[0][0])):
+        wv = write.get((n, g), [0.0])
+        fm, wm = sum(vs) / len(vs), sum(wv) / len(wv)
+        lines.append(f"| `{_short(n)}` | {g // 256} | {len(vs)} | {fm:.1f} | {wm:.1f} | "
+                     f"{fm * 1024 * f_fetch + wm * 1024 * f_write:,.0f} |")
+    lines += ["", f"Fused linear, mean over {nf} dispatches: FETCH {lf:.1f} KiB, WRITE {lw:.1f} KiB "
+              f"-> **{hbm:,.0f} HBM bytes per launch** against {alg:,.0f} algorithmic "
+              f"(packed weights) = {hbm / alg:.3f}x.", ""]
+    cnt_path = os.path.join(out_dir, f"ternary_linear_{tag}_hbm_counters.md")
+    with open(cnt_path, "w") as f:
+        f.write("\n".join(lines))
+    rec = {"source_hash": kernel_source_hash(), "workload": args.workload, "M": M,
+           "hbm_bytes_per_launch": round(hbm), "algorithmic_bytes_per_launch": round(alg),
+           "fetch_factor": round(f_fetch, 5), "write_factor": round(f_write, 5),
+           "summary": os.path.basename(cnt_path)}
+    with open(os.path.join(out_dir, f"ternary_linear_counters_{tag}.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    print(trace_path)
+    print(cnt_path)
 
 
 def main():
@@ -232,13 +452,27 @@ def main():
     ap.add_argument("--workload", default="2b_decode",
                     choices=["2b_decode", "2b_verify", "2b_sweep_outlier", "4b_stack"])
     ap.add_argument("--M", type=int, default=None, help="width (default: the workload's first)")
-    ap.add_argument("--kernel", default="auto", choices=["auto", "dot", "mfma"])
+    ap.add_argument("--kernel", default="auto", choices=["auto", "dot", "mfma", "mfma_staged"])
     ap.add_argument("--widths", default="1,2,4,8,16",
                     help="widths for the per-width linear table ('' to skip)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU oracle budget (0 skips the CPU baseline)")
-    ap.add_argument("--check", action="store_true", default=True)
+    ap.add_argument("--check", type=int, default=1,
+                    help="1: check every graph replay against the eager results (default)")
+    ap.add_argument("--per-proj", type=int, default=1,
+                    help="1: time each projection shape on its own, cold (default)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="end with plain copies of 256 MiB (byte-counter calibration)")
+    ap.add_argument("--summarize-profile", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU: summarize rocprofv3 CSV output of this script into profiles/")
+    ap.add_argument("--profile-commands", nargs=3, metavar=("TRACE_CMD", "FETCH_CMD", "WRITE_CMD"),
+                    help="the commands that produced --summarize-profile's inputs")
+    ap.add_argument("--profile-out", default=PROFILES)
     args = ap.parse_args()
+
+    if args.summarize_profile:
+        summarize_profiles(args)
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the "
@@ -251,7 +485,8 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    kernel = {"auto": twd.KERNEL_AUTO, "dot": twd.KERNEL_DOT, "mfma": twd.KERNEL_MFMA}[args.kernel]
+    kernel = {"auto": twd.KERNEL_AUTO, "dot": twd.KERNEL_DOT, "mfma": twd.KERNEL_MFMA,
+              "mfma_staged": twd.KERNEL_MFMA_STAGED}[args.kernel]
     set_name = "4b" if args.workload.startswith("4b") else "2b"
     ls = wl.LAYER_SETS[set_name]
     M = args.M or wl.workload_widths(args.workload)[0]
@@ -295,8 +530,7 @@ def main():
     two_wall, _ = time_replays(torch, g_two, reps)
     ref_gbs, ref_dur = stream_read_reference(twd, torch, dev_set, reps)
     traffic = counter_traffic(args.workload, M, bytes_step / nlaunch)
-    kname = twd.KERNEL_NAMES[twd.select_kernel(M, ls.hidden, ls.projs[2].N)] \
-        if kernel == twd.KERNEL_AUTO else args.kernel
+    kname = kernel_map(twd, ls, M, kernel)
     del g_two
 
     widths = {}
@@ -304,7 +538,7 @@ def main():
         for Mw in [int(v) for v in args.widths.split(",") if v]:
             if Mw == M:
                 widths[str(Mw)] = {"gbs": round(lin_gbs, 1), "frac": round(lin_gbs / HBM_PEAK_GBS, 4),
-                                   "us_per_launch": round(lin_dur * 1e6, 3), "kernel": kname}
+                                   "us_per_launch": round(lin_dur * 1e6, 3), "kernels": kname}
                 continue
             st = Step(twd, torch, dev_set, args.workload, Mw, kernel, outliers)
             g = capture(torch, st.fused)
@@ -313,10 +547,12 @@ def main():
             gbs = bytes_step * reps / sec / 1e9
             widths[str(Mw)] = {"gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
                                "us_per_launch": round(sec / (reps * nlaunch) * 1e6, 3),
-                               "kernel": twd.KERNEL_NAMES[twd.select_kernel(Mw, ls.hidden, ls.projs[2].N)]
-                               if kernel == twd.KERNEL_AUTO else args.kernel}
+                               "kernels": kernel_map(twd, ls, Mw, kernel)}
             del st, g
             torch.cuda.empty_cache()
+
+    proj_table = per_projection(twd, torch, ls, M, kernel, reps) if args.per_proj else None
+    calib = copy_calibration(twd, torch) if args.copy_calibration else None
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -342,7 +578,7 @@ def main():
             "packed_weight_bytes_per_step": bytes_step,
             "launches_per_step": nlaunch,
             "hip_graph": True,
-            "kernel": kname,
+            "kernels": kname,
         },
         "roofline": {
             "bound": "hbm",
@@ -351,7 +587,7 @@ def main():
             "unit": "GB/s",
             "frac": round(lin_gbs / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": f"ternary linear, activation quantization fused ({kname})",
+            "kernel": "ternary linear with fused activation quantization (every launch of the step)",
             "avg_launch_us": round(lin_dur * 1e6, 3),
             "launches_timed": args.steps * nlaunch,
         },
@@ -359,8 +595,11 @@ def main():
                             "linear_over_ref": round(lin_gbs / ref_gbs, 4)},
         "two_launch_step_gbs": round(bytes_step * reps / two_wall / 1e9, 1),
         "widths": widths,
+        "per_projection_cold": proj_table,
         "cpu_baseline": cpu,
     }
+    if calib:
+        out["copy_calibration_bytes"] = calib
     print(json.dumps(out), flush=True)
 
 

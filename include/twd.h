@@ -178,6 +178,11 @@ int twd_select_kernel(int64_t M, int64_t K, int64_t N);
 twd_status twd_stream_read(const void *buf, int64_t bytes, uint32_t *sink,
                            void *stream);
 
+/* Measurement helper: a plain copy of `bytes` device bytes from src to dst
+ * (both 16-byte aligned, not overlapping, bytes % 16 == 0).  It reads and
+ * writes exactly `bytes` each, which calibrates hardware byte counters. */
+twd_status twd_stream_copy(const void *src, void *dst, int64_t bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -9,7 +9,7 @@ Names follow the C ABI in ``include/twd.h``: ``quantize_act``,
 ``ternary_linear``, ``ternary_linear_fused``, ``ternary_linear_bf16``,
 ``pack_ternary``,
 ``unpack_ternary``, ``ternarize_absmean``, ``select_kernel``,
-``stream_read``.
+``stream_read``, ``stream_copy``.
 """
 from __future__ import annotations
 
@@ -29,8 +29,8 @@ _STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "BAD_CODE", 4: "HIP"}
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; "
-        "g.build()'` (hipcc --offload-arch=gfx950)")
+        f"{LIB_PATH} is missing: build it with `python ternary_weight_decode_amd/build.py` "
+        "or `python -c 'import __graft_entry__ as g; g.build()'` (hipcc --offload-arch=gfx950)")
 
 # PyTorch ships its own HIP runtime with the same soname as ROCm's; loading
 # torch first makes libtwd bind to that one, so a process never holds two
@@ -66,13 +66,14 @@ _lib_bf16 = _sig("twd_ternary_linear_bf16",
                  [_p, _int, _p, _p, _p, _i64, _i64, _p, _p, _int, _p])
 _lib_select = _sig("twd_select_kernel", [_i64, _i64, _i64])
 _lib_stream_read = _sig("twd_stream_read", [_p, _i64, _p, _p])
+_lib_stream_copy = _sig("twd_stream_copy", [_p, _p, _i64, _p])
 
 EXPORTS = ("twd_version", "twd_last_error", "twd_ternarize_absmean",
            "twd_pack_ternary", "twd_unpack_ternary", "twd_quantize_act",
            "twd_ternary_linear", "twd_ternary_linear_fused",
            "twd_ternary_linear_fused_kernel", "twd_ternary_linear_bf16",
            "twd_select_kernel",
-           "twd_stream_read")
+           "twd_stream_read", "twd_stream_copy")
 
 
 class TwdError(RuntimeError):
@@ -288,4 +289,11 @@ def stream_read(buf, nbytes: int, sink, stream=None):
     _need(_nbytes(buf) >= nbytes, "buf smaller than nbytes")
     _need(_nbytes(sink) >= 1024, "sink needs 1024 bytes")
     _check(_lib_stream_read(_dev_ptr(buf, "buf"), int(nbytes), _dev_ptr(sink, "sink"),
+                            _stream(stream)))
+
+
+def stream_copy(src, dst, nbytes: int, stream=None):
+    """Launch the plain copy kernel: nbytes from src to dst."""
+    _need(_nbytes(src) >= nbytes and _nbytes(dst) >= nbytes, "buffers smaller than nbytes")
+    _check(_lib_stream_copy(_dev_ptr(src, "src"), _dev_ptr(dst, "dst"), int(nbytes),
                             _stream(stream)))

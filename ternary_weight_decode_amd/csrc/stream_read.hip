@@ -1,7 +1,9 @@
-// Achievable-bandwidth reference: a plain streaming read with the same load
-// shape the linear kernels use (16-byte loads, four in flight per lane,
-// 256-thread workgroups).  It reduces what it reads to one word and stores
-// it only when it equals a guard value, so the loads cannot be removed.
+// Measurement references.  stream_read: the achievable-bandwidth reference,
+// a plain streaming read with the linear kernels' load shape (16-byte loads,
+// four in flight per lane, 256-thread workgroups); it reduces what it reads
+// to one word and stores it only when it equals a guard value, so the loads
+// cannot be removed.  stream_copy: a plain copy of known size, the
+// calibration for the HBM byte counters (bytes read = bytes written = size).
 #include "twd_internal.h"
 
 namespace twd {
@@ -27,7 +29,35 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(
         sink[threadIdx.x] = h;
 }
 
+__global__ __launch_bounds__(kThreads) void stream_copy_kernel(
+    const uint4 *__restrict__ src, uint4 *__restrict__ dst, int64_t n16) {
+    const int64_t base = static_cast<int64_t>(blockIdx.x) * kThreads * kLoads + threadIdx.x;
+    uint4 v[kLoads];
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) {
+        const int64_t i = base + static_cast<int64_t>(u) * kThreads;
+        if (i < n16)
+            v[u] = src[i];
+    }
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) {
+        const int64_t i = base + static_cast<int64_t>(u) * kThreads;
+        if (i < n16)
+            dst[i] = v[u];
+    }
+}
+
 }  // namespace
+
+hipError_t launch_stream_copy(const void *src, void *dst, int64_t bytes,
+                              hipStream_t stream) {
+    const int64_t n16 = bytes / 16;
+    const int64_t grid = (n16 + kThreads * kLoads - 1) / (kThreads * kLoads);
+    hipLaunchKernelGGL(stream_copy_kernel, dim3(static_cast<uint32_t>(grid)),
+                       dim3(kThreads), 0, stream, static_cast<const uint4 *>(src),
+                       static_cast<uint4 *>(dst), n16);
+    return hipGetLastError();
+}
 
 hipError_t launch_stream_read(const void *buf, int64_t bytes, uint32_t *sink,
                               hipStream_t stream) {

@@ -113,7 +113,7 @@ __device__ __forceinline__ void stage_row(const void *__restrict__ act,
 }
 
 template <int M, int TW, bool FUSED>
-__global__ __launch_bounds__(block_threads<M>()) void mfma_kernel(
+__global__ __launch_bounds__(block_threads<M>()) void staged_kernel(
     const uint4 *__restrict__ W, const void *__restrict__ act,
     const float *__restrict__ xscale, int K, int N, Segments segs,
     int32_t *__restrict__ acc, float *__restrict__ y) {
@@ -259,7 +259,7 @@ template <int TW, bool FUSED, int... Ms>
 struct Table {
     static bool get(int M, int K, Fn *fn, int *lds, int *threads) {
         bool found = false;
-        ((M == Ms ? (*fn = &mfma_kernel<Ms, TW, FUSED>, *lds = lds_bytes<Ms, TW>(K),
+        ((M == Ms ? (*fn = &staged_kernel<Ms, TW, FUSED>, *lds = lds_bytes<Ms, TW>(K),
                      *threads = block_threads<Ms>(), found = true)
                   : false),
          ...);

@@ -210,3 +210,18 @@ extern "C" twd_status twd_stream_read(const void *buf, int64_t bytes,
     return hip_status(launch_stream_read(buf, bytes, sink, as_stream(stream)),
                       "stream_read launch");
 }
+
+extern "C" twd_status twd_stream_copy(const void *src, void *dst, int64_t bytes,
+                                      void *stream) {
+    if (bytes < 0 || bytes % 16 != 0)
+        return set_error(TWD_ERR_INVALID_ARG,
+                         "stream_copy: bytes must be a non-negative multiple of 16");
+    if (bytes == 0)
+        return TWD_OK;
+    if (!src || !dst || !aligned(src, 16) || !aligned(dst, 16))
+        return set_error(TWD_ERR_INVALID_ARG, "stream_copy: bad pointer");
+    if (bytes / 16 / 1024 >= (int64_t(1) << 31))
+        return set_error(TWD_ERR_UNSUPPORTED, "stream_copy: too large");
+    return hip_status(launch_stream_copy(src, dst, bytes, as_stream(stream)),
+                      "stream_copy launch");
+}

@@ -57,5 +57,7 @@ hipError_t launch_staged(int tiles, const uint8_t *w, const void *act, bool fuse
 
 hipError_t launch_stream_read(const void *buf, int64_t bytes, uint32_t *sink,
                               hipStream_t stream);
+hipError_t launch_stream_copy(const void *src, void *dst, int64_t bytes,
+                              hipStream_t stream);
 
 }  // namespace twd
