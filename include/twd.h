@@ -52,8 +52,8 @@ typedef enum {
  * choose (M1's "select by replay width and input/output dimensions"). */
 typedef enum {
     TWD_KERNEL_AUTO = 0,
-    /* straight-line VALU kernel: 2-bit decode in registers + v_dot4 int8;
-     * M <= 4 and M * ceil(K / 1024) <= 32 */
+    /* row-owner VALU kernel: 2-bit decode in registers + v_dot4 int8;
+     * M <= 4 */
     TWD_KERNEL_DOT = 1,
     /* straight-line matrix-core kernel (v_mfma_i32_16x16x64_i8) where
      * M * ceil(K / 1024) <= 32, else the staged one */

@@ -1,12 +1,12 @@
 // Width dispatch -- M1's choice of "packed low-bit operators by replay width
 // and input/output dimensions" (BitMTP page, ai.info AI summary,
-// "Methodology in Plain English", paragraph 3): the straight-line kernels
-// while each wave's activation slices fit in registers, the staged
-// matrix-core kernel otherwise, and its 16-row tiles per workgroup from the
-// output size.  Straight-line flavour by measurement on the 2B and 4B layer
-// shapes: at M = 1 the VALU dot kernel and the matrix-core one stream the
-// weights equally fast (the dot kernel needs no zero block or B layout); from
-// M = 2 the matrix cores are faster, since the VALU work grows with M.
+// "Methodology in Plain English", paragraph 3).  By measurement on the 2B
+// layer shapes: at M = 1 the row-owner VALU dot kernel is fastest (whole
+// 128-byte lines per load, no cross-wave reduction); from M = 2 the matrix
+// cores win, since the VALU work grows with M -- the straight-line MFMA
+// kernel while each wave's activation slices fit in registers, else the
+// staged one.  The dot kernel picks its own launch shape from N; the staged
+// kernel takes two 16-row tiles per workgroup from 512 tiles up.
 #include "twd_internal.h"
 
 namespace twd {
@@ -16,9 +16,8 @@ LinearPlan plan_linear(int M, int K, int N, int forced_kernel) {
     p.tiles = 1;
     int k = forced_kernel;
     if (k == TWD_KERNEL_AUTO)
-        k = (M == 1 && narrow_supported(TWD_KERNEL_DOT, M, K)) ? TWD_KERNEL_DOT
-                                                               : TWD_KERNEL_MFMA;
-    if (k == TWD_KERNEL_MFMA && !narrow_supported(TWD_KERNEL_MFMA, M, K))
+        k = M == 1 ? TWD_KERNEL_DOT : TWD_KERNEL_MFMA;
+    if (k == TWD_KERNEL_MFMA && !narrow_supported(M, K))
         k = TWD_KERNEL_MFMA_STAGED;
     p.kernel = k;
     if (k == TWD_KERNEL_MFMA_STAGED && (N + 15) / 16 >= 512)
@@ -33,8 +32,9 @@ hipError_t launch_linear(const LinearPlan &plan, const uint8_t *w,
     if (plan.kernel == TWD_KERNEL_MFMA_STAGED)
         return launch_staged(plan.tiles, w, act, fused, xscale, M, K, N, segs, acc, y,
                              stream);
-    return launch_narrow(plan.kernel, w, act, fused, xscale, M, K, N, segs, acc, y,
-                         stream);
+    if (plan.kernel == TWD_KERNEL_DOT)
+        return launch_rows(w, act, fused, xscale, M, K, N, segs, acc, y, stream);
+    return launch_narrow(w, act, fused, xscale, M, K, N, segs, acc, y, stream);
 }
 
 }  // namespace twd

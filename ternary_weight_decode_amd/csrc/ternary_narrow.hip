@@ -1,6 +1,6 @@
-// Straight-line kernels of the W2A8 ternary linear, gfx950: one pass over the
-// weights with every load issued up front, for autoregressive steps (M = 1)
-// and drafted blocks whose activations fit in registers.
+// Straight-line matrix-core kernel of the W2A8 ternary linear, gfx950: one
+// pass over the weights with every load issued up front, for drafted blocks
+// (M = 2..16) whose activation slices fit in registers.
 //
 // What they compute (BitMTP page, ai.info AI summary): ternary BitNet b1.58
 // weights ("What This Paper Is About"), 8-bit activations ("Main Findings":
@@ -29,16 +29,13 @@
 //
 // Decode.  A 32-bit word holds 16 codes c = t + 1; masking with 0x03030303,
 // 0x0C0C0C0C, 0x30303030 gives byte planes holding c, 4c, 16c for elements
-// 4j..4j+3 (j = 0, 1, 2) and (w >> 6) & 0x03030303 gives plane 3.  Each plane
-// pairs with one activation word; the planes scaled by 4 and 16 have their
-// own accumulators, shifted back exactly at the end; sum q t = sum q c -
-// sum q.
-//   DOT:  v_dot4 of each plane with the activation word, per token.
-//   MFMA: plane j of the lane's four words is the A operand of a
-//         16x16x64 int8 MFMA (row = lane % 16, K group = lane / 16); the
-//         tokens fill the B columns, a zero block beyond M.  The staged
-//         activations are stored permuted within each 16-word group so that
-//         one 16-byte LDS read yields a B operand.
+// 4j..4j+3 (j = 0, 1, 2) and (w >> 6) & 0x03030303 gives plane 3.  Plane j of
+// the lane's four words is the A operand of a 16x16x64 int8 MFMA (row =
+// lane % 16, K group = lane / 16); the tokens fill the B columns, a zero
+// block beyond M.  The planes scaled by 4 and 16 have their own
+// accumulators, shifted back exactly at the end; sum q t = sum q c - sum q.
+// The staged activations are stored permuted within each 16-word group so
+// that one 16-byte LDS read yields a B operand.
 #include "kernel_common.h"
 
 namespace twd {
@@ -51,36 +48,30 @@ constexpr int kRawBufferFlags = 0x00020000;
 // An offset past every buffer bound: the load returns zeros.
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
-template <int KIND>
-__host__ __device__ constexpr int parts() { return KIND == TWD_KERNEL_DOT ? 16 : kWaves; }
-
-// Per-wave LDS region: M x U staged slices, then (MFMA) a zero block.
+// Per-wave LDS region: M x U staged slices, then a zero block.
 template <int M, int U>
 __host__ __device__ constexpr int wave_bytes() { return M * U * 256 + 64; }
 
 // LDS: per-wave regions | partials [M][16 rows][parts] | absmax partials
 // [wave][M] | row-sum partials [wave][M].
-template <int KIND, int M, int U>
+template <int M, int U>
 __host__ __device__ constexpr int lds_bytes() {
-    return kWaves * wave_bytes<M, U>() + M * 16 * parts<KIND>() * 4 + 2 * kWaves * M * 4;
+    return kWaves * wave_bytes<M, U>() + M * 16 * kWaves * 4 + 2 * kWaves * M * 4;
 }
 
-// Where lane l's activation word (elements 4l..4l+3 of the slice) is staged.
-// MFMA: word 16g + 4d + j goes to 16g + 4j + d, so the four words of plane j
-// of K group g are contiguous.
-template <int KIND>
+// Where lane l's activation word (elements 4l..4l+3 of the slice) is staged:
+// word 16g + 4d + j goes to 16g + 4j + d, so the four words of plane j of K
+// group g are contiguous.
 __device__ __forceinline__ int staged_word(int lane) {
-    if constexpr (KIND == TWD_KERNEL_DOT)
-        return lane;
     return (lane & 48) | ((lane & 3) << 2) | ((lane >> 2) & 3);
 }
 
-template <int KIND, int M, int U, bool FUSED>
-__global__ __launch_bounds__(kThreads) void narrow_kernel(
+template <int M, int U, bool FUSED>
+__global__ __launch_bounds__(kThreads) void mfma_kernel(
     const uint8_t *__restrict__ W, const void *__restrict__ act,
     const float *__restrict__ xscale, int K, int N, Segments segs,
     int32_t *__restrict__ acc, float *__restrict__ y) {
-    constexpr int P = parts<KIND>();
+    constexpr int P = kWaves;  // partial sums per output
     extern __shared__ __align__(16) uint8_t smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -138,7 +129,7 @@ __global__ __launch_bounds__(kThreads) void narrow_kernel(
     __builtin_amdgcn_sched_barrier(0);
 
     // 3. own activation slices -> LDS as int8, with this wave's row sums
-    const int slot = 4 * staged_word<KIND>(lane);
+    const int slot = 4 * staged_word(lane);
     int sq[M];
 #pragma unroll
     for (int m = 0; m < M; ++m)
@@ -183,10 +174,8 @@ __global__ __launch_bounds__(kThreads) void narrow_kernel(
                 sq[m] = sdot4(xi[m][u], kOnes, sq[m]);
             }
     }
-    if constexpr (KIND == TWD_KERNEL_MFMA) {
-        if (lane < 4)  // zero block behind the token columns past M
-            *reinterpret_cast<uint4 *>(own + M * U * 256 + 16 * lane) = make_uint4(0u, 0u, 0u, 0u);
-    }
+    if (lane < 4)  // zero block behind the token columns past M
+        *reinterpret_cast<uint4 *>(own + M * U * 256 + 16 * lane) = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
     for (int m = 0; m < M; ++m) {
         const int s = wave_sum(sq[m]);
@@ -200,38 +189,7 @@ __global__ __launch_bounds__(kThreads) void narrow_kernel(
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     // 4. decode + multiply-accumulate, one slice at a time as it arrives
-    if constexpr (KIND == TWD_KERNEL_DOT) {
-        int d1[M], d4[M], d16[M];
-#pragma unroll
-        for (int m = 0; m < M; ++m)
-            d1[m] = d4[m] = d16[m] = 0;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-#pragma unroll
-            for (int dw = 0; dw < 4; ++dw) {
-                uint4 x[M];
-#pragma unroll
-                for (int m = 0; m < M; ++m)
-                    x[m] = *reinterpret_cast<const uint4 *>(own + (m * U + u) * 256 + 64 * g + 16 * dw);
-                const uint32_t w = dw == 0 ? a[u].x : dw == 1 ? a[u].y : dw == 2 ? a[u].z : a[u].w;
-                const uint32_t p0 = w & kPlane0;
-                const uint32_t p1 = w & kPlane1;
-                const uint32_t p2 = w & kPlane2;
-                const uint32_t p3 = (w >> 6) & kPlane0;
-#pragma unroll
-                for (int m = 0; m < M; ++m) {
-                    d1[m] = sdot4(p0, x[m].x, d1[m]);
-                    d4[m] = sdot4(p1, x[m].y, d4[m]);
-                    d16[m] = sdot4(p2, x[m].z, d16[m]);
-                    d1[m] = sdot4(p3, x[m].w, d1[m]);
-                }
-            }
-        }
-        // partials [M][16 rows][wave, K group]
-#pragma unroll
-        for (int m = 0; m < M; ++m)
-            red[(m * 16 + r) * P + wave * 4 + g] = d1[m] + (d4[m] >> 2) + (d16[m] >> 4);
-    } else {
+    {
         v4i c0 = {0, 0, 0, 0}, c3 = c0, c4 = c0, c16 = c0;
         // B operand of plane j: token r's K group g; columns past M read
         // the zero block
@@ -302,14 +260,14 @@ __global__ __launch_bounds__(kThreads) void narrow_kernel(
 using Fn = void (*)(const uint8_t *, const void *, const float *, int, int, Segments,
                     int32_t *, float *);
 
-template <int KIND, int M, bool FUSED, int... Us>
+template <int M, bool FUSED, int... Us>
 bool pick_u(int U, Fn *fn, int *lds) {
     bool found = false;
     auto take = [&](auto uc) {
         constexpr int Uc = decltype(uc)::value;
         if constexpr (narrow_fits(M, Uc)) {
-            *fn = &narrow_kernel<KIND, M, Uc, FUSED>;
-            *lds = lds_bytes<KIND, M, Uc>();
+            *fn = &mfma_kernel<M, Uc, FUSED>;
+            *lds = lds_bytes<M, Uc>();
             found = true;
         }
     };
@@ -317,39 +275,30 @@ bool pick_u(int U, Fn *fn, int *lds) {
     return found;
 }
 
-template <int KIND, bool FUSED, int... Ms>
+template <bool FUSED, int... Ms>
 bool pick_m(int M, int U, Fn *fn, int *lds) {
     bool found = false;
-    ((M == Ms ? (found = pick_u<KIND, Ms, FUSED, 1, 2, 3, 4, 5, 6, 7, 8>(U, fn, lds)) : false),
-     ...);
+    ((M == Ms ? (found = pick_u<Ms, FUSED, 1, 2, 3, 4, 5, 6, 7, 8>(U, fn, lds)) : false), ...);
     return found;
 }
 
 }  // namespace
 
-bool narrow_supported(int kernel, int M, int K) {
+bool narrow_supported(int M, int K) {
     const int U = (K + 1023) / 1024;
-    if (kernel == TWD_KERNEL_DOT)
-        return M >= 1 && M <= 4 && narrow_fits(M, U);
     return M >= 1 && M <= TWD_MAX_M && narrow_fits(M, U);
 }
 
-hipError_t launch_narrow(int kernel, const uint8_t *w, const void *act, bool fused,
+hipError_t launch_narrow(const uint8_t *w, const void *act, bool fused,
                          const float *xscale, int M, int K, int N,
                          const Segments &segs, int32_t *acc, float *y,
                          hipStream_t stream) {
     const int U = (K + 1023) / 1024;  // 256-wide slices per wave
     Fn fn = nullptr;
     int lds = 0;
-    bool ok = false;
-    if (kernel == TWD_KERNEL_DOT)
-        ok = fused ? pick_m<TWD_KERNEL_DOT, true, 1, 2, 3, 4>(M, U, &fn, &lds)
-                   : pick_m<TWD_KERNEL_DOT, false, 1, 2, 3, 4>(M, U, &fn, &lds);
-    else
-        ok = fused ? pick_m<TWD_KERNEL_MFMA, true, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12,
-                            13, 14, 15, 16>(M, U, &fn, &lds)
-                   : pick_m<TWD_KERNEL_MFMA, false, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12,
-                            13, 14, 15, 16>(M, U, &fn, &lds);
+    const bool ok =
+        fused ? pick_m<true, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>(M, U, &fn, &lds)
+              : pick_m<false, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>(M, U, &fn, &lds);
     if (!ok)
         return hipErrorInvalidValue;
     hipError_t e = ensure_lds_limit(reinterpret_cast<const void *>(fn), lds);

@@ -65,10 +65,8 @@ twd_status check_linear(const uint8_t *wpacked, int nseg,
         return set_error(TWD_ERR_UNSUPPORTED,
                          "linear: K=%lld must be a multiple of 64 in 64..%d",
                          (long long)K, TWD_MAX_K);
-    if (kernel == TWD_KERNEL_DOT && M > 0 &&
-        !narrow_supported(TWD_KERNEL_DOT, static_cast<int>(M), static_cast<int>(K)))
-        return set_error(TWD_ERR_UNSUPPORTED,
-                         "linear: the dot kernel takes M <= 4 and M * ceil(K / 1024) <= 32");
+    if (kernel == TWD_KERNEL_DOT && M > 4)
+        return set_error(TWD_ERR_UNSUPPORTED, "linear: the dot kernel takes M <= 4");
     if (M == 0 || N == 0)
         return TWD_OK;
     if (!wpacked || !act || (!fused && !xscale))

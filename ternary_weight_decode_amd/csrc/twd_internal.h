@@ -23,8 +23,9 @@ struct LinearPlan {
     int tiles;   // 16-row tiles per workgroup (staged kernel)
 };
 
-// The straight-line kernels hold each wave's activation slices in registers
-// (M x U words, U = 256-wide K slices per wave): they exist for M * U <= 32.
+// The straight-line MFMA kernel holds each wave's activation slices in
+// registers (M x U words, U = 256-wide K slices per wave): it exists for
+// M * U <= 32.
 constexpr bool narrow_fits(int M, int U) { return U >= 1 && U <= 8 && M * U <= 32; }
 
 // Thread-local error message; returns `st` for convenient chaining.
@@ -42,13 +43,19 @@ hipError_t launch_linear(const LinearPlan &plan, const uint8_t *w,
                          int M, int K, int N, const Segments &segs,
                          int32_t *acc, float *y, hipStream_t stream);
 
-// Straight-line kernels (ternary_narrow.hip), kernel = TWD_KERNEL_DOT
-// (M <= 4) or TWD_KERNEL_MFMA, for the (M, K) narrow_supported accepts.
-bool narrow_supported(int kernel, int M, int K);
-hipError_t launch_narrow(int kernel, const uint8_t *w, const void *act, bool fused,
+// Straight-line MFMA kernel (ternary_narrow.hip), for the (M, K)
+// narrow_supported accepts.
+bool narrow_supported(int M, int K);
+hipError_t launch_narrow(const uint8_t *w, const void *act, bool fused,
                          const float *xscale, int M, int K, int N,
                          const Segments &segs, int32_t *acc, float *y,
                          hipStream_t stream);
+// Row-owner VALU dot kernel (ternary_rows.hip): M <= 4, any K; the launch
+// shape (rows per wave, waves per workgroup) comes from rows_shape.
+void rows_shape(int M, int N, int *rows_per_wave, int *waves);
+hipError_t launch_rows(const uint8_t *w, const void *act, bool fused, const float *xscale,
+                       int M, int K, int N, const Segments &segs, int32_t *acc, float *y,
+                       hipStream_t stream);
 // Staged matrix-core kernel (ternary_staged.hip): any M <= 16 and K.
 hipError_t launch_staged(int tiles, const uint8_t *w, const void *act, bool fused,
                        const float *xscale, int M, int K, int N,

@@ -124,6 +124,8 @@ SMALL_SHAPES = [
     (768, (50, 50)),       # two segments
     (6912, (33,)),         # 27 slices: seven per wave, one wave a slice short
     (8192, (20,)),         # the largest K
+    (512, (4104, 4104)),   # N >= 6400: the dot kernel's 8 rows x 4 waves shape at M=1
+    (256, (6400, 6417)),   # N >= 12800: 8 rows x 8 waves at M=1, ragged
 ]
 
 # (kernel family, widest M it takes); KERNEL_MFMA runs the straight-line
