@@ -166,12 +166,15 @@ def stream_read_reference(twd, torch, dev_set, reps):
 def kernel_map(twd, ls, M, kernel):
     """Kernel family each projection of the set runs at width M (a forced
     KERNEL_MFMA runs the staged form where the straight-line one does not
-    fit: M * ceil(K / 1024) > 32)."""
+    fit, M * ceil(K / 1024) > 48, and a forced KERNEL_MFMA_TILE where
+    K > 3072)."""
     out = {}
     for p in ls.projs:
         if kernel == twd.KERNEL_AUTO:
             k = twd.select_kernel(M, p.K, p.N)
-        elif kernel == twd.KERNEL_MFMA and M * (-(-p.K // 1024)) > 32:
+        elif kernel == twd.KERNEL_MFMA and M * (-(-p.K // 1024)) > 48:
+            k = twd.KERNEL_MFMA_STAGED
+        elif kernel == twd.KERNEL_MFMA_TILE and p.K > 3072:
             k = twd.KERNEL_MFMA_STAGED
         else:
             k = kernel
@@ -332,7 +335,7 @@ def _short(name):
 def _linear_fused(name):
     """The one-launch (fused quantization) instances of the linear kernels."""
     short = _short(name)
-    return (short.startswith(("narrow_kernel<", "staged_kernel<"))
+    return (short.startswith(("rows_kernel<", "mfma_kernel<", "tile_kernel<", "staged_kernel<"))
             and short.endswith("true>"))
 
 
@@ -452,7 +455,8 @@ def main():
     ap.add_argument("--workload", default="2b_decode",
                     choices=["2b_decode", "2b_verify", "2b_sweep_outlier", "4b_stack"])
     ap.add_argument("--M", type=int, default=None, help="width (default: the workload's first)")
-    ap.add_argument("--kernel", default="auto", choices=["auto", "dot", "mfma", "mfma_staged"])
+    ap.add_argument("--kernel", default="auto",
+                    choices=["auto", "dot", "mfma", "mfma_staged", "mfma_tile"])
     ap.add_argument("--widths", default="1,2,4,8,16",
                     help="widths for the per-width linear table ('' to skip)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -486,7 +490,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     kernel = {"auto": twd.KERNEL_AUTO, "dot": twd.KERNEL_DOT, "mfma": twd.KERNEL_MFMA,
-              "mfma_staged": twd.KERNEL_MFMA_STAGED}[args.kernel]
+              "mfma_staged": twd.KERNEL_MFMA_STAGED, "mfma_tile": twd.KERNEL_MFMA_TILE}[args.kernel]
     set_name = "4b" if args.workload.startswith("4b") else "2b"
     ls = wl.LAYER_SETS[set_name]
     M = args.M or wl.workload_widths(args.workload)[0]

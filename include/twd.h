@@ -56,10 +56,14 @@ typedef enum {
      * M <= 4 */
     TWD_KERNEL_DOT = 1,
     /* straight-line matrix-core kernel (v_mfma_i32_16x16x64_i8) where
-     * M * ceil(K / 1024) <= 32, else the staged one */
+     * M * ceil(K / 1024) <= 48, else the staged one */
     TWD_KERNEL_MFMA = 2,
     /* matrix cores with separate activation-staging waves: any M, K */
-    TWD_KERNEL_MFMA_STAGED = 3
+    TWD_KERNEL_MFMA_STAGED = 3,
+    /* matrix cores, one 16-row tile per wave over all of K and 64 rows per
+     * workgroup (activations staged once per 64 rows); K <= 3072, else the
+     * staged kernel */
+    TWD_KERNEL_MFMA_TILE = 4
 } twd_kernel;
 
 /* Library version string; never NULL. */
@@ -167,8 +171,8 @@ twd_status twd_ternary_linear_bf16(const uint8_t *wpacked, int nseg,
                                    int kernel, void *stream);
 
 /* The kernel family the width dispatch picks for (M, K, N), without
- * launching anything.  Returns TWD_KERNEL_DOT, TWD_KERNEL_MFMA or
- * TWD_KERNEL_MFMA_STAGED, or -1 if the shape is unsupported. */
+ * launching anything.  Returns a twd_kernel value other than
+ * TWD_KERNEL_AUTO, or -1 if the shape is unsupported. */
 int twd_select_kernel(int64_t M, int64_t K, int64_t N);
 
 /* Measurement helper: a plain streaming read of `bytes` device bytes

@@ -22,8 +22,9 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libtwd.so")
 
 TWD_OK = 0
-KERNEL_AUTO, KERNEL_DOT, KERNEL_MFMA, KERNEL_MFMA_STAGED = 0, 1, 2, 3
-KERNEL_NAMES = {KERNEL_DOT: "dot", KERNEL_MFMA: "mfma", KERNEL_MFMA_STAGED: "mfma_staged"}
+KERNEL_AUTO, KERNEL_DOT, KERNEL_MFMA, KERNEL_MFMA_STAGED, KERNEL_MFMA_TILE = 0, 1, 2, 3, 4
+KERNEL_NAMES = {KERNEL_DOT: "dot", KERNEL_MFMA: "mfma", KERNEL_MFMA_STAGED: "mfma_staged",
+                KERNEL_MFMA_TILE: "mfma_tile"}
 MAX_M, MAX_K, MAX_SEGMENTS = 16, 8192, 4
 _STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "BAD_CODE", 4: "HIP"}
 
@@ -279,8 +280,8 @@ def ternary_linear_bf16(wpacked, seg_rows, seg_gamma, x, acc=None, y=None,
 
 
 def select_kernel(M: int, K: int, N: int) -> int:
-    """Kernel family the width dispatch picks (KERNEL_DOT, KERNEL_MFMA or
-    KERNEL_MFMA_STAGED), or -1 for an unsupported shape."""
+    """Kernel family the width dispatch picks (a KERNEL_* value other than
+    KERNEL_AUTO), or -1 for an unsupported shape."""
     return int(_lib_select(M, K, N))
 
 

@@ -3,10 +3,13 @@
 // "Methodology in Plain English", paragraph 3).  By measurement on the 2B
 // layer shapes: at M = 1 the row-owner VALU dot kernel is fastest (whole
 // 128-byte lines per load, no cross-wave reduction); from M = 2 the matrix
-// cores win, since the VALU work grows with M -- the straight-line MFMA
-// kernel while each wave's activation slices fit in registers, else the
-// staged one.  The dot kernel picks its own launch shape from N; the staged
-// kernel takes two 16-row tiles per workgroup from 512 tiles up.
+// cores win, since the VALU work grows with M.  From M = 4 a wide output
+// (at least ~200 workgroups of 64 rows) takes the tile-owner kernel, which
+// quantizes the activations once per 64 rows instead of once per 16; else the
+// straight-line MFMA kernel while each wave's activation slices fit in
+// registers, else the staged one.  The dot kernel picks its own launch shape
+// from N; the staged kernel takes two 16-row tiles per workgroup from 512
+// tiles up.
 #include "twd_internal.h"
 
 namespace twd {
@@ -15,9 +18,17 @@ LinearPlan plan_linear(int M, int K, int N, int forced_kernel) {
     LinearPlan p;
     p.tiles = 1;
     int k = forced_kernel;
-    if (k == TWD_KERNEL_AUTO)
-        k = M == 1 ? TWD_KERNEL_DOT : TWD_KERNEL_MFMA;
+    if (k == TWD_KERNEL_AUTO) {
+        if (M == 1)
+            k = TWD_KERNEL_DOT;
+        else if (M >= 4 && N / 64 >= 200 && tile_supported(M, K))
+            k = TWD_KERNEL_MFMA_TILE;
+        else
+            k = TWD_KERNEL_MFMA;
+    }
     if (k == TWD_KERNEL_MFMA && !narrow_supported(M, K))
+        k = TWD_KERNEL_MFMA_STAGED;
+    if (k == TWD_KERNEL_MFMA_TILE && !tile_supported(M, K))
         k = TWD_KERNEL_MFMA_STAGED;
     p.kernel = k;
     if (k == TWD_KERNEL_MFMA_STAGED && (N + 15) / 16 >= 512)
@@ -32,6 +43,8 @@ hipError_t launch_linear(const LinearPlan &plan, const uint8_t *w,
     if (plan.kernel == TWD_KERNEL_MFMA_STAGED)
         return launch_staged(plan.tiles, w, act, fused, xscale, M, K, N, segs, acc, y,
                              stream);
+    if (plan.kernel == TWD_KERNEL_MFMA_TILE)
+        return launch_tile(w, act, fused, xscale, M, K, N, segs, acc, y, stream);
     if (plan.kernel == TWD_KERNEL_DOT)
         return launch_rows(w, act, fused, xscale, M, K, N, segs, acc, y, stream);
     return launch_narrow(w, act, fused, xscale, M, K, N, segs, acc, y, stream);

@@ -55,6 +55,41 @@ __device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
     return max(a, b);
 }
 
+// Reductions of R independent per-lane values over each 16-lane DPP row at
+// once: the total of row i (lanes 16 i .. 16 i + 15) lands in lane 16 i + 15.
+// The DPP steps of the R values interleave, so they need no hazard padding.
+template <int R>
+__device__ __forceinline__ void row_max16(uint32_t (&v)[R]) {
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+        v[i] = max(v[i], static_cast<uint32_t>(dpp<0x111>(static_cast<int>(v[i]))));
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+        v[i] = max(v[i], static_cast<uint32_t>(dpp<0x112>(static_cast<int>(v[i]))));
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+        v[i] = max(v[i], static_cast<uint32_t>(dpp<0x114>(static_cast<int>(v[i]))));
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+        v[i] = max(v[i], static_cast<uint32_t>(dpp<0x118>(static_cast<int>(v[i]))));
+}
+
+template <int R>
+__device__ __forceinline__ void row_sum16(int (&v)[R]) {
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+        v[i] += dpp<0x111>(v[i]);
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+        v[i] += dpp<0x112>(v[i]);
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+        v[i] += dpp<0x114>(v[i]);
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+        v[i] += dpp<0x118>(v[i]);
+}
+
 // Per-token int8 quantization, q = rint(x * inv), bit-exact with a plain
 // fp32 implementation (rint rounds half to even):
 //   * the product x * inv is rounded to fp32 on its own (__fmul_rn: never

@@ -48,15 +48,20 @@ constexpr int kRawBufferFlags = 0x00020000;
 // An offset past every buffer bound: the load returns zeros.
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
-// Per-wave LDS region: M x U staged slices, then a zero block.
-template <int M, int U>
-__host__ __device__ constexpr int wave_bytes() { return M * U * 256 + 64; }
+// Per-wave LDS region: M staged rows of U slices, then a zero block.  The
+// row stride is padded by 16 bytes so that the 16 token rows a B-operand read
+// touches fall on 16 different 4-bank groups (64 banks of 4 bytes).
+template <int U>
+__host__ __device__ constexpr int row_stride() { return U * 256 + 16; }
 
-// LDS: per-wave regions | partials [M][16 rows][parts] | absmax partials
-// [wave][M] | row-sum partials [wave][M].
+template <int M, int U>
+__host__ __device__ constexpr int wave_bytes() { return M * row_stride<U>() + 64; }
+
+// LDS: per-wave regions | partials [M][16 rows][wave] | absmax partials
+// [wave, DPP row][M] | row-sum partials [wave, DPP row][M] | scales [M].
 template <int M, int U>
 __host__ __device__ constexpr int lds_bytes() {
-    return kWaves * wave_bytes<M, U>() + M * 16 * kWaves * 4 + 2 * kWaves * M * 4;
+    return kWaves * wave_bytes<M, U>() + M * 16 * kWaves * 4 + 2 * 4 * kWaves * M * 4 + M * 4;
 }
 
 // Where lane l's activation word (elements 4l..4l+3 of the slice) is staged:
@@ -83,8 +88,10 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(
 
     uint8_t *own = smem + wave * wave_bytes<M, U>();
     int32_t *red = reinterpret_cast<int32_t *>(smem + kWaves * wave_bytes<M, U>());
-    uint32_t *st_max = reinterpret_cast<uint32_t *>(red + M * 16 * P);
-    int32_t *st_sum = reinterpret_cast<int32_t *>(st_max + kWaves * M);
+    uint32_t *st_max = reinterpret_cast<uint32_t *>(red + M * 16 * P);   // [16][M]
+    int32_t *st_sum = reinterpret_cast<int32_t *>(st_max + 4 * kWaves * M);  // [16][M]
+    float *st_scale = reinterpret_cast<float *>(st_sum + 4 * kWaves * M);    // [M]
+    const int part = wave * 4 + (lane >> 4);  // this lane's DPP row in the workgroup
 
     // 1. activation loads: lane l takes elements 256 s + 4 l .. + 3 of each
     //    row for this wave's slices s = wave + 4 u (zeros past K)
@@ -135,6 +142,9 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(
     for (int m = 0; m < M; ++m)
         sq[m] = 0;
     if constexpr (FUSED) {
+        // row absmax: per-lane partials, reduced over each DPP row for all
+        // rows at once, 16 partials per row to LDS
+        uint32_t amv[M];
 #pragma unroll
         for (int m = 0; m < M; ++m) {
             u16x2 am2 = {0, 0};
@@ -143,25 +153,35 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(
                 am2 = absmax_pair(am2, xb[m][u].x);
                 am2 = absmax_pair(am2, xb[m][u].y);
             }
-            const uint32_t am = wave_umax(absmax_bits(am2));
-            if (lane == 0)
-                st_max[wave * M + m] = am;
+            amv[m] = absmax_bits(am2);
+        }
+        row_max16<M>(amv);
+        if ((lane & 15) == 15) {
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+                st_max[part * M + m] = amv[m];
         }
         __syncthreads();  // row absmax partials (LDS only)
+        // lane m combines row m and divides once for it (correctly rounded
+        // fp32 division, build flag, as in the stand-alone quantizer; an
+        // all-zero row quantizes to zeros)
+        uint32_t am_l = 0;
+        if (lane < M) {
+#pragma unroll
+            for (int i = 0; i < 4 * kWaves; ++i)
+                am_l = max(am_l, st_max[i * M + lane]);
+        }
+        const float a_l = __uint_as_float(am_l);
+        const float inv_l = a_l > 0.0f ? 127.0f / a_l : 0.0f;
+        if (wave == 0 && lane < M)
+            st_scale[lane] = a_l / 127.0f;
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-            uint32_t am = st_max[m];
-#pragma unroll
-            for (int w = 1; w < kWaves; ++w)
-                am = max(am, st_max[w * M + m]);
-            const float a_m = __uint_as_float(am);
-            // correctly rounded fp32 division (build flag), as in the
-            // stand-alone quantizer; an all-zero row quantizes to zeros
-            const float inv = a_m > 0.0f ? 127.0f / a_m : 0.0f;
+            const float inv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(inv_l), m));
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const uint32_t q = quant4(xb[m][u].x, xb[m][u].y, inv);
-                *reinterpret_cast<uint32_t *>(own + (m * U + u) * 256 + slot) = q;
+                *reinterpret_cast<uint32_t *>(own + m * row_stride<U>() + u * 256 + slot) = q;
                 sq[m] = sdot4(q, kOnes, sq[m]);
             }
         }
@@ -170,17 +190,17 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(
         for (int m = 0; m < M; ++m)
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                *reinterpret_cast<uint32_t *>(own + (m * U + u) * 256 + slot) = xi[m][u];
+                *reinterpret_cast<uint32_t *>(own + m * row_stride<U>() + u * 256 + slot) = xi[m][u];
                 sq[m] = sdot4(xi[m][u], kOnes, sq[m]);
             }
     }
     if (lane < 4)  // zero block behind the token columns past M
-        *reinterpret_cast<uint4 *>(own + M * U * 256 + 16 * lane) = make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4 *>(own + M * row_stride<U>() + 16 * lane) = make_uint4(0u, 0u, 0u, 0u);
+    row_sum16<M>(sq);
+    if ((lane & 15) == 15) {
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-        const int s = wave_sum(sq[m]);
-        if (lane == 0)
-            st_sum[wave * M + m] = s;
+        for (int m = 0; m < M; ++m)
+            st_sum[part * M + m] = sq[m];
     }
     // the wave reads back only its own LDS region: its writes are ordered
     // before its reads, no workgroup barrier needed
@@ -193,7 +213,7 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(
         v4i c0 = {0, 0, 0, 0}, c3 = c0, c4 = c0, c16 = c0;
         // B operand of plane j: token r's K group g; columns past M read
         // the zero block
-        const uint8_t *bsrc = r < M ? own + r * (U * 256) + 64 * g : own + M * U * 256;
+        const uint8_t *bsrc = r < M ? own + r * row_stride<U>() + 64 * g : own + M * row_stride<U>();
         const int ustep = r < M ? 256 : 0;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -236,19 +256,10 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(
             const int4 v = *reinterpret_cast<const int4 *>(red + idx * P + p);
             total += v.x + v.y + v.z + v.w;
         }
-        float scale;
-        if constexpr (FUSED) {
-            uint32_t am = st_max[m];
+        const float scale = FUSED ? st_scale[m] : xscale[m];
 #pragma unroll
-            for (int w = 1; w < kWaves; ++w)
-                am = max(am, st_max[w * M + m]);
-            scale = __uint_as_float(am) / 127.0f;
-        } else {
-            scale = xscale[m];
-        }
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w)
-            total -= st_sum[w * M + m];
+        for (int i = 0; i < 4 * kWaves; ++i)
+            total -= st_sum[i * M + m];
         const int64_t o = static_cast<int64_t>(m) * N + n;
         if (acc)
             acc[o] = total;

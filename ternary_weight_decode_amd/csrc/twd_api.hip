@@ -35,7 +35,8 @@ twd_status check_linear(const uint8_t *wpacked, int nseg,
                         const float *y, int kernel, Segments *segs,
                         int64_t *N_out) {
     if (kernel != TWD_KERNEL_AUTO && kernel != TWD_KERNEL_DOT &&
-        kernel != TWD_KERNEL_MFMA && kernel != TWD_KERNEL_MFMA_STAGED)
+        kernel != TWD_KERNEL_MFMA && kernel != TWD_KERNEL_MFMA_STAGED &&
+        kernel != TWD_KERNEL_MFMA_TILE)
         return set_error(TWD_ERR_INVALID_ARG, "linear: unknown kernel %d", kernel);
     if (nseg < 1 || nseg > TWD_MAX_SEGMENTS)
         return set_error(TWD_ERR_INVALID_ARG, "linear: nseg=%d outside 1..%d",

@@ -19,14 +19,14 @@ struct Segments {
 
 // Launch parameters the width dispatch chose for one linear call.
 struct LinearPlan {
-    int kernel;  // TWD_KERNEL_DOT, TWD_KERNEL_MFMA or TWD_KERNEL_MFMA_STAGED
+    int kernel;  // TWD_KERNEL_DOT, _MFMA, _MFMA_TILE or _MFMA_STAGED
     int tiles;   // 16-row tiles per workgroup (staged kernel)
 };
 
 // The straight-line MFMA kernel holds each wave's activation slices in
 // registers (M x U words, U = 256-wide K slices per wave): it exists for
-// M * U <= 32.
-constexpr bool narrow_fits(int M, int U) { return U >= 1 && U <= 8 && M * U <= 32; }
+// M * U <= 48.
+constexpr bool narrow_fits(int M, int U) { return U >= 1 && U <= 8 && M * U <= 48; }
 
 // Thread-local error message; returns `st` for convenient chaining.
 twd_status set_error(twd_status st, const char *fmt, ...);
@@ -54,6 +54,12 @@ hipError_t launch_narrow(const uint8_t *w, const void *act, bool fused,
 // shape (rows per wave, waves per workgroup) comes from rows_shape.
 void rows_shape(int M, int N, int *rows_per_wave, int *waves);
 hipError_t launch_rows(const uint8_t *w, const void *act, bool fused, const float *xscale,
+                       int M, int K, int N, const Segments &segs, int32_t *acc, float *y,
+                       hipStream_t stream);
+// Tile-owner MFMA kernel (ternary_tile.hip): 64 rows per workgroup, one
+// 16-row tile per wave over all of K; K <= 3072.
+bool tile_supported(int M, int K);
+hipError_t launch_tile(const uint8_t *w, const void *act, bool fused, const float *xscale,
                        int M, int K, int N, const Segments &segs, int32_t *acc, float *y,
                        hipStream_t stream);
 // Staged matrix-core kernel (ternary_staged.hip): any M <= 16 and K.

@@ -129,13 +129,14 @@ SMALL_SHAPES = [
 ]
 
 # (kernel family, widest M it takes); KERNEL_MFMA runs the straight-line
-# matrix-core kernel where its registers allow and the staged one otherwise
-FAMILIES = [("dot", 4), ("mfma", 16), ("mfma_staged", 16)]
+# matrix-core kernel where its registers allow and KERNEL_MFMA_TILE the
+# tile-owner one for K <= 3072; both run the staged kernel otherwise
+FAMILIES = [("dot", 4), ("mfma", 16), ("mfma_staged", 16), ("mfma_tile", 16)]
 
 
 def family(twd, name):
     return {"dot": twd.KERNEL_DOT, "mfma": twd.KERNEL_MFMA,
-            "mfma_staged": twd.KERNEL_MFMA_STAGED}[name]
+            "mfma_staged": twd.KERNEL_MFMA_STAGED, "mfma_tile": twd.KERNEL_MFMA_TILE}[name]
 
 
 @pytest.mark.parametrize("fused", [False, True], ids=["int8", "bf16"])
@@ -160,8 +161,9 @@ def test_fused_bf16_zero_rows_and_outliers(env, M):
     if M > 1:
         xf[1, ::97] *= 20.0
     x = wl.f32_to_bf16_bits(xf)
-    for kernel in ((twd.KERNEL_MFMA, twd.KERNEL_MFMA_STAGED, twd.KERNEL_DOT) if M <= 4
-                   else (twd.KERNEL_MFMA, twd.KERNEL_MFMA_STAGED)):
+    for kernel in ((twd.KERNEL_MFMA, twd.KERNEL_MFMA_STAGED, twd.KERNEL_MFMA_TILE,
+                    twd.KERNEL_DOT) if M <= 4
+                   else (twd.KERNEL_MFMA, twd.KERNEL_MFMA_STAGED, twd.KERNEL_MFMA_TILE)):
         acc, y = run_case(env, W, segs, x, kernel, ("rand", 7), fused=True)
         assert not acc[0].any() and not y[0].any()
 
@@ -179,7 +181,8 @@ def test_single_linear_workload(env):
     """The single-linear case: M=1, K=256, N=512, seed 0."""
     torch, twd, orc = env
     W, segs, x = wl.single_case(seed=0)
-    for kernel in (twd.KERNEL_AUTO, twd.KERNEL_DOT, twd.KERNEL_MFMA, twd.KERNEL_MFMA_STAGED):
+    for kernel in (twd.KERNEL_AUTO, twd.KERNEL_DOT, twd.KERNEL_MFMA, twd.KERNEL_MFMA_STAGED,
+                   twd.KERNEL_MFMA_TILE):
         for fused in (False, True):
             run_case(env, W, segs, x, kernel, ("single", 0), fused=fused)
 
@@ -191,8 +194,9 @@ def test_width_invariance(env):
     wp, gammas = prepared(twd, torch, W, segs, ("rand", 3))
     xq, xs = twd.quantize_act(to_dev_bf16(torch, x))
     full = {}
-    for kernel in (twd.KERNEL_MFMA_STAGED, twd.KERNEL_MFMA, twd.KERNEL_DOT):
-        for M in (4, 2, 1) if kernel == twd.KERNEL_DOT else (16, 10, 8, 4, 1):
+    for kernel in (twd.KERNEL_MFMA_STAGED, twd.KERNEL_MFMA, twd.KERNEL_MFMA_TILE,
+                   twd.KERNEL_DOT):
+        for M in (4, 2, 1) if kernel == twd.KERNEL_DOT else (16, 13, 10, 8, 5, 4, 1):
             acc, _ = twd.ternary_linear_fused(wp, segs, gammas, xq[:M].contiguous(),
                                               xs[:M].contiguous(), kernel=kernel)
             full[(kernel, M)] = acc
@@ -242,7 +246,8 @@ def test_invariants_on_gpu(env):
     codes[2] = -1
     wp = torch.from_numpy(twd.pack_ternary(codes)).cuda()
     xq, xs = twd.quantize_act(to_dev_bf16(torch, x))
-    for kernel in (twd.KERNEL_DOT, twd.KERNEL_MFMA, twd.KERNEL_MFMA_STAGED):
+    for kernel in (twd.KERNEL_DOT, twd.KERNEL_MFMA, twd.KERNEL_MFMA_STAGED,
+                   twd.KERNEL_MFMA_TILE):
         acc, y = twd.ternary_linear_fused(wp, (N,), (1.0,), xq, xs, kernel=kernel)
         torch.cuda.synchronize()
         a = acc.cpu().numpy()
@@ -262,7 +267,8 @@ def test_extreme_values(env):
     x = wl.f32_to_bf16_bits(xf)
     W = np.ones((N, K), np.float32)
     W[::3] = -1.0
-    for kernel in (twd.KERNEL_MFMA_STAGED, twd.KERNEL_MFMA, twd.KERNEL_DOT):
+    for kernel in (twd.KERNEL_MFMA_STAGED, twd.KERNEL_MFMA, twd.KERNEL_MFMA_TILE,
+                   twd.KERNEL_DOT):
         xs_ = x[:4] if kernel == twd.KERNEL_DOT else x
         acc, _ = run_case(env, W, (N,), xs_, kernel, ("extreme",))
         assert abs(int(acc.abs().max())) == 127 * K

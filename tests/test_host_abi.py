@@ -172,13 +172,18 @@ def test_quantize_rejects_before_launch(twd):
 def test_select_kernel(twd):
     assert twd.select_kernel(1, 2560, 2560) == twd.KERNEL_DOT
     assert twd.select_kernel(16, 1024, 2560) == twd.KERNEL_MFMA
-    # 16 tokens x 3 slices per wave exceed the straight-line register budget
-    assert twd.select_kernel(16, 2560, 2560) == twd.KERNEL_MFMA_STAGED
+    assert twd.select_kernel(16, 2560, 2560) == twd.KERNEL_MFMA
+    # 16 tokens x 7 slices per wave exceed the straight-line register budget
+    assert twd.select_kernel(16, 6912, 2560) == twd.KERNEL_MFMA_STAGED
+    # wide outputs from M = 4 take the tile-owner kernel (K <= 3072)
+    assert twd.select_kernel(4, 2560, 13824) == twd.KERNEL_MFMA_TILE
+    assert twd.select_kernel(2, 2560, 13824) == twd.KERNEL_MFMA
     assert twd.select_kernel(4, 8192, 2560) == twd.KERNEL_MFMA
     assert twd.select_kernel(2, 2560, 2560) == twd.KERNEL_MFMA
     for M in range(1, 17):
         assert twd.select_kernel(M, 2560, 13824) in (twd.KERNEL_DOT, twd.KERNEL_MFMA,
-                                                     twd.KERNEL_MFMA_STAGED)
+                                                     twd.KERNEL_MFMA_STAGED,
+                                                     twd.KERNEL_MFMA_TILE)
     assert twd.select_kernel(17, 2560, 2560) == -1
     assert twd.select_kernel(1, 100, 2560) == -1
     assert twd.select_kernel(1, 2560, 0) == -1
