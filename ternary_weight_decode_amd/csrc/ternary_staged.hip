@@ -14,10 +14,10 @@
 // K group = lane / 16).  The four 2-bit planes of a lane's four words are the
 // A operands of four MFMAs (codes, 4x codes, 16x codes, codes), each with
 // its own accumulator, shifted back exactly at the end; sum q t = sum q c -
-// sum q with c = t + 1.  Separate staging waves (one per token row, up to
-// four) quantize (FUSED) or copy the activation rows into LDS while the
-// compute waves' weight loads are in flight; each wave waits only for its
-// own loads.
+// sum q with c = t + 1.  Separate staging waves (up to eight, each with
+// one or two token rows) issue the loads of all their rows at once, then
+// quantize (FUSED) or copy the rows into LDS while the compute waves' weight
+// loads are in flight; each wave waits only for its own loads.
 #include "kernel_common.h"
 
 namespace twd {
@@ -25,9 +25,12 @@ namespace {
 
 using namespace kern;
 
-// Waves that stage activation rows (one row at a time each).
+// Waves that stage activation rows, and rows per staging wave.
 template <int M>
-__host__ __device__ constexpr int staging_waves() { return M < 4 ? M : 4; }
+__host__ __device__ constexpr int staging_waves() { return M < 8 ? M : 8; }
+
+template <int M>
+__host__ __device__ constexpr int rows_per_stager() { return (M + staging_waves<M>() - 1) / staging_waves<M>(); }
 
 template <int M>
 __host__ __device__ constexpr int block_threads() { return 64 * (kWaves + staging_waves<M>()); }
@@ -47,69 +50,86 @@ __host__ __device__ constexpr int lds_bytes(int K) {
     return act_region_bytes<M, TW>(K) + 2 * M * 4;
 }
 
-// Staging wave: quantize (FUSED) or copy one activation row into LDS, with
-// its sum of q and its scale.  One wave covers the whole row, so the absmax
-// and the sum are wave reductions.
-template <bool FUSED>
-__device__ __forceinline__ void stage_row(const void *__restrict__ act,
-                                          const float *__restrict__ xscale,
-                                          int m, int K, int lane, uint8_t *dst,
-                                          int32_t *st_sum, float *st_scale) {
-    constexpr int kMax = 16;  // 16-byte chunks per lane (K <= 8192 bf16)
-    const int cpr = FUSED ? K >> 3 : K >> 4;
-    const uint4 *src = static_cast<const uint4 *>(act) + static_cast<int64_t>(m) * cpr;
-    uint4 v[kMax];
+// Staging wave: quantize (FUSED) or copy the activation rows m0, m0 + step,
+// ... (RPW of them, those below M) into LDS, with their sums of q and their
+// scales.  The loads of all its rows are issued first (16-byte buffer loads,
+// zeros past the row), so the rows' latencies overlap; one wave covers a
+// whole row, so the absmax and the sum are wave reductions.
+template <bool FUSED, int RPW>
+__device__ __forceinline__ void stage_rows(const void *__restrict__ act,
+                                           const float *__restrict__ xscale,
+                                           int m0, int step, int M, int K, int lane,
+                                           uint8_t *smem, int ldsK, int32_t *st_sum,
+                                           float *st_scale) {
+    constexpr int kMax = 16;  // 16-byte chunks per lane and row (K <= 8192 bf16)
+    constexpr int kEl = FUSED ? 2 : 1;
+    const int row_bytes = K * kEl;
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void *>(act), 0, M * row_bytes, 0x00020000);
+    uint4 v[RPW][kMax];
 #pragma unroll
-    for (int j = 0; j < kMax; ++j) {
-        const int c = lane + 64 * j;
-        if (c < cpr)
-            v[j] = src[c];
-    }
-    int part = 0;
-    if constexpr (FUSED) {
-        u16x2 am2 = {0, 0};
-#pragma unroll
-        for (int j = 0; j < kMax; ++j)
-            if (lane + 64 * j < cpr) {
-                am2 = absmax_pair(am2, v[j].x);
-                am2 = absmax_pair(am2, v[j].y);
-                am2 = absmax_pair(am2, v[j].z);
-                am2 = absmax_pair(am2, v[j].w);
-            }
-        const float a = __uint_as_float(wave_umax(absmax_bits(am2)));
-        // correctly rounded fp32 division (build flag), as in the
-        // stand-alone quantizer; an all-zero row quantizes to zeros
-        const float inv = a > 0.0f ? 127.0f / a : 0.0f;
+    for (int i = 0; i < RPW; ++i) {
+        const int m = m0 + step * i;
 #pragma unroll
         for (int j = 0; j < kMax; ++j) {
             const int c = lane + 64 * j;
-            if (c < cpr) {
-                const uint32_t lo = quant4(v[j].x, v[j].y, inv);
-                const uint32_t hi = quant4(v[j].z, v[j].w, inv);
-                *reinterpret_cast<uint2 *>(dst + 8 * c) = make_uint2(lo, hi);
+            const uint32_t off = (m < M && 16 * c < row_bytes)
+                                     ? static_cast<uint32_t>(m * row_bytes + 16 * c)
+                                     : 0x80000000u;
+            const auto x = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
+            v[i][j] = make_uint4(x[0], x[1], x[2], x[3]);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        const int m = m0 + step * i;
+        if (m >= M)
+            break;  // wave-uniform
+        uint8_t *dst = smem + m * ldsK;
+        int part = 0;
+        if constexpr (FUSED) {
+            u16x2 am2 = {0, 0};
+#pragma unroll
+            for (int j = 0; j < kMax; ++j) {
+                am2 = absmax_pair(am2, v[i][j].x);
+                am2 = absmax_pair(am2, v[i][j].y);
+                am2 = absmax_pair(am2, v[i][j].z);
+                am2 = absmax_pair(am2, v[i][j].w);
+            }
+            const float a = __uint_as_float(wave_umax(absmax_bits(am2)));
+            // correctly rounded fp32 division (build flag), as in the
+            // stand-alone quantizer; an all-zero row quantizes to zeros
+            const float inv = a > 0.0f ? 127.0f / a : 0.0f;
+#pragma unroll
+            for (int j = 0; j < kMax; ++j) {
+                const int c = lane + 64 * j;
+                const uint32_t lo = quant4(v[i][j].x, v[i][j].y, inv);
+                const uint32_t hi = quant4(v[i][j].z, v[i][j].w, inv);
+                if (16 * c < row_bytes)
+                    *reinterpret_cast<uint2 *>(dst + 8 * c) = make_uint2(lo, hi);
                 part = sdot4(hi, kOnes, sdot4(lo, kOnes, part));
             }
-        }
-        if (lane == 0)
-            st_scale[m] = a / 127.0f;
-    } else {
+            if (lane == 0)
+                st_scale[m] = a / 127.0f;
+        } else {
 #pragma unroll
-        for (int j = 0; j < kMax; ++j) {
-            const int c = lane + 64 * j;
-            if (c < cpr) {
-                *reinterpret_cast<uint4 *>(dst + 16 * c) = v[j];
-                part = sdot4(v[j].w, kOnes, sdot4(v[j].z, kOnes,
-                             sdot4(v[j].y, kOnes, sdot4(v[j].x, kOnes, part))));
+            for (int j = 0; j < kMax; ++j) {
+                const int c = lane + 64 * j;
+                if (16 * c < row_bytes)
+                    *reinterpret_cast<uint4 *>(dst + 16 * c) = v[i][j];
+                part = sdot4(v[i][j].w, kOnes, sdot4(v[i][j].z, kOnes,
+                             sdot4(v[i][j].y, kOnes, sdot4(v[i][j].x, kOnes, part))));
             }
+            if (lane == 0)
+                st_scale[m] = xscale[m];
         }
+        part = wave_sum(part);
+        if (lane < kPad / 16)
+            *reinterpret_cast<uint4 *>(dst + K + 16 * lane) = make_uint4(0u, 0u, 0u, 0u);
         if (lane == 0)
-            st_scale[m] = xscale[m];
+            st_sum[m] = part;
     }
-    part = wave_sum(part);
-    if (lane < kPad / 16)
-        *reinterpret_cast<uint4 *>(dst + K + 16 * lane) = make_uint4(0u, 0u, 0u, 0u);
-    if (lane == 0)
-        st_sum[m] = part;
 }
 
 template <int M, int TW, bool FUSED>
@@ -171,9 +191,8 @@ __global__ __launch_bounds__(block_threads<M>()) void staged_kernel(
         __builtin_amdgcn_sched_barrier(0);
     } else {
         // staging wave sw takes rows sw, sw + NS, ...
-#pragma unroll 1
-        for (int m = wave - kWaves; m < M; m += NS)
-            stage_row<FUSED>(act, xscale, m, K, lane, smem + m * ldsK, st_sum, st_scale);
+        stage_rows<FUSED, rows_per_stager<M>()>(act, xscale, wave - kWaves, NS, M, K, lane,
+                                                smem, ldsK, st_sum, st_scale);
     }
     __syncthreads();  // activation rows staged
 
