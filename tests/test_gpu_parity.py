@@ -335,3 +335,18 @@ def test_errors_on_gpu(env):
     # empty width: no launch, outputs untouched
     acc, y = twd.ternary_linear(wp, 1.0, xq[:0], xs[:0], 64)
     assert acc.shape == (0, 64)
+
+
+def test_measurement_helpers(env):
+    """The copy kernel copies exactly its bytes (its counter readings
+    calibrate the HBM byte counts); the read kernel runs without error."""
+    torch, twd, orc = env
+    n = (1 << 20) + 48
+    src = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda")
+    dst = torch.zeros(n + 64, dtype=torch.uint8, device="cuda")
+    twd.stream_copy(src, dst, n)
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+    twd.stream_read(src, n, sink)
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:n], src)
+    assert not dst[n:].any()

@@ -187,3 +187,16 @@ def test_select_kernel(twd):
     assert twd.select_kernel(17, 2560, 2560) == -1
     assert twd.select_kernel(1, 100, 2560) == -1
     assert twd.select_kernel(1, 2560, 0) == -1
+
+
+def test_measurement_helpers_reject_before_launch(twd):
+    r, c = twd._lib_stream_read, twd._lib_stream_copy
+    assert r(0x1000, 24, 0x2000, None) == 1          # bytes % 16
+    assert r(0x1000, -16, 0x2000, None) == 1         # negative
+    assert r(None, 16, 0x2000, None) == 1            # null
+    assert r(0x1008, 16, 0x2000, None) == 1          # alignment
+    assert r(0x1000, 0, None, None) == 0             # empty: no launch
+    assert c(0x1000, 0x2000, 24, None) == 1
+    assert c(0x1000, None, 16, None) == 1
+    assert c(0x1000, 0x2008, 16, None) == 1
+    assert c(0x1000, 0x2000, 0, None) == 0
