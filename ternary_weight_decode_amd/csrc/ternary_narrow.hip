@@ -233,9 +233,14 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(
             c16 = __builtin_amdgcn_mfma_i32_16x16x64_i8(p2, b2, c16, 0, 0, 0);
             c3 = __builtin_amdgcn_mfma_i32_16x16x64_i8(p3, b3, c3, 0, 0, 0);
         }
-        // lane (r, g) holds rows 4g .. 4g+3 of token r: partials [M][16][wave]
-        const v4i c = c0 + c3 + (c4 >> 2) + (c16 >> 4);
+        // lane (r, g) holds rows 4g .. 4g+3 of token r: partials [M][16][wave],
+        // each less the row sum of q over this wave's slices
         if (r < M) {
+            int qw = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                qw += st_sum[(wave * 4 + i) * M + r];
+            const v4i c = c0 + c3 + (c4 >> 2) + (c16 >> 4) - qw;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 red[(r * 16 + 4 * g + i) * P + wave] = c[i];
@@ -257,9 +262,6 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(
             total += v.x + v.y + v.z + v.w;
         }
         const float scale = FUSED ? st_scale[m] : xscale[m];
-#pragma unroll
-        for (int i = 0; i < 4 * kWaves; ++i)
-            total -= st_sum[i * M + m];
         const int64_t o = static_cast<int64_t>(m) * N + n;
         if (acc)
             acc[o] = total;

@@ -132,7 +132,16 @@ __global__ __launch_bounds__(64 * NW) void rows_kernel(
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // 3. stage the activation rows as int8 (with the row sums of q)
+    // 3. stage the activation rows as int8 (with the row sums of q).
+    //    Everything the epilogue needs besides the dot products -- scales,
+    //    row sums of q, the segment scale of this lane's row -- is settled
+    //    here, while the weights are still in flight.
+    float scale[M];
+    if constexpr (!FUSED) {
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+            scale[m] = xscale[m];
+    }
     int sq[M];
 #pragma unroll
     for (int m = 0; m < M; ++m)
@@ -158,9 +167,10 @@ __global__ __launch_bounds__(64 * NW) void rows_kernel(
             for (int w = 1; w < NW; ++w)
                 am = max(am, st_max[w * M + m]);
             const float a_m = __uint_as_float(am);
-            // correctly rounded fp32 division (build flag), as in the
+            // correctly rounded fp32 divisions (build flag), as in the
             // stand-alone quantizer; an all-zero row quantizes to zeros
             const float inv = a_m > 0.0f ? 127.0f / a_m : 0.0f;
+            scale[m] = a_m / 127.0f;
 #pragma unroll
             for (int v = 0; v < V; ++v) {
                 const int word = tid + T * v;
@@ -188,6 +198,16 @@ __global__ __launch_bounds__(64 * NW) void rows_kernel(
             st_sum[wave * M + m] = s;
     }
     __syncthreads();  // staged rows and row sums
+    const int n = n_wave + r;
+    const float gam = row_gamma(segs, n);
+    int qsum[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        qsum[m] = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+            qsum[m] += st_sum[w * M + m];
+    }
 
     // 4. decode + dot, one load at a time as it arrives
     int tot[M];
@@ -223,29 +243,15 @@ __global__ __launch_bounds__(64 * NW) void rows_kernel(
     }
 
     // 5. row totals across the row group; its last lane writes the outputs
-    const int n = n_wave + r;
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-        int t = group_sum<L>(tot[m]);
+        const int t = group_sum<L>(tot[m]) - qsum[m];
         if (p == L - 1 && n < N) {
-            float scale;
-            if constexpr (FUSED) {
-                uint32_t am = st_max[m];
-#pragma unroll
-                for (int w = 1; w < NW; ++w)
-                    am = max(am, st_max[w * M + m]);
-                scale = __uint_as_float(am) / 127.0f;
-            } else {
-                scale = xscale[m];
-            }
-#pragma unroll
-            for (int w = 0; w < NW; ++w)
-                t -= st_sum[w * M + m];
             const int64_t o = static_cast<int64_t>(m) * N + n;
             if (acc)
                 acc[o] = t;
             if (y)
-                y[o] = static_cast<float>(t) * scale * row_gamma(segs, n);
+                y[o] = static_cast<float>(t) * scale[m] * gam;
         }
     }
 }

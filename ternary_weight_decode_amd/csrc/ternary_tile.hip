@@ -195,6 +195,21 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(
     }
     __syncthreads();  // staged rows, row sums
 
+    // the epilogue's other inputs (row sum of q and scale of token r, segment
+    // scales of the lane's four rows), settled while weights are in flight
+    int qsum = 0;
+    float scale = 0.0f;
+    float gam[4];
+    if (r < M) {
+#pragma unroll
+        for (int i = 0; i < 4 * kWaves; ++i)
+            qsum += st_sum[i * MB + r];
+        scale = FUSED ? st_scale[r] : xscale[r];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        gam[i] = row_gamma(segs, n_t + 4 * g + i);
+
     // 4. decode + MFMA, one slice at a time as its weights arrive
     v4i c0 = {0, 0, 0, 0}, c3 = c0, c4 = c0, c16 = c0;
     const uint8_t *bsrc = r < M ? xs + r * S + 64 * g : zero;
@@ -222,11 +237,6 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(
     //    r: take off the row sum, dequantize, store
     if (r < M) {
         const v4i c = c0 + c3 + (c4 >> 2) + (c16 >> 4);
-        int qsum = 0;
-#pragma unroll
-        for (int i = 0; i < 4 * kWaves; ++i)
-            qsum += st_sum[i * MB + r];
-        const float scale = FUSED ? st_scale[r] : xscale[r];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int n = n_t + 4 * g + i;
@@ -236,7 +246,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(
                 if (acc)
                     acc[o] = total;
                 if (y)
-                    y[o] = static_cast<float>(total) * scale * row_gamma(segs, n);
+                    y[o] = static_cast<float>(total) * scale * gam[i];
             }
         }
     }
