@@ -380,10 +380,40 @@ def summarize_profiles(args):
         a = sum(ent) / len(ent)
         lines.append(f"| {p.name} | {p.K} | {p.N} | {len(ent)} | {a / 1e3:.3f} | "
                      f"{p.packed_bytes / a:.1f} |")
+    gaps = [int(_col(b, "Start_Timestamp")) - int(_col(a, "End_Timestamp"))
+             for a, b in zip(timed[:-1], timed[1:])]
+    gaps.sort()
     lines += ["", f"Average duration over the timed dispatches: **{avg_ns / 1e3:.3f} us** "
               f"(algorithmic bytes per launch {ls.packed_bytes_per_layer / nproj / 1e6:.3f} MB "
               f"-> {ls.packed_bytes_per_layer / nproj / avg_ns:.1f} GB/s); first start to "
-              f"last end {span_ns / 1e3:.1f} us.", ""]
+              f"last end {span_ns / 1e3:.1f} us; median gap between consecutive dispatches "
+              f"{gaps[len(gaps) // 2] / 1e3:.3f} us.", ""]
+
+    def live(path):
+        if not path or not os.path.exists(path):
+            return None
+        with open(path) as f:
+            for line in f:
+                if line.startswith("{"):
+                    return json.loads(line)["roofline"]["avg_launch_us"]
+        return None
+
+    prof_live, bench_live = live(args.profile_run_json), live(args.bench_json)
+    if prof_live is not None or bench_live is not None:
+        lines += ["## Against the live measurement", "",
+                  "bench.py times the step with HIP events around back-to-back graph replays, "
+                  "so its per-launch figure is elapsed time per launch and includes whatever "
+                  "gap separates one kernel from the next.  rocprofv3 reports each kernel "
+                  "from its start to its end; under kernel tracing the profiler also spaces "
+                  "the dispatches apart.", ""]
+        if prof_live is not None:
+            lines.append(f"- the profiled run's own live figure: {prof_live:.3f} us per launch "
+                         f"(profiler-spaced dispatches)")
+        if bench_live is not None:
+            lines.append(f"- the unprofiled default run: **{bench_live:.3f} us** per launch; the "
+                         f"kernels' own {avg_ns / 1e3:.3f} us plus {bench_live - avg_ns / 1e3:.3f} "
+                         f"us of inter-kernel gap in back-to-back replay")
+        lines.append("")
     trace_path = os.path.join(out_dir, f"ternary_linear_{tag}_kernel_trace.md")
     with open(trace_path, "w") as f:
         f.write("\n".join(lines))
@@ -472,6 +502,10 @@ def main():
     ap.add_argument("--profile-commands", nargs=3, metavar=("TRACE_CMD", "FETCH_CMD", "WRITE_CMD"),
                     help="the commands that produced --summarize-profile's inputs")
     ap.add_argument("--profile-out", default=PROFILES)
+    ap.add_argument("--profile-run-json", default=None,
+                    help="stdout of the profiled kernel-trace run (its own live timing)")
+    ap.add_argument("--bench-json", default=None,
+                    help="stdout of an unprofiled run of the default command")
     args = ap.parse_args()
 
     if args.summarize_profile:
@@ -542,17 +576,24 @@ def main():
         for Mw in [int(v) for v in args.widths.split(",") if v]:
             if Mw == M:
                 widths[str(Mw)] = {"gbs": round(lin_gbs, 1), "frac": round(lin_gbs / HBM_PEAK_GBS, 4),
-                                   "us_per_launch": round(lin_dur * 1e6, 3), "kernels": kname}
+                                   "us_per_launch": round(lin_dur * 1e6, 3),
+                                   "two_launch_gbs": round(bytes_step * reps / two_wall / 1e9, 1),
+                                   "kernels": kname}
                 continue
             st = Step(twd, torch, dev_set, args.workload, Mw, kernel, outliers)
             g = capture(torch, st.fused)
             g.replay()
             _, sec = time_replays(torch, g, reps)
             gbs = bytes_step * reps / sec / 1e9
+            del g
+            g2 = capture(torch, st.two_launch)
+            g2.replay()
+            _, sec2 = time_replays(torch, g2, reps)
             widths[str(Mw)] = {"gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
                                "us_per_launch": round(sec / (reps * nlaunch) * 1e6, 3),
+                               "two_launch_gbs": round(bytes_step * reps / sec2 / 1e9, 1),
                                "kernels": kernel_map(twd, ls, Mw, kernel)}
-            del st, g
+            del st, g2
             torch.cuda.empty_cache()
 
     proj_table = per_projection(twd, torch, ls, M, kernel, reps) if args.per_proj else None
