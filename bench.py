@@ -477,6 +477,55 @@ def summarize_profiles(args):
     print(cnt_path)
 
 
+SIMDS = 1024  # MI355X: 256 compute units x 4 SIMDs
+
+
+def summarize_util(args):
+    """Per-kernel means of the utilization counters (one --pmc run).  The
+    instruction counts per wave are exact; the MFMA busy share divides
+    SQ_VALU_MFMA_BUSY_CYCLES (16 per v_mfma_i32_16x16x64_i8) by the SIMD
+    cycles of the dispatch's own duration (2.4 GHz x 1024 SIMDs)."""
+    pmc_dir, command = args.summarize_util
+    M = args.M or wl.workload_widths(args.workload)[0]
+    agg = {}
+    for r in _csv_rows(pmc_dir, "counter_collection.csv"):
+        name = _col(r, "Kernel_Name")
+        if not _linear_fused(name):
+            continue
+        key = (_short(name), int(_col(r, "Grid_Size", "Grid_Size_X", "grid_size")) // 64)
+        d = agg.setdefault(key, {})
+        d.setdefault(_col(r, "Counter_Name"), []).append(float(_col(r, "Counter_Value")))
+        d.setdefault("_dur", {})[_col(r, "Correlation_Id", "Dispatch_Id")] = (
+            int(_col(r, "End_Timestamp")) - int(_col(r, "Start_Timestamp")))
+    lines = [f"# ternary linear, {args.workload}, M={M}: utilization counters", "",
+             "Command (from the repository root):", "", "    " + command, "",
+             "Means per dispatch of the fused linear kernels (one rocprofv3 --pmc run; "
+             "dispatches run slower under counter collection than unprofiled).  MFMA busy "
+             "share = SQ_VALU_MFMA_BUSY_CYCLES / (dispatch duration x 2.4 GHz x 1024 "
+             "SIMDs).", "",
+             "| kernel | waves | dispatches | duration us | MFMA i8 instrs | MFMA busy cycles | "
+             "MFMA busy % | VALU instrs / wave | LDS instrs / wave | LDS bank-conflict cycles |",
+             "|---|---|---|---|---|---|---|---|---|---|"]
+    for (name, waves_grid), d in sorted(agg.items()):
+        durs = list(d.pop("_dur").values())
+        dur_ns = sum(durs) / len(durs)
+        mean = {k: sum(v) / len(v) for k, v in d.items()}
+        waves = mean.get("SQ_WAVES", 0.0) or 1.0
+        busy = mean.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+        lines.append(
+            f"| `{name}` | {waves_grid} | {len(durs)} | {dur_ns / 1e3:.2f} | "
+            f"{mean.get('SQ_INSTS_VALU_MFMA_I8', 0):,.0f} | {busy:,.0f} | "
+            f"{100 * busy / (dur_ns * 2.4 * SIMDS):.2f} | "
+            f"{mean.get('SQ_INSTS_VALU', 0) / waves:.0f} | "
+            f"{mean.get('SQ_INSTS_LDS', 0) / waves:.1f} | "
+            f"{mean.get('SQ_LDS_BANK_CONFLICT', 0):,.0f} |")
+    lines.append("")
+    out = os.path.join(args.profile_out, f"ternary_linear_{args.workload}_m{M}_util.md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+    print(out)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -501,6 +550,8 @@ def main():
                     help="no GPU: summarize rocprofv3 CSV output of this script into profiles/")
     ap.add_argument("--profile-commands", nargs=3, metavar=("TRACE_CMD", "FETCH_CMD", "WRITE_CMD"),
                     help="the commands that produced --summarize-profile's inputs")
+    ap.add_argument("--summarize-util", nargs=2, metavar=("PMC_DIR", "COMMAND"),
+                    help="no GPU: summarize a rocprofv3 --pmc run of the utilization counters")
     ap.add_argument("--profile-out", default=PROFILES)
     ap.add_argument("--profile-run-json", default=None,
                     help="stdout of the profiled kernel-trace run (its own live timing)")
@@ -510,6 +561,9 @@ def main():
 
     if args.summarize_profile:
         summarize_profiles(args)
+        return
+    if args.summarize_util:
+        summarize_util(args)
         return
 
     if args.gpus != 1:

@@ -57,11 +57,15 @@ __host__ __device__ constexpr int row_stride() { return U * 256 + 16; }
 template <int M, int U>
 __host__ __device__ constexpr int wave_bytes() { return M * row_stride<U>() + 64; }
 
-// LDS: per-wave regions | partials [M][16 rows][wave] | absmax partials
-// [wave, DPP row][M] | row-sum partials [wave, DPP row][M] | scales [M].
+// LDS: per-wave regions | partials [M][17][wave] (16 rows, padded so that
+// the 16 token columns a write touches fall on different banks) | absmax
+// partials [wave, DPP row][M] | row-sum partials [wave, DPP row][M] |
+// scales [M].
+constexpr int kRedStride = 17;
+
 template <int M, int U>
 __host__ __device__ constexpr int lds_bytes() {
-    return kWaves * wave_bytes<M, U>() + M * 16 * kWaves * 4 + 2 * 4 * kWaves * M * 4 + M * 4;
+    return kWaves * wave_bytes<M, U>() + M * kRedStride * kWaves * 4 + 2 * 4 * kWaves * M * 4 + M * 4;
 }
 
 // Where lane l's activation word (elements 4l..4l+3 of the slice) is staged:
@@ -88,7 +92,7 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(
 
     uint8_t *own = smem + wave * wave_bytes<M, U>();
     int32_t *red = reinterpret_cast<int32_t *>(smem + kWaves * wave_bytes<M, U>());
-    uint32_t *st_max = reinterpret_cast<uint32_t *>(red + M * 16 * P);   // [16][M]
+    uint32_t *st_max = reinterpret_cast<uint32_t *>(red + M * kRedStride * P);  // [16][M]
     int32_t *st_sum = reinterpret_cast<int32_t *>(st_max + 4 * kWaves * M);  // [16][M]
     float *st_scale = reinterpret_cast<float *>(st_sum + 4 * kWaves * M);    // [M]
     const int part = wave * 4 + (lane >> 4);  // this lane's DPP row in the workgroup
@@ -243,7 +247,7 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(
             const v4i c = c0 + c3 + (c4 >> 2) + (c16 >> 4) - qw;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                red[(r * 16 + 4 * g + i) * P + wave] = c[i];
+                red[(r * kRedStride + 4 * g + i) * P + wave] = c[i];
         }
     }
 
@@ -258,7 +262,7 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(
         int total = 0;
 #pragma unroll
         for (int p = 0; p < P; p += 4) {
-            const int4 v = *reinterpret_cast<const int4 *>(red + idx * P + p);
+            const int4 v = *reinterpret_cast<const int4 *>(red + (m * kRedStride + (idx & 15)) * P + p);
             total += v.x + v.y + v.z + v.w;
         }
         const float scale = FUSED ? st_scale[m] : xscale[m];

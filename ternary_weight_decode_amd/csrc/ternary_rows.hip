@@ -42,14 +42,23 @@ constexpr uint32_t kOutOfRange = 0x80000000u;
 template <int R>
 __host__ __device__ constexpr int lanes_per_row() { return 64 / R; }
 
-// Activation row stride in LDS: all U loads' worth of K, zero past K.
+// Activation row length: all U loads' worth of K, zero past K.  In LDS,
+// 16 bytes of padding follow every 256 bytes (four 64-element chunks), so
+// that the 16-byte reads of the lanes of a row group, 64 bytes apart, fall
+// on different banks.
 template <int R, int U>
-__host__ __device__ constexpr int act_stride() { return U * lanes_per_row<R>() * 64; }
+__host__ __device__ constexpr int act_len() { return U * lanes_per_row<R>() * 64; }
+
+template <int R, int U>
+__host__ __device__ constexpr int act_stride() { return act_len<R, U>() + act_len<R, U>() / 16; }
+
+// LDS byte offset of activation byte k of a staged row.
+__device__ __forceinline__ int act_off(int k) { return k + ((k >> 8) << 4); }
 
 // Staging: each of the NW * 64 threads quantizes / copies the 4-element
 // words t, t + 64 NW, ...
 template <int R, int NW, int U>
-__host__ __device__ constexpr int stage_words() { return (act_stride<R, U>() / 4 + 64 * NW - 1) / (64 * NW); }
+__host__ __device__ constexpr int stage_words() { return (act_len<R, U>() / 4 + 64 * NW - 1) / (64 * NW); }
 
 template <int M, int R, int NW, int U>
 __host__ __device__ constexpr int lds_bytes() { return M * act_stride<R, U>() + 2 * NW * M * 4; }
@@ -74,7 +83,8 @@ __global__ __launch_bounds__(64 * NW) void rows_kernel(
     const float *__restrict__ xscale, int K, int N, Segments segs,
     int32_t *__restrict__ acc, float *__restrict__ y) {
     constexpr int L = lanes_per_row<R>();
-    constexpr int S = act_stride<R, U>();
+    constexpr int S = act_stride<R, U>();  // LDS row stride
+    constexpr int SL = act_len<R, U>();    // staged elements per row
     constexpr int V = stage_words<R, NW, U>();
     constexpr int T = 64 * NW;
     static_assert(L == 8 || L == 16, "row groups of 8 or 16 lanes");
@@ -175,8 +185,8 @@ __global__ __launch_bounds__(64 * NW) void rows_kernel(
             for (int v = 0; v < V; ++v) {
                 const int word = tid + T * v;
                 const uint32_t q = quant4(xb[m][v].x, xb[m][v].y, inv);
-                if (V * T * 4 == S || 4 * word < S)
-                    *reinterpret_cast<uint32_t *>(xs + m * S + 4 * word) = q;
+                if (V * T * 4 == SL || 4 * word < SL)
+                    *reinterpret_cast<uint32_t *>(xs + m * S + act_off(4 * word)) = q;
                 sq[m] = sdot4(q, kOnes, sq[m]);
             }
         }
@@ -186,8 +196,8 @@ __global__ __launch_bounds__(64 * NW) void rows_kernel(
 #pragma unroll
             for (int v = 0; v < V; ++v) {
                 const int word = tid + T * v;
-                if (V * T * 4 == S || 4 * word < S)
-                    *reinterpret_cast<uint32_t *>(xs + m * S + 4 * word) = xi[m][v];
+                if (V * T * 4 == SL || 4 * word < SL)
+                    *reinterpret_cast<uint32_t *>(xs + m * S + act_off(4 * word)) = xi[m][v];
                 sq[m] = sdot4(xi[m][v], kOnes, sq[m]);
             }
     }
@@ -220,7 +230,7 @@ __global__ __launch_bounds__(64 * NW) void rows_kernel(
 #pragma unroll
         for (int m = 0; m < M; ++m)
             d1[m] = d4[m] = d16[m] = 0;
-        const int kb = 64 * (u * L + p);  // first element of this chunk
+        const int kb = act_off(64 * (u * L + p));  // first element of this chunk
 #pragma unroll
         for (int dw = 0; dw < 4; ++dw) {
             const uint32_t w = dw == 0 ? a[u].x : dw == 1 ? a[u].y : dw == 2 ? a[u].z : a[u].w;
