@@ -256,7 +256,7 @@ def counter_traffic(workload, M, launches_bytes):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(ls, workload, M, outliers, budget_s):
+def cpu_baseline(ls, workload, M, outliers, budget_s, threads=None):
     """The CPU oracle (quantize, int8 x ternary loops, dequant) over the
     layers of the set in order, repeating whole passes until its compute time
     reaches budget_s; timed on the host's cores.  Setup (weight generation and
@@ -264,7 +264,7 @@ def cpu_baseline(ls, workload, M, outliers, budget_s):
     not timed."""
     import oracle
     oracle.build(force=False)
-    threads = host_threads()
+    threads = threads or host_threads()
 
     def prep(key):
         layer, pi = key
@@ -287,7 +287,7 @@ def cpu_baseline(ls, workload, M, outliers, budget_s):
         spent += time.perf_counter() - t0
         done_bytes += p.packed_bytes
 
-    with ThreadPoolExecutor(max_workers=threads) as ex:
+    with ThreadPoolExecutor(max_workers=host_threads()) as ex:
         prepared = list(ex.map(prep, keys))
     while passes == 0 or spent < budget_s:
         for item in prepared:
@@ -653,9 +653,10 @@ def main():
     proj_table = per_projection(twd, torch, ls, M, kernel, reps) if args.per_proj else None
     calib = copy_calibration(twd, torch) if args.copy_calibration else None
 
-    cpu = None
+    cpu = cpu1 = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(ls, args.workload, M, outliers, args.cpu_seconds)
+        cpu1 = cpu_baseline(ls, args.workload, M, outliers, args.cpu_seconds / 3, threads=1)
 
     out = {
         "metric": METRIC,
@@ -696,6 +697,7 @@ def main():
         "widths": widths,
         "per_projection_cold": proj_table,
         "cpu_baseline": cpu,
+        "cpu_single_thread": cpu1,
     }
     if calib:
         out["copy_calibration_bytes"] = calib
