@@ -3,7 +3,7 @@
 // "Methodology in Plain English", paragraph 3).  By measurement on the 2B
 // layer shapes: at M = 1 the row-owner VALU dot kernel is fastest (whole
 // 128-byte lines per load, no cross-wave reduction); from M = 2 the matrix
-// cores win, since the VALU work grows with M.  From M = 4 a wide output
+// cores win, since the VALU work grows with M.  From M = 3 a wide output
 // (at least ~200 workgroups of 64 rows) takes the tile-owner kernel, which
 // quantizes the activations once per 64 rows instead of once per 16; else the
 // straight-line MFMA kernel while each wave's activation slices fit in
@@ -21,7 +21,7 @@ LinearPlan plan_linear(int M, int K, int N, int forced_kernel) {
     if (k == TWD_KERNEL_AUTO) {
         if (M == 1)
             k = TWD_KERNEL_DOT;
-        else if (M >= 4 && N / 64 >= 200 && tile_supported(M, K))
+        else if (M >= 3 && N / 64 >= 200 && tile_supported(M, K))
             k = TWD_KERNEL_MFMA_TILE;
         else
             k = TWD_KERNEL_MFMA;

@@ -280,8 +280,8 @@ bool pick_u(int U, Fn *fn, int *lds) {
 }
 
 // U = ceil(K / (64 L)) <= 8 (R = 4) or 16 (R = 8) for K <= 8192.  The
-// shapes with 8 rows per wave (wide outputs) exist for M = 1 only; M = 2..4
-// take 4 rows per wave and four waves.
+// shapes with 8 rows per wave (wide outputs) exist for M <= 2; M = 3, 4 take
+// 4 rows per wave and four waves.
 template <bool FUSED>
 bool pick(int M, int R, int NW, int U, Fn *fn, int *lds) {
     if (R == 4 && NW == 4) {
@@ -293,12 +293,16 @@ bool pick(int M, int R, int NW, int U, Fn *fn, int *lds) {
         }
         return false;
     }
-    if (M != 1 || R != 8)
+    if (M > 2 || R != 8)
         return false;
-    if (NW == 4)
+    if (M == 1 && NW == 4)
         return pick_u<1, 8, 4, FUSED, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>(U, fn, lds);
-    if (NW == 8)
+    if (M == 1 && NW == 8)
         return pick_u<1, 8, 8, FUSED, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>(U, fn, lds);
+    if (M == 2 && NW == 4)
+        return pick_u<2, 8, 4, FUSED, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>(U, fn, lds);
+    if (M == 2 && NW == 8)
+        return pick_u<2, 8, 8, FUSED, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>(U, fn, lds);
     return false;
 }
 
@@ -311,7 +315,7 @@ bool pick(int M, int R, int NW, int U, Fn *fn, int *lds) {
 void rows_shape(int M, int N, int *rows_per_wave, int *waves) {
     *rows_per_wave = 4;
     *waves = 4;
-    if (M != 1)
+    if (M > 2)
         return;
     if (N / 64 >= 200) {
         *rows_per_wave = 8;

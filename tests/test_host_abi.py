@@ -175,8 +175,8 @@ def test_select_kernel(twd):
     assert twd.select_kernel(16, 2560, 2560) == twd.KERNEL_MFMA
     # 16 tokens x 7 slices per wave exceed the straight-line register budget
     assert twd.select_kernel(16, 6912, 2560) == twd.KERNEL_MFMA_STAGED
-    # wide outputs from M = 4 take the tile-owner kernel (K <= 3072)
-    assert twd.select_kernel(4, 2560, 13824) == twd.KERNEL_MFMA_TILE
+    # wide outputs from M = 3 take the tile-owner kernel (K <= 3072)
+    assert twd.select_kernel(3, 2560, 13824) == twd.KERNEL_MFMA_TILE
     assert twd.select_kernel(2, 2560, 13824) == twd.KERNEL_MFMA
     assert twd.select_kernel(4, 8192, 2560) == twd.KERNEL_MFMA
     assert twd.select_kernel(2, 2560, 2560) == twd.KERNEL_MFMA
