@@ -350,3 +350,29 @@ def test_measurement_helpers(env):
     torch.cuda.synchronize()
     assert torch.equal(dst[:n], src)
     assert not dst[n:].any()
+
+
+def _random_shapes(seed=2024):
+    """One seeded random draw per width M = 1..16: K a multiple of 64 up to
+    4096, 1..4 segments of 1..400 rows."""
+    rng = np.random.default_rng(seed)
+    shapes = []
+    for M in range(1, 17):
+        K = 64 * int(rng.integers(1, 65))
+        nseg = int(rng.integers(1, 5))
+        segs = tuple(int(v) for v in rng.integers(1, 401, size=nseg))
+        shapes.append((M, K, segs))
+    return shapes
+
+
+@pytest.mark.parametrize("M,K,segs", _random_shapes())
+@pytest.mark.parametrize("fam,max_m", FAMILIES)
+def test_random_shapes(env, fam, max_m, M, K, segs):
+    """Random shapes through every family, both forms, against the oracle."""
+    if M > max_m:
+        pytest.skip(f"{fam} takes M <= {max_m}")
+    torch, twd, orc = env
+    W, segs, x = wl.random_case(seed=11, M=M, K=K, seg_rows=segs)
+    ref = orc.forward(W, segs, x)
+    for fused in (False, True):
+        run_case(env, W, segs, x, family(twd, fam), ("rand", 11, K, segs), ref=ref, fused=fused)
