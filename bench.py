@@ -163,17 +163,14 @@ def stream_read_reference(twd, torch, dev_set, reps):
     return dev_set.bytes_per_sweep * reps / sec / 1e9, sec / (reps * len(keys))
 
 
-def kernel_map(twd, ls, M, kernel):
-    """Kernel family each projection of the set runs at width M (a forced
-    KERNEL_MFMA runs the staged form where the straight-line one does not
-    fit, M * ceil(K / 1024) > 48, and a forced KERNEL_MFMA_TILE where
-    K > 3072)."""
+def kernel_map(twd, ls, M, kernel, bf16_input=True):
+    """Kernel family each projection of the set runs at width M, for bf16
+    activations (one launch) or int8 ones (the linear of the two-launch
+    form); a forced KERNEL_MFMA_TILE runs the staged kernel where K > 3072."""
     out = {}
     for p in ls.projs:
         if kernel == twd.KERNEL_AUTO:
-            k = twd.select_kernel(M, p.K, p.N)
-        elif kernel == twd.KERNEL_MFMA and M * (-(-p.K // 1024)) > 48:
-            k = twd.KERNEL_MFMA_STAGED
+            k = twd.select_kernel(M, p.K, p.N, bf16_input)
         elif kernel == twd.KERNEL_MFMA_TILE and p.K > 3072:
             k = twd.KERNEL_MFMA_STAGED
         else:
@@ -632,7 +629,8 @@ def main():
                 widths[str(Mw)] = {"gbs": round(lin_gbs, 1), "frac": round(lin_gbs / HBM_PEAK_GBS, 4),
                                    "us_per_launch": round(lin_dur * 1e6, 3),
                                    "two_launch_gbs": round(bytes_step * reps / two_wall / 1e9, 1),
-                                   "kernels": kname}
+                                   "kernels": kname,
+                                   "two_launch_kernels": kernel_map(twd, ls, M, kernel, False)}
                 continue
             st = Step(twd, torch, dev_set, args.workload, Mw, kernel, outliers)
             g = capture(torch, st.fused)
@@ -646,7 +644,8 @@ def main():
             widths[str(Mw)] = {"gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
                                "us_per_launch": round(sec / (reps * nlaunch) * 1e6, 3),
                                "two_launch_gbs": round(bytes_step * reps / sec2 / 1e9, 1),
-                               "kernels": kernel_map(twd, ls, Mw, kernel)}
+                               "kernels": kernel_map(twd, ls, Mw, kernel),
+                               "two_launch_kernels": kernel_map(twd, ls, Mw, kernel, False)}
             del st, g2
             torch.cuda.empty_cache()
 

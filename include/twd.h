@@ -55,8 +55,8 @@ typedef enum {
     /* row-owner VALU kernel: 2-bit decode in registers + v_dot4 int8;
      * M <= 4 */
     TWD_KERNEL_DOT = 1,
-    /* straight-line matrix-core kernel (v_mfma_i32_16x16x64_i8) where
-     * M * ceil(K / 1024) <= 48, else the staged one */
+    /* straight-line matrix-core kernel (v_mfma_i32_16x16x64_i8): 16 rows
+     * per workgroup, K split over 4, 8 or 16 waves by M and K */
     TWD_KERNEL_MFMA = 2,
     /* matrix cores with separate activation-staging waves: any M, K */
     TWD_KERNEL_MFMA_STAGED = 3,
@@ -171,9 +171,11 @@ twd_status twd_ternary_linear_bf16(const uint8_t *wpacked, int nseg,
                                    int kernel, void *stream);
 
 /* The kernel family the width dispatch picks for (M, K, N), without
- * launching anything.  Returns a twd_kernel value other than
- * TWD_KERNEL_AUTO, or -1 if the shape is unsupported. */
-int twd_select_kernel(int64_t M, int64_t K, int64_t N);
+ * launching anything: for twd_ternary_linear_bf16 if bf16_input != 0, else
+ * for the int8 entry points (the choice can differ where the quantization
+ * inside the launch changes which kernel is fastest).  Returns a twd_kernel
+ * value other than TWD_KERNEL_AUTO, or -1 if the shape is unsupported. */
+int twd_select_kernel(int64_t M, int64_t K, int64_t N, int bf16_input);
 
 /* Measurement helper: a plain streaming read of `bytes` device bytes
  * (16-byte aligned, bytes % 16 == 0) that stores nothing but a guard word

@@ -65,7 +65,7 @@ _lib_fused_kernel = _sig("twd_ternary_linear_fused_kernel",
                          [_p, _int, _p, _p, _p, _p, _i64, _i64, _p, _p, _int, _p])
 _lib_bf16 = _sig("twd_ternary_linear_bf16",
                  [_p, _int, _p, _p, _p, _i64, _i64, _p, _p, _int, _p])
-_lib_select = _sig("twd_select_kernel", [_i64, _i64, _i64])
+_lib_select = _sig("twd_select_kernel", [_i64, _i64, _i64, _int])
 _lib_stream_read = _sig("twd_stream_read", [_p, _i64, _p, _p])
 _lib_stream_copy = _sig("twd_stream_copy", [_p, _p, _i64, _p])
 
@@ -279,10 +279,11 @@ def ternary_linear_bf16(wpacked, seg_rows, seg_gamma, x, acc=None, y=None,
     return acc, y
 
 
-def select_kernel(M: int, K: int, N: int) -> int:
+def select_kernel(M: int, K: int, N: int, bf16_input: bool = True) -> int:
     """Kernel family the width dispatch picks (a KERNEL_* value other than
-    KERNEL_AUTO), or -1 for an unsupported shape."""
-    return int(_lib_select(M, K, N))
+    KERNEL_AUTO) for ternary_linear_bf16 (bf16_input) or for the int8 entry
+    points, or -1 for an unsupported shape."""
+    return int(_lib_select(M, K, N, 1 if bf16_input else 0))
 
 
 def stream_read(buf, nbytes: int, sink, stream=None):

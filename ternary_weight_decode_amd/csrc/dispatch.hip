@@ -6,15 +6,18 @@
 // cores win, since the VALU work grows with M.  From M = 3 a wide output
 // (at least ~200 workgroups of 64 rows) takes the tile-owner kernel, which
 // quantizes the activations once per 64 rows instead of once per 16; else the
-// straight-line MFMA kernel while each wave's activation slices fit in
-// registers, else the staged one.  The dot kernel picks its own launch shape
-// from N; the staged kernel takes two 16-row tiles per workgroup from 512
-// tiles up.
+// straight-line MFMA kernel.  That kernel runs four waves per 16 rows while
+// each wave's activation slices fit in registers; past that it splits K over
+// 8 or 16 waves, which beats the staged kernel on int8 activations but not
+// with the bf16 quantization inside (every one of the extra waves repeats
+// its share of it), so a bf16 input there takes the staged kernel.  The dot
+// kernel picks its own launch shape from N; the staged kernel takes two
+// 16-row tiles per workgroup from 512 tiles up.
 #include "twd_internal.h"
 
 namespace twd {
 
-LinearPlan plan_linear(int M, int K, int N, int forced_kernel) {
+LinearPlan plan_linear(int M, int K, int N, bool bf16_input, int forced_kernel) {
     LinearPlan p;
     p.tiles = 1;
     int k = forced_kernel;
@@ -23,6 +26,8 @@ LinearPlan plan_linear(int M, int K, int N, int forced_kernel) {
             k = TWD_KERNEL_DOT;
         else if (M >= 3 && N / 64 >= 200 && tile_supported(M, K))
             k = TWD_KERNEL_MFMA_TILE;
+        else if (bf16_input && narrow_waves(M, K) != 4)
+            k = TWD_KERNEL_MFMA_STAGED;
         else
             k = TWD_KERNEL_MFMA;
     }

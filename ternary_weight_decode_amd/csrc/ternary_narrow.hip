@@ -10,8 +10,9 @@
 // With FUSED the per-token absmax int8 quantization of the bf16 activations
 // (same arithmetic as the stand-alone quantizer) happens inside.
 //
-// Work split.  A workgroup of four waves owns 16 weight rows and all of K.
-// Wave w takes the 256-wide K slices w, w + 4, ..., exactly U of them (U is a
+// Work split.  A workgroup of NW = 4, 8 or 16 waves owns 16 weight rows and
+// all of K.  Wave w takes the 256-wide K slices w, w + NW, ..., exactly U of
+// them (U is a
 // compile-time count, so every load is straight-line code; a wave with one
 // slice fewer loads a slice whose activations are zero).  All loads are
 // buffer loads: 32-bit offsets against a descriptor whose size bound makes
@@ -63,9 +64,9 @@ __host__ __device__ constexpr int wave_bytes() { return M * row_stride<U>() + 64
 // scales [M].
 constexpr int kRedStride = 17;
 
-template <int M, int U>
+template <int M, int NW, int U>
 __host__ __device__ constexpr int lds_bytes() {
-    return kWaves * wave_bytes<M, U>() + M * kRedStride * kWaves * 4 + 2 * 4 * kWaves * M * 4 + M * 4;
+    return NW * wave_bytes<M, U>() + M * kRedStride * NW * 4 + 2 * 4 * NW * M * 4 + M * 4;
 }
 
 // Where lane l's activation word (elements 4l..4l+3 of the slice) is staged:
@@ -75,12 +76,12 @@ __device__ __forceinline__ int staged_word(int lane) {
     return (lane & 48) | ((lane & 3) << 2) | ((lane >> 2) & 3);
 }
 
-template <int M, int U, bool FUSED>
-__global__ __launch_bounds__(kThreads) void mfma_kernel(
+template <int M, int NW, int U, bool FUSED>
+__global__ __launch_bounds__(64 * NW) void mfma_kernel(
     const uint8_t *__restrict__ W, const void *__restrict__ act,
     const float *__restrict__ xscale, int K, int N, Segments segs,
     int32_t *__restrict__ acc, float *__restrict__ y) {
-    constexpr int P = kWaves;  // partial sums per output
+    constexpr int P = NW;  // partial sums per output
     extern __shared__ __align__(16) uint8_t smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -91,14 +92,14 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(
     const int row_bytes = K >> 2;
 
     uint8_t *own = smem + wave * wave_bytes<M, U>();
-    int32_t *red = reinterpret_cast<int32_t *>(smem + kWaves * wave_bytes<M, U>());
-    uint32_t *st_max = reinterpret_cast<uint32_t *>(red + M * kRedStride * P);  // [16][M]
-    int32_t *st_sum = reinterpret_cast<int32_t *>(st_max + 4 * kWaves * M);  // [16][M]
-    float *st_scale = reinterpret_cast<float *>(st_sum + 4 * kWaves * M);    // [M]
+    int32_t *red = reinterpret_cast<int32_t *>(smem + NW * wave_bytes<M, U>());
+    uint32_t *st_max = reinterpret_cast<uint32_t *>(red + M * kRedStride * P);  // [4 NW][M]
+    int32_t *st_sum = reinterpret_cast<int32_t *>(st_max + 4 * NW * M);  // [4 NW][M]
+    float *st_scale = reinterpret_cast<float *>(st_sum + 4 * NW * M);    // [M]
     const int part = wave * 4 + (lane >> 4);  // this lane's DPP row in the workgroup
 
     // 1. activation loads: lane l takes elements 256 s + 4 l .. + 3 of each
-    //    row for this wave's slices s = wave + 4 u (zeros past K)
+    //    row for this wave's slices s = wave + NW u (zeros past K)
     constexpr int kEl = FUSED ? 2 : 1;  // bytes per element
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<void *>(act), 0, M * K * kEl, kRawBufferFlags);
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(
     uint32_t xi[FUSED ? 1 : M][U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int k0 = 256 * (wave + kWaves * u) + 4 * lane;
+        const int k0 = 256 * (wave + NW * u) + 4 * lane;
 #pragma unroll
         for (int m = 0; m < M; ++m) {
             const uint32_t off =
@@ -132,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const auto v = __builtin_amdgcn_raw_buffer_load_b128(
-            wr, wbase + 64u * static_cast<uint32_t>(wave + kWaves * u), 0, 0);
+            wr, wbase + 64u * static_cast<uint32_t>(wave + NW * u), 0, 0);
         a[u] = make_uint4(v[0], v[1], v[2], v[3]);
     }
     // keep every load issued before any use (the scheduler would otherwise
@@ -172,7 +173,7 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(
         uint32_t am_l = 0;
         if (lane < M) {
 #pragma unroll
-            for (int i = 0; i < 4 * kWaves; ++i)
+            for (int i = 0; i < 4 * NW; ++i)
                 am_l = max(am_l, st_max[i * M + lane]);
         }
         const float a_l = __uint_as_float(am_l);
@@ -254,7 +255,7 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(
     // 5. one thread per output adds its partials, takes off the row sum and
     //    dequantizes
     __syncthreads();
-    for (int idx = tid; idx < M * 16; idx += kThreads) {
+    for (int idx = tid; idx < M * 16; idx += 64 * NW) {
         const int m = idx >> 4;
         const int n = n0 + (idx & 15);
         if (n >= N)
@@ -277,14 +278,15 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(
 using Fn = void (*)(const uint8_t *, const void *, const float *, int, int, Segments,
                     int32_t *, float *);
 
-template <int M, bool FUSED, int... Us>
+template <int M, int NW, bool FUSED, int... Us>
 bool pick_u(int U, Fn *fn, int *lds) {
     bool found = false;
     auto take = [&](auto uc) {
         constexpr int Uc = decltype(uc)::value;
         if constexpr (narrow_fits(M, Uc)) {
-            *fn = &mfma_kernel<M, Uc, FUSED>;
-            *lds = lds_bytes<M, Uc>();
+            static_assert(lds_bytes<M, NW, Uc>() <= 160 * 1024, "LDS budget");
+            *fn = &mfma_kernel<M, NW, Uc, FUSED>;
+            *lds = lds_bytes<M, NW, Uc>();
             found = true;
         }
     };
@@ -292,36 +294,56 @@ bool pick_u(int U, Fn *fn, int *lds) {
     return found;
 }
 
+// U = ceil(ceil(K / 256) / NW) <= 8, 4, 2 for NW = 4, 8, 16 (K <= 8192)
 template <bool FUSED, int... Ms>
-bool pick_m(int M, int U, Fn *fn, int *lds) {
+bool pick_m(int M, int NW, int U, Fn *fn, int *lds) {
     bool found = false;
-    ((M == Ms ? (found = pick_u<Ms, FUSED, 1, 2, 3, 4, 5, 6, 7, 8>(U, fn, lds)) : false), ...);
+    if (NW == 4)
+        ((M == Ms ? (found = pick_u<Ms, 4, FUSED, 1, 2, 3, 4, 5, 6, 7, 8>(U, fn, lds)) : false), ...);
+    else if (NW == 8)
+        ((M == Ms ? (found = pick_u<Ms, 8, FUSED, 1, 2, 3, 4>(U, fn, lds)) : false), ...);
+    else if (NW == 16)
+        ((M == Ms ? (found = pick_u<Ms, 16, FUSED, 1, 2>(U, fn, lds)) : false), ...);
     return found;
 }
 
 }  // namespace
 
+// Waves per 16-row workgroup: the fewest of 4, 8, 16 whose K share per wave
+// (U slices) keeps M x U activation words per lane within the register
+// budget -- more waves split K finer, for wide M or long K.
+int narrow_waves(int M, int K) {
+    const int S = (K + 255) / 256;
+    for (int nw = 4; nw <= 16; nw *= 2)
+        if (narrow_fits(M, (S + nw - 1) / nw))
+            return nw;
+    return 0;
+}
+
 bool narrow_supported(int M, int K) {
-    const int U = (K + 1023) / 1024;
-    return M >= 1 && M <= TWD_MAX_M && narrow_fits(M, U);
+    return M >= 1 && M <= TWD_MAX_M && K >= 1 && narrow_waves(M, K) != 0;
 }
 
 hipError_t launch_narrow(const uint8_t *w, const void *act, bool fused,
                          const float *xscale, int M, int K, int N,
                          const Segments &segs, int32_t *acc, float *y,
-                         hipStream_t stream) {
-    const int U = (K + 1023) / 1024;  // 256-wide slices per wave
+                         hipStream_t stream, int waves) {
+    const int NW = waves ? waves : narrow_waves(M, K);
+    if (NW != 4 && NW != 8 && NW != 16)
+        return hipErrorInvalidValue;
+    const int S = (K + 255) / 256;
+    const int U = (S + NW - 1) / NW;  // 256-wide slices per wave
     Fn fn = nullptr;
     int lds = 0;
     const bool ok =
-        fused ? pick_m<true, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>(M, U, &fn, &lds)
-              : pick_m<false, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>(M, U, &fn, &lds);
+        fused ? pick_m<true, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>(M, NW, U, &fn, &lds)
+              : pick_m<false, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>(M, NW, U, &fn, &lds);
     if (!ok)
         return hipErrorInvalidValue;
     hipError_t e = ensure_lds_limit(reinterpret_cast<const void *>(fn), lds);
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(fn, dim3((N + 15) / 16), dim3(kThreads), lds, stream, w, act,
+    hipLaunchKernelGGL(fn, dim3((N + 15) / 16), dim3(64 * NW), lds, stream, w, act,
                        xscale, K, N, segs, acc, y);
     return hipGetLastError();
 }

@@ -139,7 +139,7 @@ twd_status run_linear(const uint8_t *wpacked, int nseg, const int64_t *seg_rows,
     if (st != TWD_OK || M == 0 || N == 0)
         return st;
     const LinearPlan plan = plan_linear(static_cast<int>(M), static_cast<int>(K),
-                                        static_cast<int>(N), kernel);
+                                        static_cast<int>(N), fused, kernel);
     return hip_status(launch_linear(plan, wpacked, act, fused, xscale,
                                     static_cast<int>(M), static_cast<int>(K),
                                     static_cast<int>(N), segs, acc, y,
@@ -186,12 +186,12 @@ extern "C" twd_status twd_ternary_linear(const uint8_t *wpacked, float gamma,
                                            K, acc, y, TWD_KERNEL_AUTO, stream);
 }
 
-extern "C" int twd_select_kernel(int64_t M, int64_t K, int64_t N) {
+extern "C" int twd_select_kernel(int64_t M, int64_t K, int64_t N, int bf16_input) {
     if (M < 1 || M > TWD_MAX_M || K < 64 || K > TWD_MAX_K || K % 64 != 0 ||
         N < 1 || N > kMaxN)
         return -1;
     return plan_linear(static_cast<int>(M), static_cast<int>(K),
-                       static_cast<int>(N), TWD_KERNEL_AUTO)
+                       static_cast<int>(N), bf16_input != 0, TWD_KERNEL_AUTO)
         .kernel;
 }
 

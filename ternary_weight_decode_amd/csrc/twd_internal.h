@@ -25,13 +25,13 @@ struct LinearPlan {
 
 // The straight-line MFMA kernel holds each wave's activation slices in
 // registers (M x U words, U = 256-wide K slices per wave): it exists for
-// M * U <= 48.
+// M * U <= 48, with 4, 8 or 16 waves sharing K.
 constexpr bool narrow_fits(int M, int U) { return U >= 1 && U <= 8 && M * U <= 48; }
 
 // Thread-local error message; returns `st` for convenient chaining.
 twd_status set_error(twd_status st, const char *fmt, ...);
 
-LinearPlan plan_linear(int M, int K, int N, int forced_kernel);
+LinearPlan plan_linear(int M, int K, int N, bool bf16_input, int forced_kernel);
 
 hipError_t launch_quantize_act(const uint16_t *x, int M, int K, int8_t *xq,
                                float *xscale, hipStream_t stream);
@@ -44,12 +44,15 @@ hipError_t launch_linear(const LinearPlan &plan, const uint8_t *w,
                          int32_t *acc, float *y, hipStream_t stream);
 
 // Straight-line MFMA kernel (ternary_narrow.hip), for the (M, K)
-// narrow_supported accepts.
+// narrow_supported accepts; narrow_waves gives its waves per workgroup
+// (waves = 0), or waves = 4, 8, 16 forces a count (the launch fails if the
+// slices per wave then exceed the register budget).
+int narrow_waves(int M, int K);
 bool narrow_supported(int M, int K);
 hipError_t launch_narrow(const uint8_t *w, const void *act, bool fused,
                          const float *xscale, int M, int K, int N,
                          const Segments &segs, int32_t *acc, float *y,
-                         hipStream_t stream);
+                         hipStream_t stream, int waves = 0);
 // Row-owner VALU dot kernel (ternary_rows.hip): M <= 4, any K; the launch
 // shape (rows per wave, waves per workgroup) comes from rows_shape.
 void rows_shape(int M, int N, int *rows_per_wave, int *waves);

@@ -170,23 +170,29 @@ def test_quantize_rejects_before_launch(twd):
 
 
 def test_select_kernel(twd):
-    assert twd.select_kernel(1, 2560, 2560) == twd.KERNEL_DOT
-    assert twd.select_kernel(16, 1024, 2560) == twd.KERNEL_MFMA
-    assert twd.select_kernel(16, 2560, 2560) == twd.KERNEL_MFMA
-    # 16 tokens x 7 slices per wave exceed the straight-line register budget
-    assert twd.select_kernel(16, 6912, 2560) == twd.KERNEL_MFMA_STAGED
-    # wide outputs from M = 3 take the tile-owner kernel (K <= 3072)
-    assert twd.select_kernel(3, 2560, 13824) == twd.KERNEL_MFMA_TILE
-    assert twd.select_kernel(2, 2560, 13824) == twd.KERNEL_MFMA
-    assert twd.select_kernel(4, 8192, 2560) == twd.KERNEL_MFMA
-    assert twd.select_kernel(2, 2560, 2560) == twd.KERNEL_MFMA
-    for M in range(1, 17):
-        assert twd.select_kernel(M, 2560, 13824) in (twd.KERNEL_DOT, twd.KERNEL_MFMA,
-                                                     twd.KERNEL_MFMA_STAGED,
-                                                     twd.KERNEL_MFMA_TILE)
-    assert twd.select_kernel(17, 2560, 2560) == -1
-    assert twd.select_kernel(1, 100, 2560) == -1
-    assert twd.select_kernel(1, 2560, 0) == -1
+    for bf16 in (True, False):
+        assert twd.select_kernel(1, 2560, 2560, bf16) == twd.KERNEL_DOT
+        assert twd.select_kernel(16, 1024, 2560, bf16) == twd.KERNEL_MFMA
+        assert twd.select_kernel(16, 2560, 2560, bf16) == twd.KERNEL_MFMA
+        # wide outputs from M = 3 take the tile-owner kernel (K <= 3072)
+        assert twd.select_kernel(3, 2560, 13824, bf16) == twd.KERNEL_MFMA_TILE
+        assert twd.select_kernel(2, 2560, 13824, bf16) == twd.KERNEL_MFMA
+        assert twd.select_kernel(4, 8192, 2560, bf16) == twd.KERNEL_MFMA
+        assert twd.select_kernel(2, 2560, 2560, bf16) == twd.KERNEL_MFMA
+        # a long K past four waves' register budget: int8 activations split
+        # K over more waves of the straight-line kernel; with the bf16
+        # quantization inside, the staged kernel is faster
+        for M, K, N in ((16, 6912, 2560), (16, 8192, 3072), (7, 6912, 2560)):
+            assert twd.select_kernel(M, K, N, bf16) == (
+                twd.KERNEL_MFMA_STAGED if bf16 else twd.KERNEL_MFMA)
+        assert twd.select_kernel(6, 6912, 2560, bf16) == twd.KERNEL_MFMA
+        for M in range(1, 17):
+            assert twd.select_kernel(M, 2560, 13824, bf16) in (
+                twd.KERNEL_DOT, twd.KERNEL_MFMA, twd.KERNEL_MFMA_STAGED, twd.KERNEL_MFMA_TILE)
+        assert twd.select_kernel(17, 2560, 2560, bf16) == -1
+        assert twd.select_kernel(1, 100, 2560, bf16) == -1
+        assert twd.select_kernel(1, 2560, 0, bf16) == -1
+    assert twd.select_kernel(16, 6912, 2560) == twd.KERNEL_MFMA_STAGED  # default: bf16
 
 
 def test_measurement_helpers_reject_before_launch(twd):
