@@ -1,4 +1,5 @@
-"""CPU oracle for the W2A8 ternary linear layer -- TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for the W2A8 ternary linear layer and the role-dependent
+(FP8 fast / bf16 critical) projections -- TEST INFRASTRUCTURE ONLY.
 
 Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  The product library never links,
@@ -64,6 +65,18 @@ def _load():
     lib.orc_dequant.restype = None
     lib.orc_max_threads.argtypes = []
     lib.orc_max_threads.restype = ctypes.c_int
+    lib.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
+    lib.orc_e4m3_decode.restype = ctypes.c_double
+    lib.orc_e4m3_encode.argtypes = [ctypes.c_float, p]
+    lib.orc_e4m3_encode.restype = ctypes.c_int
+    lib.orc_quantize_fp8_rows.argtypes = [p, i64, i64, p, p]
+    lib.orc_quantize_fp8_rows.restype = ctypes.c_int
+    lib.orc_quantize_act_fp8.argtypes = [p, i64, i64, p, p]
+    lib.orc_quantize_act_fp8.restype = ctypes.c_int
+    lib.orc_fp8_linear.argtypes = [p, p, i64, i64, i64, p, p]
+    lib.orc_fp8_linear.restype = ctypes.c_int
+    lib.orc_bf16_linear.argtypes = [p, p, i64, i64, i64, p, p]
+    lib.orc_bf16_linear.restype = None
     _lib = lib
     return lib
 
@@ -171,3 +184,93 @@ def forward(W: np.ndarray, seg_rows, x_bf16: np.ndarray, threads: int = 1):
     acc = linear(q, t, threads)
     y = dequant(acc, s, grow)
     return dict(t=t, gammas=gammas, gamma_row=grow, q=q, scale=s, acc=acc, y=y)
+
+
+# ---------------------------------------------------------------------------
+# Role-dependent projections ("Methodology in Plain English", the paragraph
+# on M1: "fast" projections for drafting, "critical" ones for autoregressive
+# steps and verification, FP8 draft projections on H20).  Readings stated at
+# the top of oracle.c.
+# ---------------------------------------------------------------------------
+
+def e4m3_decode(code: int) -> float:
+    """Value of an OCP E4M3 code (NaN for 0x7F / 0xFF)."""
+    return float(_load().orc_e4m3_decode(int(code) & 0xFF))
+
+
+def e4m3_encode(v: float) -> int:
+    """fp32 value -> E4M3 code, round to nearest, ties to even.  Raises if v
+    is not finite or rounds beyond 448."""
+    out = ctypes.c_uint8(0)
+    rc = _load().orc_e4m3_encode(ctypes.c_float(v), ctypes.byref(out))
+    if rc != 0:
+        raise ValueError(f"{v!r} has no finite E4M3 code")
+    return int(out.value)
+
+
+def quantize_fp8_rows(W: np.ndarray):
+    """Per-output-row absmax FP8 quantization of weights (fp32 [N, K]).
+    Returns (codes uint8 [N, K], scale fp32 [N])."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    N, K = W.shape
+    codes = np.empty((N, K), dtype=np.uint8)
+    s = np.empty(N, dtype=np.float32)
+    if _load().orc_quantize_fp8_rows(_ptr(W), N, K, _ptr(codes), _ptr(s)) != 0:
+        raise ValueError("non-finite weight")
+    return codes, s
+
+
+def quantize_act_fp8(x_bf16: np.ndarray):
+    """Per-token absmax FP8 quantization of bf16 activations [M, K].
+    Returns (codes uint8 [M, K], scale fp32 [M])."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    M, K = x.shape
+    codes = np.empty((M, K), dtype=np.uint8)
+    s = np.empty(M, dtype=np.float32)
+    rc = _load().orc_quantize_act_fp8(_ptr(x), M, K, _ptr(codes), _ptr(s))
+    if rc != 0:
+        raise ValueError("non-finite activation or K > 8192")
+    return codes, s
+
+
+def fp8_linear(xq: np.ndarray, wq: np.ndarray):
+    """Exact sum_k dec(xq[m, k]) dec(wq[n, k]) and the same sum of absolute
+    products, as float64 [M, N] each."""
+    xq = np.ascontiguousarray(xq, dtype=np.uint8)
+    wq = np.ascontiguousarray(wq, dtype=np.uint8)
+    M, K = xq.shape
+    N, K2 = wq.shape
+    if K != K2:
+        raise ValueError("K mismatch")
+    dot = np.empty((M, N), dtype=np.float64)
+    absdot = np.empty((M, N), dtype=np.float64)
+    if _load().orc_fp8_linear(_ptr(xq), _ptr(wq), M, N, K, _ptr(dot), _ptr(absdot)) != 0:
+        raise ValueError("NaN code")
+    return dot, absdot
+
+
+def bf16_linear(x_bf16: np.ndarray, w_bf16: np.ndarray):
+    """sum_k x[m, k] w[n, k] over bf16 bit patterns, in double, and the sum of
+    absolute products, as float64 [M, N] each."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    w = np.ascontiguousarray(w_bf16, dtype=np.uint16)
+    M, K = x.shape
+    N, K2 = w.shape
+    if K != K2:
+        raise ValueError("K mismatch")
+    dot = np.empty((M, N), dtype=np.float64)
+    absdot = np.empty((M, N), dtype=np.float64)
+    _load().orc_bf16_linear(_ptr(x), _ptr(w), M, N, K, _ptr(dot), _ptr(absdot))
+    return dot, absdot
+
+
+def fast_projection(W: np.ndarray, x_bf16: np.ndarray):
+    """The fast (FP8) projection on the CPU: quantize the weights per row and
+    the activations per token, contract exactly, dequantize in double.
+    Returns a dict of every intermediate."""
+    wq, ws = quantize_fp8_rows(W)
+    xq, xs = quantize_act_fp8(x_bf16)
+    dot, absdot = fp8_linear(xq, wq)
+    scale = xs.astype(np.float64)[:, None] * ws.astype(np.float64)[None, :]
+    return dict(wq=wq, wscale=ws, xq=xq, xscale=xs, dot=dot, absdot=absdot,
+                y=dot * scale, yabs=absdot * scale)

@@ -27,6 +27,18 @@ def read_golden(name):
     return out
 
 
+def read_golden_rows(name, key):
+    """Every 'KEY v1 v2 ...' line of a golden fixture with the given key, in
+    order (for keys that repeat)."""
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            parts = line.split()
+            if parts and parts[0] == key:
+                rows.append(parts[1:])
+    return rows
+
+
 @pytest.fixture(scope="session")
 def orc():
     import oracle

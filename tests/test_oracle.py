@@ -8,7 +8,7 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
-from conftest import read_golden
+from conftest import read_golden, read_golden_rows
 from workloads import bf16_bits_to_f32, f32_to_bf16_bits
 
 
@@ -245,3 +245,150 @@ def test_segments_concatenate(orc):
     assert gammas == [g0, g1] and g1 > 4 * g0
     np.testing.assert_array_equal(t, np.concatenate([t0, t1]))
     assert np.all(grow[:32] == g0) and np.all(grow[32:] == g1)
+
+
+# ------------------------------------------- role-dependent projections (FP8)
+
+def _torch_e4m3():
+    torch = pytest.importorskip("torch")
+    if not hasattr(torch, "float8_e4m3fn"):
+        pytest.skip("torch without float8_e4m3fn")
+    return torch
+
+
+def test_e4m3_decode_against_torch_and_hand(orc):
+    torch = _torch_e4m3()
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    got = np.array([orc.e4m3_decode(c) for c in range(256)])
+    assert np.array_equal(np.isnan(ref), np.isnan(got))
+    assert np.isnan(got).sum() == 2 and np.isnan(got[0x7F]) and np.isnan(got[0xFF])
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(got[ok], ref[ok])
+    g = read_golden("fp8_e4m3_hand.txt")
+    for key, vals in g.items():
+        if key.startswith("DECODE_"):
+            c = int(key[7:], 16)
+            v = orc.e4m3_decode(c)
+            assert v == float(vals[0]) and math.copysign(1, v) == math.copysign(1, float(vals[0]))
+
+
+def test_e4m3_encode_hand_ties(orc):
+    rows = read_golden_rows("fp8_e4m3_hand.txt", "ENCODE")
+    assert len(rows) == 8
+    for v, c in rows:
+        assert orc.e4m3_encode(float(v)) == int(c, 16), v
+    with pytest.raises(ValueError):
+        orc.e4m3_encode(470.0)  # rounds to 480, beyond the largest finite value
+    with pytest.raises(ValueError):
+        orc.e4m3_encode(float("inf"))
+
+
+def test_e4m3_encode_against_torch(orc):
+    torch = _torch_e4m3()
+    rng = np.random.default_rng(11)
+    finite = np.array([orc.e4m3_decode(c) for c in range(0x7F)])  # 0 .. 448
+    mids = (finite[:-1] + finite[1:]) / 2  # every tie between neighbours
+    f32 = mids.astype(np.float32)
+    assert np.array_equal(f32.astype(np.float64), mids)  # ties are exact in fp32
+    up = np.nextafter(f32, np.float32(np.inf))
+    dn = np.nextafter(f32, np.float32(0))
+    rand = np.exp(rng.uniform(np.log(2.0 ** -12), np.log(448.0), 3000)).astype(np.float32)
+    vals = np.concatenate([f32, up, dn, rand, finite.astype(np.float32)])
+    vals = vals[np.abs(vals) < 464.0]
+    vals = np.concatenate([vals, -vals])
+    ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([orc.e4m3_encode(float(v)) for v in vals], dtype=np.uint8)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_e4m3_round_trip_every_code(orc):
+    for c in range(256):
+        if c in (0x7F, 0xFF):
+            continue
+        assert orc.e4m3_encode(orc.e4m3_decode(c)) == c
+
+
+def test_fp8_quantizer_properties(orc):
+    rng = np.random.default_rng(12)
+    M, K = 6, 320
+    x = rng.standard_normal((M, K)).astype(np.float32) * np.float32(3.0)
+    x[2] = 0.0
+    x[3, 7] = 500.0  # a single outlier dominates the scale
+    xb = f32_to_bf16_bits(x)
+    codes, s = orc.quantize_act_fp8(xb)
+    xf = bf16_bits_to_f32(xb)
+    dec = np.vectorize(orc.e4m3_decode)(codes)
+    for m in range(M):
+        a = np.float32(np.abs(xf[m]).max())
+        if a == 0:
+            assert not codes[m].any() and s[m] == 0
+            continue
+        assert s[m] == np.float32(a / np.float32(448.0))
+        assert np.abs(dec[m]).max() == 448.0
+        inv = np.float32(448.0) / a
+        p = (xf[m] * inv).astype(np.float64)
+        # |rounding error| <= half the spacing at |p| (2^-10 below 2^-6)
+        spacing = np.where(np.abs(p) < 2.0 ** -6, 2.0 ** -9,
+                           2.0 ** (np.floor(np.log2(np.maximum(np.abs(p), 2.0 ** -6))) - 3))
+        assert np.all(np.abs(dec[m] - p) <= spacing / 2)
+        assert np.all((dec[m] == 0) | (np.sign(dec[m]) == np.sign(p)))
+    # the weight quantizer applies the same rule per output row
+    wc, ws = orc.quantize_fp8_rows(xf)
+    np.testing.assert_array_equal(wc, codes)
+    np.testing.assert_array_equal(ws, s)
+
+
+def test_fp8_linear_exact_against_fractions(orc):
+    rng = np.random.default_rng(13)
+    finite = [c for c in range(256) if c not in (0x7F, 0xFF)]
+    M, N, K = 3, 4, 37
+    xq = rng.choice(finite, size=(M, K)).astype(np.uint8)
+    wq = rng.choice(finite, size=(N, K)).astype(np.uint8)
+    dot, absdot = orc.fp8_linear(xq, wq)
+    val = {c: Fraction(orc.e4m3_decode(c)) for c in finite}
+    for m in range(M):
+        for n in range(N):
+            exact = sum(val[int(xq[m, k])] * val[int(wq[n, k])] for k in range(K))
+            assert Fraction(dot[m, n]) == exact
+            assert Fraction(absdot[m, n]) == sum(abs(val[int(xq[m, k])] * val[int(wq[n, k])])
+                                                 for k in range(K))
+    # extremes: 8192 products of 448 * 448 stay exact
+    big = np.full((1, 8192), 0x7E, np.uint8)
+    d, _ = orc.fp8_linear(big, big)
+    assert d[0, 0] == 448.0 * 448.0 * 8192
+    with pytest.raises(ValueError):
+        orc.fp8_linear(np.array([[0x7F]], np.uint8), np.array([[0x38]], np.uint8))
+
+
+def test_fast_projection_hand_example(orc):
+    g = read_golden("fp8_e4m3_hand.txt")
+    W = np.array([[float(v) for v in g["W"]]], dtype=np.float32)
+    x = np.array([[float(v) for v in g["X0"]], [float(v) for v in g["X1"]]], dtype=np.float32)
+    r = orc.fast_projection(W, f32_to_bf16_bits(x))
+    np.testing.assert_array_equal(r["wq"][0], [int(c, 16) for c in g["WQ"]])
+    np.testing.assert_array_equal(r["xq"][0], [int(c, 16) for c in g["XQ0"]])
+    np.testing.assert_array_equal(r["xq"][1], [int(c, 16) for c in g["XQ1"]])
+    np.testing.assert_array_equal(r["xscale"], [float(v) for v in g["XSCALE"]])
+    assert r["wscale"][0] == 1.0
+    np.testing.assert_array_equal(r["y"][:, 0], [float(v) for v in g["Y"]])
+
+
+def test_bf16_linear_against_fractions(orc):
+    rng = np.random.default_rng(14)
+    M, N, K = 2, 3, 29
+    x = f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    w = f32_to_bf16_bits((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    dot, absdot = orc.bf16_linear(x, w)
+    xf, wf = bf16_bits_to_f32(x), bf16_bits_to_f32(w)
+    for m in range(M):
+        for n in range(N):
+            exact = sum(Fraction(float(xf[m, k])) * Fraction(float(wf[n, k])) for k in range(K))
+            bound = K * 2.0 ** -53 * absdot[m, n]
+            assert abs(Fraction(dot[m, n]) - exact) <= Fraction(bound)
+    # one-hot weight rows pick single activations; a zero row gives zero
+    w1 = np.zeros((2, K), np.uint16)
+    w1[0, 5] = 0x3F80  # 1.0
+    d, _ = orc.bf16_linear(x, w1)
+    np.testing.assert_array_equal(d[:, 0], xf[:, 5].astype(np.float64))
+    assert not d[:, 1].any()
