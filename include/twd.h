@@ -47,6 +47,7 @@ typedef enum {
 #define TWD_MAX_M 16          /* token rows per call */
 #define TWD_MAX_K 8192        /* input width (activation rows are staged in LDS) */
 #define TWD_MAX_SEGMENTS 4    /* independently scaled row segments (fused) */
+#define TWD_MAX_K_PROJECTION 4096 /* input width of the fast / critical projections */
 
 /* Kernel families of the linear; TWD_KERNEL_AUTO lets the width dispatch
  * choose (M1's "select by replay width and input/output dimensions"). */
@@ -176,6 +177,51 @@ twd_status twd_ternary_linear_bf16(const uint8_t *wpacked, int nseg,
  * inside the launch changes which kernel is fastest).  Returns a twd_kernel
  * value other than TWD_KERNEL_AUTO, or -1 if the shape is unsupported. */
 int twd_select_kernel(int64_t M, int64_t K, int64_t N, int bf16_input);
+
+/* ------------------------------------------------------------------------
+ * Role-dependent output projections.  The M1 paragraph of "Methodology in
+ * Plain English" pairs cheaper "fast" projections for drafting with careful
+ * "critical" ones for autoregressive steps and verification, and names FP8
+ * draft projections (on H20).  The pages define neither; the readings here:
+ * fast = OCP E4M3 weights with one fp32 scale per output row and E4M3
+ * activations with one scale per token; critical = bf16 weights and
+ * activations.  Both accumulate in fp32.  W is [N][K] row-major (output
+ * rows x input columns), x is [M][K] bf16 bit patterns, y is fp32 [M][N].
+ * ---------------------------------------------------------------------- */
+
+/* Per-output-row FP8 quantization of weights W[N][K] (fp32, host memory):
+ * a = max_k |W[n][k]|, inv = 448 / a (fp32 division), codes[n][k] =
+ * E4M3(W[n][k] * inv) (fp32 multiply, round to nearest, ties to even),
+ * scale[n] = a / 448 (fp32 division); a == 0 gives zero codes and scale 0.
+ * codes: host uint8 [N][K]; scale: host fp32 [N].
+ * Errors: INVALID_ARG for null pointers, negative sizes or a non-finite W. */
+twd_status twd_quantize_fp8_rows(const float *W, int64_t N, int64_t K,
+                                 uint8_t *codes, float *scale);
+
+/* Fast projection: y[m][n] = (sum_k dec(xq[m][k]) dec(wq[n][k])) * xs[m] *
+ * wscale[n] in fp32, where the per-token FP8 quantization of x_bf16 (xs =
+ * max|x| / 448, xq = E4M3(x * (448 / max|x|)), as twd_quantize_fp8_rows
+ * does per row) happens inside the launch.  wq: device E4M3 codes [N][K]
+ * (16-byte aligned); wscale: device fp32 [N] (16-byte aligned); x_bf16:
+ * device [M][K] (16-byte aligned); y: device fp32 [M][N].  xq (device uint8
+ * [M][K], 8-byte aligned) and xscale (device fp32 [M]) may be NULL; if given
+ * they receive the activation codes and scales.  Sums are accumulated in
+ * fp32 (products of E4M3 values are exact), so y differs from the exact
+ * value by at most the fp32 summation error.
+ * Shapes: 0 <= M <= 16, 0 <= N <= 2^24 (either zero is a no-op), 16 <= K
+ * <= TWD_MAX_K_PROJECTION with K % 16 == 0; else UNSUPPORTED. */
+twd_status twd_projection_fp8(const uint8_t *wq, const float *wscale,
+                              const uint16_t *x_bf16, int64_t M, int64_t K,
+                              int64_t N, float *y, uint8_t *xq, float *xscale,
+                              void *stream);
+
+/* Critical projection: y[m][n] = sum_k x[m][k] w[n][k] over bf16 values,
+ * fp32 accumulation.  w_bf16: device [N][K]; x_bf16: device [M][K] (both
+ * 16-byte aligned); y: device fp32 [M][N].  Shapes as twd_projection_fp8
+ * but 8 <= K with K % 8 == 0. */
+twd_status twd_projection_bf16(const uint16_t *w_bf16, const uint16_t *x_bf16,
+                               int64_t M, int64_t K, int64_t N, float *y,
+                               void *stream);
 
 /* Measurement helper: a plain streaming read of `bytes` device bytes
  * (16-byte aligned, bytes % 16 == 0) that stores nothing but a guard word

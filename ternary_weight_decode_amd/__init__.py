@@ -66,6 +66,9 @@ _lib_fused_kernel = _sig("twd_ternary_linear_fused_kernel",
 _lib_bf16 = _sig("twd_ternary_linear_bf16",
                  [_p, _int, _p, _p, _p, _i64, _i64, _p, _p, _int, _p])
 _lib_select = _sig("twd_select_kernel", [_i64, _i64, _i64, _int])
+_lib_quantize_fp8_rows = _sig("twd_quantize_fp8_rows", [_p, _i64, _i64, _p, _p])
+_lib_proj_fp8 = _sig("twd_projection_fp8", [_p, _p, _p, _i64, _i64, _i64, _p, _p, _p, _p])
+_lib_proj_bf16 = _sig("twd_projection_bf16", [_p, _p, _i64, _i64, _i64, _p, _p])
 _lib_stream_read = _sig("twd_stream_read", [_p, _i64, _p, _p])
 _lib_stream_copy = _sig("twd_stream_copy", [_p, _p, _i64, _p])
 
@@ -73,8 +76,8 @@ EXPORTS = ("twd_version", "twd_last_error", "twd_ternarize_absmean",
            "twd_pack_ternary", "twd_unpack_ternary", "twd_quantize_act",
            "twd_ternary_linear", "twd_ternary_linear_fused",
            "twd_ternary_linear_fused_kernel", "twd_ternary_linear_bf16",
-           "twd_select_kernel",
-           "twd_stream_read", "twd_stream_copy")
+           "twd_select_kernel", "twd_quantize_fp8_rows", "twd_projection_fp8",
+           "twd_projection_bf16", "twd_stream_read", "twd_stream_copy")
 
 
 class TwdError(RuntimeError):
@@ -284,6 +287,59 @@ def select_kernel(M: int, K: int, N: int, bf16_input: bool = True) -> int:
     KERNEL_AUTO) for ternary_linear_bf16 (bf16_input) or for the int8 entry
     points, or -1 for an unsupported shape."""
     return int(_lib_select(M, K, N, 1 if bf16_input else 0))
+
+
+def quantize_fp8_rows(W: np.ndarray):
+    """Per-output-row FP8 (OCP E4M3) quantization of fp32 weights [N, K] for
+    the fast projection -> (codes uint8 [N, K], scale fp32 [N])."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    N, K = W.shape
+    codes = np.empty((N, K), np.uint8)
+    scale = np.empty(N, np.float32)
+    _check(_lib_quantize_fp8_rows(_np_ptr(W), N, K, _np_ptr(codes), _np_ptr(scale)))
+    return codes, scale
+
+
+def projection_fp8(wq, wscale, x, y=None, want_codes=False, stream=None):
+    """Fast (FP8) projection of bf16 activations x [M, K] with E4M3 weight
+    codes wq [N, K] and per-row scales wscale [N].  Returns y fp32 [M, N],
+    or (y, xq uint8 [M, K], xscale fp32 [M]) with want_codes."""
+    torch = _torch()
+    _need(x.dim() == 2 and wq.dim() == 2, "x must be [M, K], wq [N, K]")
+    M, K = x.shape
+    N = wq.shape[0]
+    _need(wq.shape[1] == K, "wq must be [N, K]")
+    _need(wscale.numel() >= N, "wscale must hold N values")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _need(tuple(y.shape) == (M, N), "y must be [M, N]")
+    xq = xs = None
+    if want_codes:
+        xq = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+        xs = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _check(_lib_proj_fp8(_dev_ptr(wq, "wq", (torch.uint8,)),
+                         _dev_ptr(wscale, "wscale", (torch.float32,)),
+                         _dev_ptr(x, "x", (torch.bfloat16, torch.int16)), M, K, N,
+                         _dev_ptr(y, "y", (torch.float32,)),
+                         _dev_ptr(xq, "xq", (torch.uint8,)),
+                         _dev_ptr(xs, "xscale", (torch.float32,)), _stream(stream)))
+    return (y, xq, xs) if want_codes else y
+
+
+def projection_bf16(w, x, y=None, stream=None):
+    """Critical (bf16) projection: y fp32 [M, N] = x [M, K] . w [N, K]^T."""
+    torch = _torch()
+    _need(x.dim() == 2 and w.dim() == 2, "x must be [M, K], w [N, K]")
+    M, K = x.shape
+    N = w.shape[0]
+    _need(w.shape[1] == K, "w must be [N, K]")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _need(tuple(y.shape) == (M, N), "y must be [M, N]")
+    _check(_lib_proj_bf16(_dev_ptr(w, "w", (torch.bfloat16, torch.int16)),
+                          _dev_ptr(x, "x", (torch.bfloat16, torch.int16)), M, K, N,
+                          _dev_ptr(y, "y", (torch.float32,)), _stream(stream)))
+    return y
 
 
 def stream_read(buf, nbytes: int, sink, stream=None):

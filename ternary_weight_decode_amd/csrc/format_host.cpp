@@ -12,6 +12,46 @@ namespace {
 // 16-weight word: element e = 4*j + b sits at bit 8*b + 2*j.
 inline int field_shift(int e) { return 8 * (e & 3) + 2 * (e >> 2); }
 
+// fp32 -> OCP E4M3 code by rounding the fp32 bit pattern: nearest, ties to
+// even.  Returns false when the value rounds beyond the largest finite code
+// (448) or is not finite.
+bool e4m3_from_bits(uint32_t u, uint8_t *code) {
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    if (a >= 0x7F800000u)
+        return false;
+    const int e32 = static_cast<int>(a >> 23) - 127;
+    uint32_t c;
+    if (e32 >= -6) {
+        // keep the exponent and 3 mantissa bits, round on the other 20
+        uint32_t keep = a >> 20;
+        const uint32_t rest = a & 0xFFFFFu;
+        if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u)))
+            ++keep;  // a carry moves into the exponent, as it should
+        c = keep - (120u << 3);  // rebias 127 -> 7
+        if (c > 0x7Eu)
+            return false;
+    } else if (a < 0x00800000u) {
+        c = 0;  // fp32 subnormal: far below half the smallest E4M3 step
+    } else {
+        // subnormal E4M3: m = value / 2^-9, with value = sig 2^(e32 - 23)
+        const uint32_t sig = (a & 0x7FFFFFu) | 0x800000u;
+        const int shift = 14 - e32;  // >= 21
+        if (shift > 25) {
+            c = 0;
+        } else {
+            uint32_t m = sig >> shift;
+            const uint32_t rest = sig & ((1u << shift) - 1u);
+            const uint32_t half = 1u << (shift - 1);
+            if (rest > half || (rest == half && (m & 1u)))
+                ++m;  // m == 8 is the smallest normal code, 0x08
+            c = m;
+        }
+    }
+    *code = static_cast<uint8_t>(sign | c);
+    return true;
+}
+
 }  // namespace
 
 extern "C" twd_status twd_ternarize_absmean(const float *W, int64_t N,
@@ -110,6 +150,47 @@ extern "C" twd_status twd_unpack_ternary(const uint8_t *packed, int64_t N,
                 row[16 * wi + e] = static_cast<int8_t>(static_cast<int>(c) - 1);
             }
         }
+    }
+    return TWD_OK;
+}
+
+// Per-output-row FP8 quantization for the fast projection: inv = 448 /
+// max|row| (fp32 division), code = E4M3(w * inv) (fp32 multiply, nearest
+// even), scale = max|row| / 448; an all-zero row gives zero codes and scale 0.
+extern "C" twd_status twd_quantize_fp8_rows(const float *W, int64_t N, int64_t K,
+                                            uint8_t *codes, float *scale) {
+    using twd::set_error;
+    if (!W || !codes || !scale)
+        return set_error(TWD_ERR_INVALID_ARG, "quantize_fp8_rows: null pointer");
+    if (N < 0 || K < 0)
+        return set_error(TWD_ERR_INVALID_ARG, "quantize_fp8_rows: negative size");
+    for (int64_t n = 0; n < N; ++n) {
+        const float *row = W + n * K;
+        float a = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            if (!std::isfinite(row[k]))
+                return set_error(TWD_ERR_INVALID_ARG,
+                                 "quantize_fp8_rows: non-finite weight at row %lld",
+                                 (long long)n);
+            a = std::fmax(a, std::fabs(row[k]));
+        }
+        uint8_t *out = codes + n * K;
+        if (a == 0.0f) {
+            std::memset(out, 0, static_cast<size_t>(K));
+            scale[n] = 0.0f;
+            continue;
+        }
+        const float inv = 448.0f / a;
+        for (int64_t k = 0; k < K; ++k) {
+            const float p = row[k] * inv;
+            uint32_t bits;
+            std::memcpy(&bits, &p, sizeof bits);
+            if (!e4m3_from_bits(bits, &out[k]))
+                return set_error(TWD_ERR_INVALID_ARG,
+                                 "quantize_fp8_rows: value beyond E4M3 at row %lld",
+                                 (long long)n);
+        }
+        scale[n] = a / 448.0f;
     }
     return TWD_OK;
 }

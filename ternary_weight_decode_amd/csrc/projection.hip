@@ -1,0 +1,380 @@
+// Role-dependent output projections, gfx950: the "fast" FP8 projection for
+// drafting and the "critical" bf16 one for autoregressive steps and
+// verification (BitMTP page, ai.info AI summary, "Methodology in Plain
+// English", the paragraph on M1, which also names FP8 draft projections).
+//
+//   fast     : y[m][n] = (sum_k dec(xq[m][k]) dec(wq[n][k])) * s_m * s_n, with
+//              OCP E4M3 weight codes wq and per-row scales s_n prepared
+//              offline, and the per-token FP8 quantization of the bf16
+//              activations (inv = 448 / max|x|, code = e4m3(x * inv), round
+//              to nearest even, s_m = max|x| / 448) done inside the launch.
+//   critical : y[m][n] = sum_k x[m][k] w[n][k] over bf16 x and w.
+//
+// Both are pure weight streams (1 or 2 bytes per weight, read once for all
+// M <= 16 tokens), so the kernel is built around HBM: a persistent grid of
+// one 16-wave workgroup per compute unit, each wave streaming whole 16-row
+// tiles t = wave id, + total waves, ..., double-buffered in chunks of eight
+// 16-byte loads per lane.
+//
+// Arithmetic.  Every E4M3 value is exactly a bf16 value, so both roles run
+// on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16, fp32 accumulation):
+// a fast-role weight code is widened exactly (v_cvt_pk_f32_fp8, then the
+// high halves of the fp32 results are the bf16 bits), and the activation
+// codes are staged in LDS as the bf16 values they decode to.  The gfx950
+// FP8 matrix instruction was not used: on random codes its sums differ
+// from the exact ones by up to ~1e-4 of the sum of |products|, more than
+// fp32 accumulation of the same products allows.
+//
+// Layout.  In load j of chunk c, lane l (row r = l % 16, K group g = l / 16)
+// reads the 16 bytes at byte (8 c + j) 64 + 16 g of weight row r of its
+// tile: one load covers 64 contiguous bytes of each of 16 rows.  As an MFMA
+// A operand the lane's bf16 values are elements e0 .. e0 + 7 (+ 8 .. 15 for
+// FP8 codes, a second MFMA) of row r; the B operand of token column r reads
+// the same elements of staged token row r, so the contraction covers every
+// k exactly once.  Loads past the row end or past N fall outside the buffer
+// descriptor and return zeros; token columns past M read a zero block.
+#include "kernel_common.h"
+
+namespace twd {
+namespace {
+
+using namespace kern;
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+constexpr int kRawBufferFlags = 0x00020000;
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+constexpr int kProjWaves = 16;            // waves per workgroup
+constexpr int kThreadsP = 64 * kProjWaves;    // threads per workgroup
+constexpr int kLoadsP = 8;                // 16-byte weight loads per lane per chunk
+constexpr int kPieceP = 512;              // activation elements per wave load pass
+constexpr int kPasses = 8;                // passes: K <= 4096
+constexpr int kScaleTiles = 4;            // weight-scale tiles per wave staged in LDS
+
+template <bool FP8>
+struct Role {
+    static constexpr int kElemBytes = FP8 ? 1 : 2;
+    static constexpr int kPerLoad = FP8 ? 64 : 32;  // row elements per 64-byte load step
+    static constexpr int kChunk = kLoadsP * kPerLoad;
+};
+
+// LDS: M staged token rows of Kp bf16 values (stride 2 Kp + 16 bytes, so
+// that the 16 token rows of one B read fall on different banks) | a 16-byte
+// zero block | token scales [16] | weight scales of each wave's first
+// kScaleTiles tiles [kProjWaves][kScaleTiles][16].
+__host__ __device__ constexpr int stage_stride(int Kp) { return 2 * Kp + 16; }
+__host__ __device__ constexpr int stage_bytes(int M, int Kp) {
+    return M * stage_stride(Kp) + 16 + 16 * 4 + kProjWaves * kScaleTiles * 16 * 4;
+}
+
+// Two E4M3 codes (the low or high 16 bits of w) widened exactly to a bf16
+// pair: exact fp32 values whose low 16 bits are zero, so their high halves
+// are the bf16 bits.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_bf16(uint32_t w) {
+    const v2f f = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), HI);
+    return __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
+}
+
+__device__ __forceinline__ v8bf as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    const uint4 u = make_uint4(a, b, c, d);
+    return __builtin_bit_cast(v8bf, u);
+}
+
+template <bool FP8>
+__device__ __forceinline__ void load_chunk(uint4 (&buf)[kLoadsP], const uint8_t *W, int tile,
+                                           int tiles, int N, int row_bytes, int c, int r, int g) {
+    const int n0 = tile * 16;
+    const int rows = tile < tiles ? min(16, N - n0) : 0;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(W + static_cast<int64_t>(tile < tiles ? n0 : 0) * row_bytes), 0,
+        __builtin_amdgcn_readfirstlane(rows * row_bytes), kRawBufferFlags);
+#pragma unroll
+    for (int j = 0; j < kLoadsP; ++j) {
+        const int col = (c * kLoadsP + j) * 64 + 16 * g;
+        const uint32_t off = col < row_bytes ? static_cast<uint32_t>(r * row_bytes + col) : kOutOfRange;
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+        buf[j] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+}
+
+template <bool FP8>
+__device__ __forceinline__ v4f compute_chunk(const uint4 (&buf)[kLoadsP], v4f acc, const uint8_t *bsrc,
+                                             int estep, int c, int g) {
+#pragma unroll
+    for (int j = 0; j < kLoadsP; ++j) {
+        const uint4 w = buf[j];
+        if constexpr (FP8) {
+            const int e0 = (c * kLoadsP + j) * 64 + 16 * g;
+            const v8bf a0 = as_bf16x8(fp8x2_bf16<false>(w.x), fp8x2_bf16<true>(w.x),
+                                      fp8x2_bf16<false>(w.y), fp8x2_bf16<true>(w.y));
+            const v8bf a1 = as_bf16x8(fp8x2_bf16<false>(w.z), fp8x2_bf16<true>(w.z),
+                                      fp8x2_bf16<false>(w.w), fp8x2_bf16<true>(w.w));
+            const v8bf b0 = *reinterpret_cast<const v8bf *>(bsrc + 2 * e0 * estep);
+            const v8bf b1 = *reinterpret_cast<const v8bf *>(bsrc + 2 * (e0 + 8) * estep);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, acc, 0, 0, 0);
+        } else {
+            const int e0 = (c * kLoadsP + j) * 32 + 8 * g;
+            const v8bf a = __builtin_bit_cast(v8bf, w);
+            const v8bf b = *reinterpret_cast<const v8bf *>(bsrc + 2 * e0 * estep);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+        }
+    }
+    return acc;
+}
+
+template <bool FP8>
+__global__ __launch_bounds__(kThreadsP) void projection_kernel(
+    const uint8_t *__restrict__ W, const float *__restrict__ wscale,
+    const uint16_t *__restrict__ x, int M, int K, int N, int Kp, float *__restrict__ y, int ldy,
+    uint8_t *__restrict__ xq_out, float *__restrict__ xs_out) {
+    using R = Role<FP8>;
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 15;
+    const int g = lane >> 4;
+    const int stride = stage_stride(Kp);
+    uint8_t *zero = smem + M * stride;
+    float *st_scale = reinterpret_cast<float *>(zero + 16);
+    float *st_ws = st_scale + 16;  // [wave][kScaleTiles][16]
+    const int row_bytes = K * R::kElemBytes;
+    const int tiles = (N + 15) / 16;
+    const int nwaves = gridDim.x * kProjWaves;
+    const int C = Kp / R::kChunk;  // chunks per tile
+    const int first = blockIdx.x * kProjWaves + wave;
+    const int ntiles = first < tiles ? (tiles - 1 - first) / nwaves + 1 : 0;
+    const int total = ntiles * C;
+
+    // 1. Loads, oldest first, so that waiting for the activations never
+    //    waits for weights: (fast role) one weight scale per thread -- row
+    //    16 (first tile of wave tid / 64, + (tid / 16) % 4 strides) + tid % 16
+    //    -- then this wave's token row, then the first two weight chunks.
+    float wsv = 0.0f;
+    if constexpr (FP8) {
+        const int w = tid >> 6;
+        const int n = (blockIdx.x * kProjWaves + w + ((tid >> 4) & 3) * nwaves) * 16 + (tid & 15);
+        const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float *>(wscale), 0, N * 4, kRawBufferFlags);
+        wsv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            sr, n < N ? static_cast<uint32_t>(4 * n) : kOutOfRange, 0, 0));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // lane l takes elements 512 p + 8 l .. + 7 of pass p (zeros past K)
+    uint4 xv[kPasses];
+    {
+        const int m = wave < M ? wave : 0;
+        const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(x + static_cast<int64_t>(m) * K), 0,
+            __builtin_amdgcn_readfirstlane(wave < M ? K * 2 : 0), kRawBufferFlags);
+#pragma unroll
+        for (int p = 0; p < kPasses; ++p) {
+            const int k0 = kPieceP * p + 8 * lane;
+            const uint32_t off = k0 < K ? static_cast<uint32_t>(2 * k0) : kOutOfRange;
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
+            xv[p] = make_uint4(v[0], v[1], v[2], v[3]);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // Every step issues 8 loads and then 4 stores (out of range, and so
+    // dropped, unless a tile has just finished): the body is straight-line
+    // and the load counter waits stay exact, one chunk always in flight.
+    const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
+        y, 0, M * ldy * 4, kRawBufferFlags);
+    uint4 bA[kLoadsP], bB[kLoadsP];
+    int t_ld = first, c_ld = 0;  // next item to load
+    auto next_load = [&](uint4 (&buf)[kLoadsP]) {
+        load_chunk<FP8>(buf, W, t_ld, tiles, N, row_bytes, c_ld, r, g);
+        if (++c_ld == C) {
+            c_ld = 0;
+            t_ld += nwaves;
+        }
+    };
+    // (the tile-finished condition enters as a row limit, so the stores
+    // stay unconditional per-lane selects rather than a branch)
+    auto put = [&](v4f v, int n, int lim) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool ok = r < M && n + i < lim;
+            const uint32_t off = ok ? static_cast<uint32_t>(4 * (r * ldy + n + i)) : kOutOfRange;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[i]), yr, off, 0, 0);
+        }
+    };
+    const v4f zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    next_load(bA);
+    put(zero4, 0, 0);
+    next_load(bB);
+    put(zero4, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2. stage the activations as bf16 (wave m owns token row m)
+    if constexpr (FP8)
+        st_ws[tid] = wsv;
+    if (wave < M) {
+        const int m = wave;
+        uint8_t *row = smem + m * stride;
+        if constexpr (FP8) {
+            u16x2 am2 = {0, 0};
+#pragma unroll
+            for (int p = 0; p < kPasses; ++p) {
+                am2 = absmax_pair(am2, xv[p].x);
+                am2 = absmax_pair(am2, xv[p].y);
+                am2 = absmax_pair(am2, xv[p].z);
+                am2 = absmax_pair(am2, xv[p].w);
+            }
+            const float a = __uint_as_float(wave_umax(absmax_bits(am2)));
+            // correctly rounded fp32 divisions (build flag)
+            const float inv = a > 0.0f ? 448.0f / a : 0.0f;
+            const float s = a / 448.0f;
+            if (lane == 0) {
+                st_scale[m] = s;
+                if (xs_out && blockIdx.x == 0)
+                    xs_out[m] = s;
+            }
+#pragma unroll
+            for (int p = 0; p < kPasses; ++p) {
+                const int k0 = kPieceP * p + 8 * lane;
+                const uint32_t w4[4] = {xv[p].x, xv[p].y, xv[p].z, xv[p].w};
+                uint32_t q[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t lo = w4[2 * h], hi = w4[2 * h + 1];
+                    // x * inv rounded to fp32 on its own, then to E4M3
+                    // (nearest even); an all-zero row gives +0 codes
+                    const float p0 = __fmul_rn(__uint_as_float(lo << 16), inv);
+                    const float p1 = __fmul_rn(__uint_as_float(lo & 0xFFFF0000u), inv);
+                    const float p2 = __fmul_rn(__uint_as_float(hi << 16), inv);
+                    const float p3 = __fmul_rn(__uint_as_float(hi & 0xFFFF0000u), inv);
+                    const int c01 = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+                    const int c0123 = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, c01, true);
+                    q[h] = a > 0.0f ? static_cast<uint32_t>(c0123) : 0u;
+                }
+                if (xq_out && blockIdx.x == 0 && k0 < K)
+                    *reinterpret_cast<uint2 *>(xq_out + static_cast<int64_t>(m) * K + k0) =
+                        make_uint2(q[0], q[1]);
+                if (k0 < Kp)
+                    *reinterpret_cast<uint4 *>(row + 2 * k0) =
+                        make_uint4(fp8x2_bf16<false>(q[0]), fp8x2_bf16<true>(q[0]),
+                                   fp8x2_bf16<false>(q[1]), fp8x2_bf16<true>(q[1]));
+            }
+        } else {
+#pragma unroll
+            for (int p = 0; p < kPasses; ++p) {
+                const int k0 = kPieceP * p + 8 * lane;
+                if (k0 < Kp)
+                    *reinterpret_cast<uint4 *>(row + 2 * k0) = xv[p];
+            }
+        }
+    }
+    if (tid < 4)
+        reinterpret_cast<uint32_t *>(zero)[tid] = 0u;
+    __syncthreads();  // staged rows, scales, weight scales, zero block
+
+    // 3. stream this wave's tiles: compute a chunk, then reload its buffer
+    //    with the item two ahead
+    const uint8_t *bsrc = r < M ? smem + r * stride : zero;
+    const int estep = r < M ? 1 : 0;
+    const float sx = FP8 && r < M ? st_scale[r] : 1.0f;
+    int t_cp = first, c_cp = 0, ord = 0;  // item being computed, its tile ordinal
+    v4f acc = zero4;
+    auto step = [&](uint4 (&buf)[kLoadsP]) {
+        acc = compute_chunk<FP8>(buf, acc, bsrc, estep, c_cp, g);
+        next_load(buf);
+        // lane (g, r) holds rows 4g .. 4g+3 of the tile for token r
+        const int lim = c_cp == C - 1 ? N : 0;
+        const int n = t_cp * 16 + 4 * g;
+        v4f v = acc;
+        if constexpr (FP8) {
+            const int o = ord < kScaleTiles ? ord : kScaleTiles - 1;
+            const float4 ws =
+                *reinterpret_cast<const float4 *>(st_ws + (wave * kScaleTiles + o) * 16 + 4 * g);
+            v[0] = acc[0] * sx * ws.x;
+            v[1] = acc[1] * sx * ws.y;
+            v[2] = acc[2] * sx * ws.z;
+            v[3] = acc[3] * sx * ws.w;
+        }
+        put(v, n, lim);
+        if (++c_cp == C) {
+            c_cp = 0;
+            t_cp += nwaves;
+            ++ord;
+            acc = zero4;
+        }
+    };
+    for (int it = 0; it < total; it += 2) {
+        step(bA);
+        if (it + 1 >= total)
+            break;
+        step(bB);
+    }
+}
+
+using ProjFn = void (*)(const uint8_t *, const float *, const uint16_t *, int, int, int, int,
+                        float *, int, uint8_t *, float *);
+
+int compute_units() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return 0;
+    if (dev < 64) {
+        const int v = cached[dev].load(std::memory_order_relaxed);
+        if (v > 0)
+            return v;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    if (dev < 64)
+        cached[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
+}  // namespace
+
+int projection_padded_k(bool fp8, int K) {
+    const int chunk = fp8 ? Role<true>::kChunk : Role<false>::kChunk;
+    return (K + chunk - 1) / chunk * chunk;
+}
+
+int projection_lds_bytes(bool fp8, int M, int K) {
+    return stage_bytes(M, projection_padded_k(fp8, K));
+}
+
+hipError_t launch_projection(bool fp8, const uint8_t *w, const float *wscale,
+                             const uint16_t *x, int M, int K, int N, float *y,
+                             uint8_t *xq_out, float *xs_out, hipStream_t stream) {
+    const int Kp = projection_padded_k(fp8, K);
+    const int lds = stage_bytes(M, Kp);
+    const ProjFn fn = fp8 ? &projection_kernel<true> : &projection_kernel<false>;
+    hipError_t e = ensure_lds_limit(reinterpret_cast<const void *>(fn), lds);
+    if (e != hipSuccess)
+        return e;
+    const int cus = compute_units();
+    if (cus <= 0)
+        return hipErrorInvalidDevice;
+    // one launch per span of rows in which every wave has at most
+    // kScaleTiles tiles (the weight scales it keeps in LDS)
+    const int64_t row_bytes = static_cast<int64_t>(K) * (fp8 ? 1 : 2);
+    const int span = kScaleTiles * kProjWaves * cus * 16;
+    for (int n0 = 0; n0 < N; n0 += span) {
+        const int rows = N - n0 < span ? N - n0 : span;
+        const int tiles = (rows + 15) / 16;
+        const int want = (tiles + kProjWaves - 1) / kProjWaves;
+        const int grid = want < cus ? want : cus;
+        hipLaunchKernelGGL(fn, dim3(grid), dim3(kThreadsP), lds, stream, w + n0 * row_bytes,
+                           wscale ? wscale + n0 : nullptr, x, M, K, rows, Kp, y + n0, N,
+                           n0 == 0 ? xq_out : nullptr, n0 == 0 ? xs_out : nullptr);
+        e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace twd

@@ -195,6 +195,70 @@ extern "C" int twd_select_kernel(int64_t M, int64_t K, int64_t N, int bf16_input
         .kernel;
 }
 
+namespace {
+
+// Shared checks of the two projection roles.
+twd_status check_projection(bool fp8, const void *w, const float *wscale, const void *x,
+                            int64_t M, int64_t K, int64_t N, const float *y,
+                            const uint8_t *xq, const float *xscale) {
+    const char *name = fp8 ? "projection_fp8" : "projection_bf16";
+    if (M < 0 || M > TWD_MAX_M)
+        return set_error(TWD_ERR_UNSUPPORTED, "%s: M=%lld outside 0..%d", name,
+                         (long long)M, TWD_MAX_M);
+    if (N < 0 || N > (int64_t(1) << 24))
+        return set_error(N < 0 ? TWD_ERR_INVALID_ARG : TWD_ERR_UNSUPPORTED,
+                         "%s: N=%lld outside 0..2^24", name, (long long)N);
+    const int kq = fp8 ? 16 : 8;
+    if (K < kq || K > TWD_MAX_K_PROJECTION || K % kq != 0)
+        return set_error(TWD_ERR_UNSUPPORTED, "%s: K=%lld must be a multiple of %d in %d..%d",
+                         name, (long long)K, kq, kq, TWD_MAX_K_PROJECTION);
+    if (projection_lds_bytes(fp8, static_cast<int>(M), static_cast<int>(K)) > 160 * 1024)
+        return set_error(TWD_ERR_UNSUPPORTED,
+                         "%s: M=%lld tokens of K=%lld do not fit the 160 KiB of LDS", name,
+                         (long long)M, (long long)K);
+    if (M == 0 || N == 0)
+        return TWD_OK;
+    if (!w || !x || !y || (fp8 && !wscale))
+        return set_error(TWD_ERR_INVALID_ARG, "%s: null pointer", name);
+    if (!aligned(w, 16) || !aligned(x, 16) || (fp8 && !aligned(wscale, 16)))
+        return set_error(TWD_ERR_INVALID_ARG,
+                         "%s: weights, activations and weight scales must be 16-byte aligned",
+                         name);
+    if (!aligned(y, 4) || (xq && !aligned(xq, 8)) || (xscale && !aligned(xscale, 4)))
+        return set_error(TWD_ERR_INVALID_ARG,
+                         "%s: y and xscale must be 4-byte aligned, xq 8-byte aligned", name);
+    return TWD_OK;
+}
+
+}  // namespace
+
+extern "C" twd_status twd_projection_fp8(const uint8_t *wq, const float *wscale,
+                                         const uint16_t *x_bf16, int64_t M, int64_t K,
+                                         int64_t N, float *y, uint8_t *xq, float *xscale,
+                                         void *stream) {
+    twd_status st = check_projection(true, wq, wscale, x_bf16, M, K, N, y, xq, xscale);
+    if (st != TWD_OK || M == 0 || N == 0)
+        return st;
+    return hip_status(launch_projection(true, wq, wscale, x_bf16, static_cast<int>(M),
+                                        static_cast<int>(K), static_cast<int>(N), y, xq,
+                                        xscale, as_stream(stream)),
+                      "projection_fp8 launch");
+}
+
+extern "C" twd_status twd_projection_bf16(const uint16_t *w_bf16, const uint16_t *x_bf16,
+                                          int64_t M, int64_t K, int64_t N, float *y,
+                                          void *stream) {
+    twd_status st = check_projection(false, w_bf16, nullptr, x_bf16, M, K, N, y, nullptr,
+                                     nullptr);
+    if (st != TWD_OK || M == 0 || N == 0)
+        return st;
+    return hip_status(launch_projection(false, reinterpret_cast<const uint8_t *>(w_bf16),
+                                        nullptr, x_bf16, static_cast<int>(M),
+                                        static_cast<int>(K), static_cast<int>(N), y, nullptr,
+                                        nullptr, as_stream(stream)),
+                      "projection_bf16 launch");
+}
+
 extern "C" twd_status twd_stream_read(const void *buf, int64_t bytes,
                                       uint32_t *sink, void *stream) {
     if (bytes < 0 || bytes % 16 != 0)

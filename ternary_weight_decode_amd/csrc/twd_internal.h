@@ -71,6 +71,18 @@ hipError_t launch_staged(int tiles, const uint8_t *w, const void *act, bool fuse
                        const Segments &segs, int32_t *acc, float *y,
                        hipStream_t stream);
 
+// Role-dependent output projections (projection.hip): fp8 selects the fast
+// role (E4M3 weight codes with per-row scales, activations quantized to
+// E4M3 per token inside), else the critical role (bf16 weights).  K is
+// padded to the kernel's chunk; the staged activations take
+// projection_lds_bytes of LDS.  xq_out / xs_out (fast role, nullable)
+// receive the activation codes and scales.
+int projection_padded_k(bool fp8, int K);
+int projection_lds_bytes(bool fp8, int M, int K);
+hipError_t launch_projection(bool fp8, const uint8_t *w, const float *wscale,
+                             const uint16_t *x, int M, int K, int N, float *y,
+                             uint8_t *xq_out, float *xs_out, hipStream_t stream);
+
 hipError_t launch_stream_read(const void *buf, int64_t bytes, uint32_t *sink,
                               hipStream_t stream);
 hipError_t launch_stream_copy(const void *src, void *dst, int64_t bytes,

@@ -206,3 +206,51 @@ def test_measurement_helpers_reject_before_launch(twd):
     assert c(0x1000, None, 16, None) == 1
     assert c(0x1000, 0x2008, 16, None) == 1
     assert c(0x1000, 0x2000, 0, None) == 0
+
+
+# ------------------------------------------------ role-dependent projections
+
+@pytest.mark.parametrize("shape,sigma", [((7, 48), 0.02), ((33, 320), 1.0), ((4, 4096), 3.0)])
+def test_quantize_fp8_rows_bit_exact_vs_oracle(twd, orc, shape, sigma):
+    rng = np.random.default_rng(sum(shape))
+    W = rng.standard_normal(shape).astype(np.float32) * np.float32(sigma)
+    W[0] = 0.0                      # zero row
+    W[1, 3] = 57.0                  # an outlier sets the row scale
+    W[2, :] = np.float32(2.0 ** -20)  # one large value; the rest scale below
+    W[2, 1] = np.float32(1.0)         # the smallest E4M3 subnormal -> zero codes
+    W[3, :5] = np.float32(2.0 ** -9) * np.arange(1, 6, dtype=np.float32)  # subnormals
+    codes, scale = twd.quantize_fp8_rows(W)
+    rc, rs = orc.quantize_fp8_rows(W)
+    np.testing.assert_array_equal(codes, rc)
+    np.testing.assert_array_equal(scale.view(np.uint32), rs.view(np.uint32))
+
+
+def test_quantize_fp8_rows_hand_and_errors(twd):
+    g = read_golden("fp8_e4m3_hand.txt")
+    W = np.array([[float(v) for v in g["W"]]], dtype=np.float32)
+    codes, scale = twd.quantize_fp8_rows(W)
+    assert [int(c) for c in codes[0]] == [int(c, 16) for c in g["WQ"]] and scale[0] == 1.0
+    with pytest.raises(twd.TwdError):
+        twd.quantize_fp8_rows(np.array([[1.0, np.inf]], np.float32))
+
+
+def test_projection_rejects_before_launch(twd):
+    f8, f16 = twd._lib_proj_fp8, twd._lib_proj_bf16
+    ok = (0x1000, 0x2000, 0x3000)
+    assert f8(*ok, 17, 256, 64, 0x4000, None, None, None) == 2     # M > 16
+    assert f8(*ok, 1, 8, 64, 0x4000, None, None, None) == 2        # K % 16
+    assert f8(*ok, 1, 4112, 64, 0x4000, None, None, None) == 2     # K > 4096
+    assert f8(*ok, 1, 256, (1 << 24) + 1, 0x4000, None, None, None) == 2
+    assert f8(*ok, 1, 256, -1, 0x4000, None, None, None) == 1
+    assert f8(0x1000, None, 0x3000, 1, 256, 64, 0x4000, None, None, None) == 1
+    assert f8(0x1008, 0x2000, 0x3000, 1, 256, 64, 0x4000, None, None, None) == 1
+    assert f8(*ok, 1, 256, 64, 0x4002, None, None, None) == 1      # y alignment
+    assert f8(*ok, 1, 256, 64, 0x4000, 0x5004, None, None) == 1    # xq alignment
+    assert f8(*ok, 0, 256, 64, None, None, None, None) == 0        # empty
+    assert f8(*ok, 3, 256, 0, None, None, None, None) == 0
+    assert f16(0x1000, 0x3000, 1, 12, 64, 0x4000, None) == 2       # K % 8
+    assert f16(0x1000, 0x3000, 1, 4104, 64, 0x4000, None) == 2
+    assert f16(None, 0x3000, 1, 256, 64, 0x4000, None) == 1
+    assert f16(0x1000, 0x3008, 1, 256, 64, 0x4000, None) == 1
+    assert f16(0x1000, 0x3000, 0, 256, 64, None, None) == 0
+    assert twd._lib_last_error()

@@ -28,6 +28,12 @@ Recipe (all draws are numpy ``default_rng`` standard normals in fp32):
     scaled by 20 in every row, so per-token absmax scales vary widely.
   * Activations are rounded from fp32 to bf16 with round-to-nearest-even and
     handed over as uint16 bit patterns.
+  * Output (vocabulary) projection of the 2B-class set, for the fast and
+    critical projection roles: hidden 2560 -> 128256 rows (the size of the
+    2B backbone's vocabulary; the pages do not state it).  Rows come in
+    blocks of 4096, block b drawn N(0, 0.02^2) from ``default_rng([6, b])``,
+    so any row can be regenerated on its own; activations for width M are
+    N(0, 1) rows from ``default_rng([1006, M])``.
 """
 from __future__ import annotations
 
@@ -153,6 +159,32 @@ def random_case(seed: int, M: int, K: int, seg_rows, w_sigma: float = 1.0,
     rng = np.random.default_rng([78, seed, M, K])
     x = rng.standard_normal((M, K), dtype=np.float32) * np.float32(x_sigma)
     return W, tuple(seg_rows), f32_to_bf16_bits(x)
+
+
+HEAD_K = 2560
+HEAD_N = 128256
+HEAD_BLOCK = 4096
+
+
+def head_weight_block(b: int, K: int = HEAD_K, N: int = HEAD_N, sigma: float = 0.02):
+    """fp32 rows [4096 b, min(4096 (b + 1), N)) of the output projection."""
+    rows = min(HEAD_BLOCK, N - HEAD_BLOCK * b)
+    rng = np.random.default_rng([6, b])
+    w = rng.standard_normal((rows, K), dtype=np.float32)
+    w *= np.float32(sigma)
+    return w
+
+
+def head_weights(K: int = HEAD_K, N: int = HEAD_N):
+    """The whole output projection, fp32 [N, K]."""
+    nb = -(-N // HEAD_BLOCK)
+    return np.concatenate([head_weight_block(b, K, N) for b in range(nb)], axis=0)
+
+
+def head_activations(M: int, K: int = HEAD_K):
+    """bf16 bits [M, K] of N(0, 1) rows for the output projection."""
+    rng = np.random.default_rng([1006, M])
+    return f32_to_bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
 
 
 def workload_widths(workload: str):
