@@ -12,9 +12,9 @@
 //
 // Both are pure weight streams (1 or 2 bytes per weight, read once for all
 // M <= 16 tokens), so the kernel is built around HBM: a persistent grid of
-// one 16-wave workgroup per compute unit, each wave streaming whole 16-row
-// tiles t = wave id, + total waves, ..., double-buffered in chunks of eight
-// 16-byte loads per lane.
+// one 16-wave workgroup per compute unit, each wave streaming a contiguous
+// range of whole 16-row tiles, double-buffered in chunks of eight 16-byte
+// loads per lane.
 //
 // Arithmetic.  Every E4M3 value is exactly a bf16 value, so both roles run
 // on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16, fp32 accumulation):
@@ -28,11 +28,12 @@
 // Layout.  In load j of chunk c, lane l (row r = l % 16, K group g = l / 16)
 // reads the 16 bytes at byte (8 c + j) 64 + 16 g of weight row r of its
 // tile: one load covers 64 contiguous bytes of each of 16 rows.  As an MFMA
-// A operand the lane's bf16 values are elements e0 .. e0 + 7 (+ 8 .. 15 for
-// FP8 codes, a second MFMA) of row r; the B operand of token column r reads
-// the same elements of staged token row r, so the contraction covers every
-// k exactly once.  Loads past the row end or past N fall outside the buffer
-// descriptor and return zeros; token columns past M read a zero block.
+// B operand the lane's bf16 values are elements e0 .. e0 + 7 (+ 8 .. 15 for
+// FP8 codes, a second MFMA) of weight column r; the A operand of token row
+// r reads the same elements of staged token row r, so the contraction
+// covers every k exactly once, and lane (g, r) ends with tokens 4g .. 4g+3
+// of weight row r.  Loads past the row end or past N fall outside the
+// buffer descriptor and return zeros; token rows past M read a zero block.
 #include "kernel_common.h"
 
 namespace twd {
@@ -86,11 +87,12 @@ __device__ __forceinline__ v8bf as_bf16x8(uint32_t a, uint32_t b, uint32_t c, ui
 
 template <bool FP8>
 __device__ __forceinline__ void load_chunk(uint4 (&buf)[kLoadsP], const uint8_t *W, int tile,
-                                           int tiles, int N, int row_bytes, int c, int r, int g) {
+                                           int tile_end, int N, int row_bytes, int c, int r, int g) {
+    // tiles at or past tile_end (this wave's range) load nothing
     const int n0 = tile * 16;
-    const int rows = tile < tiles ? min(16, N - n0) : 0;
+    const int rows = tile < tile_end ? min(16, N - n0) : 0;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t *>(W + static_cast<int64_t>(tile < tiles ? n0 : 0) * row_bytes), 0,
+        const_cast<uint8_t *>(W + static_cast<int64_t>(tile < tile_end ? n0 : 0) * row_bytes), 0,
         __builtin_amdgcn_readfirstlane(rows * row_bytes), kRawBufferFlags);
 #pragma unroll
     for (int j = 0; j < kLoadsP; ++j) {
@@ -115,13 +117,13 @@ __device__ __forceinline__ v4f compute_chunk(const uint4 (&buf)[kLoadsP], v4f ac
                                       fp8x2_bf16<false>(w.w), fp8x2_bf16<true>(w.w));
             const v8bf b0 = *reinterpret_cast<const v8bf *>(bsrc + 2 * e0 * estep);
             const v8bf b1 = *reinterpret_cast<const v8bf *>(bsrc + 2 * (e0 + 8) * estep);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b0, a0, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b1, a1, acc, 0, 0, 0);
         } else {
             const int e0 = (c * kLoadsP + j) * 32 + 8 * g;
             const v8bf a = __builtin_bit_cast(v8bf, w);
             const v8bf b = *reinterpret_cast<const v8bf *>(bsrc + 2 * e0 * estep);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, a, acc, 0, 0, 0);
         }
     }
     return acc;
@@ -147,18 +149,24 @@ __global__ __launch_bounds__(kThreadsP) void projection_kernel(
     const int tiles = (N + 15) / 16;
     const int nwaves = gridDim.x * kProjWaves;
     const int C = Kp / R::kChunk;  // chunks per tile
-    const int first = blockIdx.x * kProjWaves + wave;
-    const int ntiles = first < tiles ? (tiles - 1 - first) / nwaves + 1 : 0;
+    // each wave owns a contiguous, even-sized range of tiles: it writes the
+    // outputs of two neighbouring tiles together, so that every 128-byte
+    // line of y leaves the L2 whole (a half-written line would be evicted
+    // by the weight stream before its other half arrived)
+    const int tpw = 2 * ((tiles + 2 * nwaves - 1) / (2 * nwaves));
+    const int first = (blockIdx.x * kProjWaves + wave) * tpw;
+    const int ntiles = max(0, min(tpw, tiles - first));
+    const int tile_end = first + ntiles;
     const int total = ntiles * C;
 
     // 1. Loads, oldest first, so that waiting for the activations never
     //    waits for weights: (fast role) one weight scale per thread -- row
-    //    16 (first tile of wave tid / 64, + (tid / 16) % 4 strides) + tid % 16
-    //    -- then this wave's token row, then the first two weight chunks.
+    //    16 (first tile of wave tid / 64, + (tid / 16) % 4) + tid % 16 --
+    //    then this wave's token row, then the first two weight chunks.
     float wsv = 0.0f;
     if constexpr (FP8) {
         const int w = tid >> 6;
-        const int n = (blockIdx.x * kProjWaves + w + ((tid >> 4) & 3) * nwaves) * 16 + (tid & 15);
+        const int n = ((blockIdx.x * kProjWaves + w) * tpw + ((tid >> 4) & 3)) * 16 + (tid & 15);
         const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<float *>(wscale), 0, N * 4, kRawBufferFlags);
         wsv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
@@ -189,27 +197,34 @@ __global__ __launch_bounds__(kThreadsP) void projection_kernel(
     uint4 bA[kLoadsP], bB[kLoadsP];
     int t_ld = first, c_ld = 0;  // next item to load
     auto next_load = [&](uint4 (&buf)[kLoadsP]) {
-        load_chunk<FP8>(buf, W, t_ld, tiles, N, row_bytes, c_ld, r, g);
+        load_chunk<FP8>(buf, W, t_ld, tile_end, N, row_bytes, c_ld, r, g);
         if (++c_ld == C) {
             c_ld = 0;
-            t_ld += nwaves;
+            ++t_ld;
         }
     };
     // (the tile-finished condition enters as a row limit, so the stores
     // stay unconditional per-lane selects rather than a branch)
-    auto put = [&](v4f v, int n, int lim) {
+    // stores of tile pair (held, cur) at rows n and n + 16; each limit is N
+    // when that tile is to be written now, else 0
+    auto put = [&](v4f held, v4f cur, int n, int lim_h, int lim_c) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const bool ok = r < M && n + i < lim;
-            const uint32_t off = ok ? static_cast<uint32_t>(4 * (r * ldy + n + i)) : kOutOfRange;
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[i]), yr, off, 0, 0);
+            const int m = 4 * g + i;
+            // (unsigned compares: n is negative for an unpaired first tile)
+            const bool okh = m < M && static_cast<unsigned>(n) < static_cast<unsigned>(lim_h);
+            const bool okc = m < M && static_cast<unsigned>(n + 16) < static_cast<unsigned>(lim_c);
+            const uint32_t oh = okh ? static_cast<uint32_t>(4 * (m * ldy + n)) : kOutOfRange;
+            const uint32_t oc = okc ? static_cast<uint32_t>(4 * (m * ldy + n + 16)) : kOutOfRange;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(held[i]), yr, oh, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(cur[i]), yr, oc, 0, 0);
         }
     };
     const v4f zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
     next_load(bA);
-    put(zero4, 0, 0);
+    put(zero4, zero4, 0, 0, 0);
     next_load(bB);
-    put(zero4, 0, 0);
+    put(zero4, zero4, 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
 
     // 2. stage the activations as bf16 (wave m owns token row m)
@@ -279,29 +294,39 @@ __global__ __launch_bounds__(kThreadsP) void projection_kernel(
     //    with the item two ahead
     const uint8_t *bsrc = r < M ? smem + r * stride : zero;
     const int estep = r < M ? 1 : 0;
-    const float sx = FP8 && r < M ? st_scale[r] : 1.0f;
+    // the tokens are the MFMA's A rows and the weight rows its B columns:
+    // lane (g, r) accumulates tokens 4g .. 4g+3 against weight row r, so
+    // each of its four stores is one of 16 contiguous floats of a y row
+    float sx[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        sx[i] = FP8 && 4 * g + i < M ? st_scale[4 * g + i] : 1.0f;
     int t_cp = first, c_cp = 0, ord = 0;  // item being computed, its tile ordinal
-    v4f acc = zero4;
+    v4f acc = zero4, held = zero4;
     auto step = [&](uint4 (&buf)[kLoadsP]) {
         acc = compute_chunk<FP8>(buf, acc, bsrc, estep, c_cp, g);
         next_load(buf);
-        // lane (g, r) holds rows 4g .. 4g+3 of the tile for token r
-        const int lim = c_cp == C - 1 ? N : 0;
-        const int n = t_cp * 16 + 4 * g;
         v4f v = acc;
         if constexpr (FP8) {
             const int o = ord < kScaleTiles ? ord : kScaleTiles - 1;
-            const float4 ws =
-                *reinterpret_cast<const float4 *>(st_ws + (wave * kScaleTiles + o) * 16 + 4 * g);
-            v[0] = acc[0] * sx * ws.x;
-            v[1] = acc[1] * sx * ws.y;
-            v[2] = acc[2] * sx * ws.z;
-            v[3] = acc[3] * sx * ws.w;
+            const float ws = st_ws[(wave * kScaleTiles + o) * 16 + r];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                v[i] = acc[i] * sx[i] * ws;
         }
-        put(v, n, lim);
+        // a finished tile with an odd ordinal completes a pair: write both;
+        // an even one waits in `held`, unless it is the wave's last
+        const bool fin = c_cp == C - 1;
+        const bool odd = (ord & 1) != 0;
+        const int lim_h = fin && odd ? N : 0;
+        const int lim_c = fin && (odd || ord == ntiles - 1) ? N : 0;
+        const int n = (t_cp - (odd ? 1 : 0)) * 16 + r;
+        put(held, v, n - (odd ? 0 : 16), lim_h, lim_c);
+        if (fin && !odd)
+            held = v;
         if (++c_cp == C) {
             c_cp = 0;
-            t_cp += nwaves;
+            ++t_cp;
             ++ord;
             acc = zero4;
         }
