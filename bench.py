@@ -163,6 +163,54 @@ def stream_read_reference(twd, torch, dev_set, reps):
     return dev_set.bytes_per_sweep * reps / sec / 1e9, sec / (reps * len(keys))
 
 
+def output_projection_bench(twd, torch, widths, reps):
+    """The role-dependent output projection (hidden 2560 -> 128256 rows) in
+    both roles: fast (E4M3 weight codes, activations quantized inside) and
+    critical (bf16).  Each graph cycles through two distinct weight copies
+    (656 MB / 1.3 GB, beyond the 256 MB Infinity Cache), so every launch
+    reads cold weights; the weights are random on-device values (random
+    finite E4M3 codes, N(0, 0.02) bf16), since the kernels' timing does not
+    depend on them.  The streaming read over the same buffers is the
+    achievable-bandwidth reference."""
+    K, N = wl.HEAD_K, wl.HEAD_N
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    copies = 2
+    w8 = []
+    for _ in range(copies):
+        b = torch.randint(0, 256, (N, K), dtype=torch.uint8, device="cuda", generator=gen)
+        b[(b & 0x7F) == 0x7F] = 0x38  # no NaN codes
+        w8.append(b)
+    ws = torch.rand(N, device="cuda", generator=gen) * 1e-3
+    w16 = [(torch.randn((N, K), device="cuda", generator=gen) * 0.02).to(torch.bfloat16)
+           for _ in range(copies)]
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+
+    def timed(fn, nbytes):
+        g = capture(torch, lambda: [fn(c) for c in range(copies)])
+        g.replay()
+        _, sec = time_replays(torch, g, reps)
+        us = sec / (reps * copies) * 1e6
+        return {"us": round(us, 2), "gbs": round(nbytes / us / 1e3, 1),
+                "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+
+    out = {"shape": f"K={K} -> N={N} (2B-class output projection)",
+           "weights": "random finite E4M3 codes / N(0,0.02) bf16 on device; two copies per graph",
+           "fast_fp8": {}, "critical_bf16": {}}
+    for M in widths:
+        x = torch.randn((M, K), device="cuda", generator=gen).to(torch.bfloat16)
+        y = torch.empty((M, N), device="cuda")
+        out["fast_fp8"][str(M)] = timed(lambda c: twd.projection_fp8(w8[c], ws, x, y=y), N * K)
+        out["critical_bf16"][str(M)] = timed(lambda c: twd.projection_bf16(w16[c], x, y=y),
+                                             2 * N * K)
+    out["stream_read_fp8_bytes"] = timed(lambda c: twd.stream_read(w8[c], N * K, sink), N * K)
+    out["stream_read_bf16_bytes"] = timed(lambda c: twd.stream_read(w16[c], 2 * N * K, sink),
+                                          2 * N * K)
+    del w8, w16
+    torch.cuda.empty_cache()
+    return out
+
+
 def kernel_map(twd, ls, M, kernel, bf16_input=True):
     """Kernel family each projection of the set runs at width M, for bf16
     activations (one launch) or int8 ones (the linear of the two-launch
@@ -474,6 +522,80 @@ def summarize_profiles(args):
     print(cnt_path)
 
 
+def summarize_projection(args):
+    """Kernel trace and HBM counters of the output projection (both roles)
+    from three rocprofv3 runs of this script with --projection-widths 1
+    (trace, FETCH_SIZE, WRITE_SIZE; the counter runs add --copy-calibration)."""
+    trace_dir, fetch_dir, write_dir = args.summarize_projection
+    cmds = args.profile_commands or ("?", "?", "?")
+    K, N = wl.HEAD_K, wl.HEAD_N
+    roles = (("projection_kernel<true>", "fast (E4M3 weights)", N * K),
+             ("projection_kernel<false>", "critical (bf16 weights)", 2 * N * K))
+    trace = _csv_rows(trace_dir, "kernel_trace.csv")
+    lines = ["# output projection 2560 -> 128256, M=1: rocprofv3 kernel trace and HBM counters",
+             "", "Commands (from the repository root):", "", "    " + cmds[0], "",
+             "    " + cmds[1], "", "    " + cmds[2], "",
+             "bench.py times each role over two distinct weight copies per graph replay "
+             "(every launch reads cold weights); the trace covers all of that run's "
+             "dispatches of the kernel, eager warm-up included.", "",
+             "| role | kernel | dispatches | average us | min us | algorithmic bytes | GB/s (avg) |"
+             " % of 8 TB/s |", "|---|---|---|---|---|---|---|---|"]
+    avg = {}
+    for kname, role, nbytes in roles:
+        d = [int(_col(r, "End_Timestamp")) - int(_col(r, "Start_Timestamp"))
+             for r in trace if _short(_col(r, "Kernel_Name")) == kname]
+        a = sum(d) / len(d)
+        avg[kname] = a
+        lines.append(f"| {role} | `{kname}` | {len(d)} | {a / 1e3:.2f} | {min(d) / 1e3:.2f} | "
+                     f"{nbytes:,} | {nbytes / a:.1f} | {100 * nbytes / a / HBM_PEAK_GBS:.1f} |")
+    # the streaming reads over the projection's weight copies (the largest
+    # grids of that kernel in the run; the layer sweep's are far smaller)
+    def grid(r):
+        return int(_col(r, "Grid_Size", "Grid_Size_X", "grid_size"))
+
+    sr = [r for r in trace if _short(_col(r, "Kernel_Name")) == "stream_read_kernel"]
+    big = max((grid(r) for r in sr), default=0)
+    reads = {}
+    for r in sr:
+        if grid(r) * 4 >= big:  # fp8-size and bf16-size reads
+            reads.setdefault(grid(r), []).append(
+                int(_col(r, "End_Timestamp")) - int(_col(r, "Start_Timestamp")))
+
+    def per_kernel(d, counter):
+        agg = {}
+        for r in _csv_rows(d, "counter_collection.csv"):
+            if _col(r, "Counter_Name") == counter:
+                agg.setdefault(_short(_col(r, "Kernel_Name")), []).append(
+                    float(_col(r, "Counter_Value")))
+        return {k: sum(v) / len(v) for k, v in agg.items()}
+
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    copy_bytes = 256 << 20
+    ff = copy_bytes / (fetch["stream_copy_kernel"] * 1024.0)
+    fw = copy_bytes / (write["stream_copy_kernel"] * 1024.0)
+    lines += ["", f"Counter calibration: the plain copy of {copy_bytes} bytes reads "
+              f"FETCH_SIZE {fetch['stream_copy_kernel']:.1f} KiB (factor {ff:.4f}) and "
+              f"WRITE_SIZE {write['stream_copy_kernel']:.1f} KiB (factor {fw:.4f}).", "",
+              "| role | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes read (calibrated) | "
+              "over algorithmic | HBM bytes written |", "|---|---|---|---|---|---|"]
+    for kname, role, nbytes in roles:
+        rd = fetch[kname] * 1024 * ff
+        wr = write[kname] * 1024 * fw
+        lines.append(f"| {role} | {fetch[kname]:.1f} | {write[kname]:.1f} | {rd:,.0f} | "
+                     f"{rd / nbytes:.3f}x | {wr:,.0f} |")
+    for g, d in sorted(reads.items()):
+        nbytes = g * 16 * 4  # 256 threads x 4 loads x 16 bytes per workgroup
+        a = sum(d) / len(d)
+        lines += ["", f"Streaming-read reference over {nbytes:,} bytes in the same run: "
+                  f"average {a / 1e3:.2f} us over {len(d)} dispatches ({nbytes / a:.1f} GB/s)."]
+    lines.append("")
+    path = os.path.join(args.profile_out, "output_projection_2b_m1_trace_and_counters.md")
+    os.makedirs(args.profile_out, exist_ok=True)
+    with open(path, "w") as f:
+        f.write("\n".join(lines))
+    print(path)
+
+
 SIMDS = 1024  # MI355X: 256 compute units x 4 SIMDs
 
 
@@ -541,12 +663,17 @@ def main():
                     help="1: check every graph replay against the eager results (default)")
     ap.add_argument("--per-proj", type=int, default=1,
                     help="1: time each projection shape on its own, cold (default)")
+    ap.add_argument("--projection-widths", default="1,4,8,16",
+                    help="widths of the fast / critical output-projection table ('' skips it)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with plain copies of 256 MiB (byte-counter calibration)")
     ap.add_argument("--summarize-profile", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="no GPU: summarize rocprofv3 CSV output of this script into profiles/")
     ap.add_argument("--profile-commands", nargs=3, metavar=("TRACE_CMD", "FETCH_CMD", "WRITE_CMD"),
                     help="the commands that produced --summarize-profile's inputs")
+    ap.add_argument("--summarize-projection", nargs=3,
+                    metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="summarize rocprofv3 runs of the output-projection table")
     ap.add_argument("--summarize-util", nargs=2, metavar=("PMC_DIR", "COMMAND"),
                     help="no GPU: summarize a rocprofv3 --pmc run of the utilization counters")
     ap.add_argument("--profile-out", default=PROFILES)
@@ -561,6 +688,9 @@ def main():
         return
     if args.summarize_util:
         summarize_util(args)
+        return
+    if args.summarize_projection:
+        summarize_projection(args)
         return
 
     if args.gpus != 1:
@@ -650,6 +780,10 @@ def main():
             torch.cuda.empty_cache()
 
     proj_table = per_projection(twd, torch, ls, M, kernel, reps) if args.per_proj else None
+    head = None
+    if args.projection_widths:
+        head = output_projection_bench(
+            twd, torch, [int(v) for v in args.projection_widths.split(",") if v], reps)
     calib = copy_calibration(twd, torch) if args.copy_calibration else None
 
     cpu = cpu1 = None
@@ -695,6 +829,7 @@ def main():
         "two_launch_step_gbs": round(bytes_step * reps / two_wall / 1e9, 1),
         "widths": widths,
         "per_projection_cold": proj_table,
+        "output_projection": head,
         "cpu_baseline": cpu,
         "cpu_single_thread": cpu1,
     }
