@@ -392,3 +392,90 @@ def test_bf16_linear_against_fractions(orc):
     d, _ = orc.bf16_linear(x, w1)
     np.testing.assert_array_equal(d[:, 0], xf[:, 5].astype(np.float64))
     assert not d[:, 1].any()
+
+
+# ------------------------------------------- accepted-prefix KV commit
+
+def _kv():
+    from oracle import kv_commit
+    return kv_commit
+
+
+def test_kv_segment_geometry_closed_form():
+    kv = _kv()
+    for c0 in (1, 2, 16, 128):
+        nseg = 9
+        for s in range(nseg):
+            start = c0 * (2 ** s - 1)           # after c0 (1 + 2 + ... + 2^(s-1))
+            end = c0 * (2 ** (s + 1) - 1)
+            assert kv.locate(start, c0, nseg) == (s, 0)
+            assert kv.locate(end - 1, c0, nseg) == (s, c0 * 2 ** s - 1)
+        assert kv.locate(c0 * (2 ** nseg - 1), c0, nseg) is None
+        # a history of H positions needs ceil(log2(H / c0 + 1)) segments
+        for H in range(1, c0 * 200, max(1, c0 // 3)):
+            last = kv.locate(H - 1, c0, 12)[0]
+            assert last + 1 == math.ceil(math.log2(H / c0 + 1) - 1e-12)
+
+
+def test_kv_commit_hand_sequence():
+    kv = _kv()
+    st = kv.KVStore(c0=2, nseg=3, layers=1, row=2)
+    commits = read_golden_rows("kv_commit_hand.txt", "COMMIT")
+    states = read_golden_rows("kv_commit_hand.txt", "STATE")
+    assert len(commits) == len(states) == 6
+    for (c, W, n_mat, n_new), state in zip(commits, states):
+        c, W = int(c), int(W)
+        block = np.zeros((1, 2, W, 2), np.uint16)
+        for j in range(W):
+            for k in range(2):
+                block[0, k, j] = [100 * c + 10 * j + k, 100 * c + 10 * j + k + 500]
+        st.commit(block, int(n_mat), int(n_new))
+        assert st.state == [int(v) for v in state]
+    want = [np.zeros((1, 2, cap, 2), np.uint16) for cap in (2, 4, 8)]
+    for s, o, k0, k1, v0, v1 in read_golden_rows("kv_commit_hand.txt", "SEG"):
+        want[int(s)][0, 0, int(o)] = [int(k0), int(k1)]
+        want[int(s)][0, 1, int(o)] = [int(v0), int(v1)]
+    for got, w in zip(st.segs, want):
+        np.testing.assert_array_equal(got, w)
+
+
+def test_kv_commit_invariants_and_errors():
+    kv = _kv()
+    rng = np.random.default_rng(21)
+    st = kv.KVStore(c0=4, nseg=5, layers=2, row=3)
+    dense = []  # the materialized rows, kept independently in order
+    for it in range(40):
+        P, L, S, _ = st.state
+        W = int(rng.integers(1, 7))
+        block = rng.integers(0, 65535, (2, 2, W, 3)).astype(np.uint16)
+        mode = rng.integers(0, 3)
+        if mode == 0 and S <= W:            # verify: S pending + drafts
+            a = int(rng.integers(0, W - S + 1))
+            n_mat, n_new = S + a, a + 1
+        elif mode == 1:                     # confidence-only
+            n_mat, n_new = 0, int(rng.integers(1, 3))
+        else:                               # autoregressive-like
+            n_mat, n_new = min(1, S, W), 1
+        if L + n_mat > st.capacity:
+            break
+        st.commit(block, n_mat, n_new)
+        assert st.state[3] == 0
+        P2, L2, S2, _ = st.state
+        assert P2 == L2 + S2 and L2 == L + n_mat and P2 == P + n_new and S2 >= 0
+        dense.extend(block[:, :, j, :] for j in range(n_mat))
+        hist = st.history()
+        np.testing.assert_array_equal(hist, np.stack(dense, axis=2) if dense else hist)
+    assert len(dense) > 20
+    # error paths leave every segment untouched
+    before = [s.copy() for s in st.segs]
+    bad = kv.KVStore(c0=4, nseg=5, layers=2, row=3, state=(5, 2, 2, 0))
+    bad.commit(np.ones((2, 2, 2, 3), np.uint16), 1, 1)
+    assert bad.state == [5, 2, 2, kv.ERR_IDENTITY] and not any(s.any() for s in bad.segs)
+    full = kv.KVStore(c0=2, nseg=3, layers=1, row=2, state=(14, 13, 1, 0))
+    full.commit(np.ones((1, 2, 2, 2), np.uint16), 2, 1)
+    assert full.state == [14, 13, 1, kv.ERR_CAPACITY]
+    st2 = kv.KVStore(c0=2, nseg=3, layers=1, row=2)
+    st2.commit(np.ones((1, 2, 2, 2), np.uint16), 3, 1)    # n_mat > W
+    assert st2.state[3] == kv.ERR_COUNTS
+    for a, b in zip(before, st.segs):
+        np.testing.assert_array_equal(a, b)
