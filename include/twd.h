@@ -48,6 +48,8 @@ typedef enum {
 #define TWD_MAX_K 8192        /* input width (activation rows are staged in LDS) */
 #define TWD_MAX_SEGMENTS 4    /* independently scaled row segments (fused) */
 #define TWD_MAX_K_PROJECTION 4096 /* input width of the fast / critical projections */
+#define TWD_KV_MAX_SEGMENTS 24    /* KV segments of the accepted-prefix commit */
+#define TWD_KV_MAX_WIDTH 64       /* block rows one KV commit can take */
 
 /* Kernel families of the linear; TWD_KERNEL_AUTO lets the width dispatch
  * choose (M1's "select by replay width and input/output dimensions"). */
@@ -222,6 +224,48 @@ twd_status twd_projection_fp8(const uint8_t *wq, const float *wscale,
 twd_status twd_projection_bf16(const uint16_t *w_bf16, const uint16_t *x_bf16,
                                int64_t M, int64_t K, int64_t N, float *y,
                                void *stream);
+
+/* ------------------------------------------------------------------------
+ * Accepted-prefix KV commit over shared, geometrically sized segments
+ * ("Methodology in Plain English", paragraph 3: a state triple -- committed
+ * prefix, materialized causal KV length, pending suffix -- kept consistent by
+ * a length identity, and one physical KV buffer per segment, viewed by every
+ * captured graph, with capacities growing geometrically; "Key
+ * Contributions", item 1).  The pages write out neither the identity nor the
+ * layout; the readings here:
+ *
+ * State: device int32[4] = {P committed tokens, L of them with stored causal
+ * KV rows, S = P - L pending, error}.  Identity P == L + S, L >= 0, S >= 0.
+ * Segments: segment s (0 <= s < nseg) holds C0 * 2^s positions, following
+ * segments 0..s-1; its buffer is [layers][2 (K, V)][C0 * 2^s][row_bytes].
+ * Block: the rows a pass computed for W consecutive positions starting at L,
+ * [layers][2][W][row_bytes].
+ * Commit: with n_mat and n_new read from device memory, rows 0 .. n_mat-1 of
+ * the block are stored at positions L .. L+n_mat-1, and state_out = {P +
+ * n_new, L + n_mat, P + n_new - L - n_mat, 0}.  A verification pass uses
+ * n_mat = S + accepted drafts and n_new = accepted + 1 (the verifier's own
+ * next token stays pending); an autoregressive step n_mat = n_new = 1; a
+ * commit without KV (confidence-only) n_mat = 0.
+ * Errors found on the device write nothing to the segments and set
+ * state_out = state_in with error = 1 (identity broken on entry), 2 (n_mat
+ * outside 0..W, n_new < 0, P + n_new >= 2^31 or L + n_mat > P + n_new) or 3
+ * (L + n_mat beyond the segments); an error already set in state_in is
+ * carried over.
+ * ---------------------------------------------------------------------- */
+
+/* segments: HOST array of nseg device pointers (16-byte aligned), copied into
+ * the kernel arguments; seg0_positions = C0 >= 1; layers >= 1; row_bytes a
+ * multiple of 16 in 16..65536; block: device, 16-byte aligned; 1 <= W <=
+ * TWD_KV_MAX_WIDTH; n_mat, n_new: device int32; state_in, state_out: device
+ * int32[4] that do not overlap (alternate two state words between calls).
+ * Asynchronous on stream; reads no device memory on the host, so it can be
+ * captured into a graph.  Errors: INVALID_ARG (null, misaligned, overlap,
+ * bad sizes), UNSUPPORTED (nseg outside 1..TWD_KV_MAX_SEGMENTS, capacity
+ * C0 * (2^nseg - 1) >= 2^31, 2 * layers > 65535). */
+twd_status twd_kv_commit(void *const *segments, int nseg, int64_t seg0_positions,
+                         int64_t layers, int64_t row_bytes, const void *block,
+                         int64_t W, const int32_t *n_mat, const int32_t *n_new,
+                         const int32_t *state_in, int32_t *state_out, void *stream);
 
 /* Measurement helper: a plain streaming read of `bytes` device bytes
  * (16-byte aligned, bytes % 16 == 0) that stores nothing but a guard word

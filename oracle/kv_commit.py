@@ -14,7 +14,8 @@ so that graphs reuse the shared history instead of copying it.  The pages
 write out neither the identity nor the layout; the readings taken here:
 
   state     : P committed tokens, L of them with causal KV rows stored
-              (materialized), S = P - L pending; identity P == L + S.
+              (materialized), S = P - L pending; identity P == L + S over
+              lengths L, S >= 0 (int32 words, so P stays below 2^31).
   segments  : segment s holds C0 * 2^s positions, following segments 0..s-1,
               so position p lives in the first segment whose cumulative
               capacity exceeds p.  Per segment, one buffer laid out
@@ -24,9 +25,10 @@ write out neither the identity nor the layout; the readings taken here:
               materialized, the leading ones) and n_new (tokens newly
               committed): L' = L + n_mat, P' = P + n_new, S' = P' - L'.  Valid
               iff the identity holds on entry, no error is set, 0 <= n_mat
-              <= W, n_new >= 0, L' <= P' and L' fits the segments; otherwise
-              nothing is written and the error code is set (1 identity,
-              2 counts, 3 capacity; an error already set is kept).
+              <= W, n_new >= 0, P' < 2^31, L' <= P' and L' fits the segments;
+              otherwise nothing is written and the error code is set
+              (1 identity, 2 counts, 3 capacity; an error already set is
+              kept).
   roles     : a verification pass has n_mat = S + a (the pending tokens and
               the a accepted drafts) and n_new = a + 1 (with the verifier's
               own next token, which stays pending); an autoregressive step
@@ -84,10 +86,10 @@ class KVStore:
         W = block.shape[2]
         if err:
             return
-        if P != L + S:
+        if L < 0 or S < 0 or P != L + S:
             self.state[3] = ERR_IDENTITY
             return
-        if not (0 <= n_mat <= W) or n_new < 0 or L + n_mat > P + n_new:
+        if not (0 <= n_mat <= W) or n_new < 0 or P + n_new > 2 ** 31 - 1 or L + n_mat > P + n_new:
             self.state[3] = ERR_COUNTS
             return
         if L + n_mat > self.capacity:

@@ -69,6 +69,8 @@ _lib_select = _sig("twd_select_kernel", [_i64, _i64, _i64, _int])
 _lib_quantize_fp8_rows = _sig("twd_quantize_fp8_rows", [_p, _i64, _i64, _p, _p])
 _lib_proj_fp8 = _sig("twd_projection_fp8", [_p, _p, _p, _i64, _i64, _i64, _p, _p, _p, _p])
 _lib_proj_bf16 = _sig("twd_projection_bf16", [_p, _p, _i64, _i64, _i64, _p, _p])
+_lib_kv_commit = _sig("twd_kv_commit",
+                      [_p, _int, _i64, _i64, _i64, _p, _i64, _p, _p, _p, _p, _p])
 _lib_stream_read = _sig("twd_stream_read", [_p, _i64, _p, _p])
 _lib_stream_copy = _sig("twd_stream_copy", [_p, _p, _i64, _p])
 
@@ -77,7 +79,7 @@ EXPORTS = ("twd_version", "twd_last_error", "twd_ternarize_absmean",
            "twd_ternary_linear", "twd_ternary_linear_fused",
            "twd_ternary_linear_fused_kernel", "twd_ternary_linear_bf16",
            "twd_select_kernel", "twd_quantize_fp8_rows", "twd_projection_fp8",
-           "twd_projection_bf16", "twd_stream_read", "twd_stream_copy")
+           "twd_projection_bf16", "twd_kv_commit", "twd_stream_read", "twd_stream_copy")
 
 
 class TwdError(RuntimeError):
@@ -340,6 +342,31 @@ def projection_bf16(w, x, y=None, stream=None):
                           _dev_ptr(x, "x", (torch.bfloat16, torch.int16)), M, K, N,
                           _dev_ptr(y, "y", (torch.float32,)), _stream(stream)))
     return y
+
+
+def kv_segment_positions(c0: int, nseg: int):
+    """Positions held by each KV segment: c0, 2 c0, 4 c0, ..."""
+    return [c0 << s for s in range(nseg)]
+
+
+def kv_commit(segments, c0: int, layers: int, row_bytes: int, block, W: int, n_mat, n_new,
+              state_in, state_out, stream=None):
+    """Accepted-prefix KV commit: store the first n_mat rows of block
+    ([layers][2][W][row_bytes] bytes on the device) into the segment buffers
+    at positions L.., and write the new (P, L, S, error) state to state_out.
+    segments: device tensors, segment s holding [layers][2][c0 2^s][row_bytes]
+    bytes; n_mat, n_new: device int32 (one element used); state_in /
+    state_out: device int32[4], distinct."""
+    nseg = len(segments)
+    for s, t in enumerate(segments):
+        _need(_nbytes(t) >= layers * 2 * (c0 << s) * row_bytes,
+              f"segment {s} smaller than layers * 2 * c0 * 2^s * row_bytes")
+    _need(_nbytes(block) >= layers * 2 * W * row_bytes, "block smaller than its rows")
+    ptrs = (ctypes.c_void_p * max(nseg, 1))(*[t.data_ptr() for t in segments])
+    _check(_lib_kv_commit(ptrs, nseg, int(c0), int(layers), int(row_bytes),
+                          _dev_ptr(block, "block"), int(W), _dev_ptr(n_mat, "n_mat"),
+                          _dev_ptr(n_new, "n_new"), _dev_ptr(state_in, "state_in"),
+                          _dev_ptr(state_out, "state_out"), _stream(stream)))
 
 
 def stream_read(buf, nbytes: int, sink, stream=None):

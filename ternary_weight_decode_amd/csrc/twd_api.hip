@@ -259,6 +259,49 @@ extern "C" twd_status twd_projection_bf16(const uint16_t *w_bf16, const uint16_t
                       "projection_bf16 launch");
 }
 
+extern "C" twd_status twd_kv_commit(void *const *segments, int nseg, int64_t seg0_positions,
+                                    int64_t layers, int64_t row_bytes, const void *block,
+                                    int64_t W, const int32_t *n_mat, const int32_t *n_new,
+                                    const int32_t *state_in, int32_t *state_out,
+                                    void *stream) {
+    if (nseg < 1 || nseg > TWD_KV_MAX_SEGMENTS)
+        return set_error(TWD_ERR_UNSUPPORTED, "kv_commit: nseg=%d outside 1..%d", nseg,
+                         TWD_KV_MAX_SEGMENTS);
+    if (seg0_positions < 1 || layers < 1 || row_bytes < 16 || row_bytes > 65536 ||
+        row_bytes % 16 != 0 || W < 1 || W > TWD_KV_MAX_WIDTH)
+        return set_error(TWD_ERR_INVALID_ARG,
+                         "kv_commit: need C0 >= 1, layers >= 1, row_bytes %% 16 == 0 in "
+                         "16..65536, 1 <= W <= %d",
+                         TWD_KV_MAX_WIDTH);
+    const int64_t capacity = seg0_positions * ((int64_t(1) << nseg) - 1);
+    if (seg0_positions >= (int64_t(1) << 31) || capacity >= (int64_t(1) << 31))
+        return set_error(TWD_ERR_UNSUPPORTED, "kv_commit: capacity C0 (2^nseg - 1) >= 2^31");
+    if (2 * layers > 65535)
+        return set_error(TWD_ERR_UNSUPPORTED, "kv_commit: layers > 32767");
+    if (!segments || !block || !n_mat || !n_new || !state_in || !state_out)
+        return set_error(TWD_ERR_INVALID_ARG, "kv_commit: null pointer");
+    KvSegments segs{};
+    for (int s = 0; s < nseg; ++s) {
+        if (!segments[s] || !aligned(segments[s], 16))
+            return set_error(TWD_ERR_INVALID_ARG,
+                             "kv_commit: segment %d is null or not 16-byte aligned", s);
+        segs.ptr[s] = segments[s];
+    }
+    segs.capacity = capacity;
+    if (!aligned(block, 16) || !aligned(n_mat, 4) || !aligned(n_new, 4) ||
+        !aligned(state_in, 4) || !aligned(state_out, 4))
+        return set_error(TWD_ERR_INVALID_ARG, "kv_commit: misaligned pointer");
+    const uintptr_t a = reinterpret_cast<uintptr_t>(state_in);
+    const uintptr_t b = reinterpret_cast<uintptr_t>(state_out);
+    if ((a < b ? b - a : a - b) < 16)
+        return set_error(TWD_ERR_INVALID_ARG, "kv_commit: state_in and state_out overlap");
+    return hip_status(launch_kv_commit(segs, static_cast<int>(seg0_positions),
+                                       static_cast<int>(layers), static_cast<int>(row_bytes),
+                                       block, static_cast<int>(W), n_mat, n_new, state_in,
+                                       state_out, as_stream(stream)),
+                      "kv_commit launch");
+}
+
 extern "C" twd_status twd_stream_read(const void *buf, int64_t bytes,
                                       uint32_t *sink, void *stream) {
     if (bytes < 0 || bytes % 16 != 0)

@@ -83,6 +83,17 @@ hipError_t launch_projection(bool fp8, const uint8_t *w, const float *wscale,
                              const uint16_t *x, int M, int K, int N, float *y,
                              uint8_t *xq_out, float *xs_out, hipStream_t stream);
 
+// Accepted-prefix KV commit (kv_commit.hip): the segment buffers as a kernel
+// argument, and the total positions they hold.
+struct KvSegments {
+    void *ptr[TWD_KV_MAX_SEGMENTS];
+    int64_t capacity;
+};
+hipError_t launch_kv_commit(const KvSegments &segs, int C0, int layers, int row_bytes,
+                            const void *block, int W, const int32_t *n_mat,
+                            const int32_t *n_new, const int32_t *state_in, int32_t *state_out,
+                            hipStream_t stream);
+
 hipError_t launch_stream_read(const void *buf, int64_t bytes, uint32_t *sink,
                               hipStream_t stream);
 hipError_t launch_stream_copy(const void *src, void *dst, int64_t bytes,

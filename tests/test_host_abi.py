@@ -254,3 +254,29 @@ def test_projection_rejects_before_launch(twd):
     assert f16(0x1000, 0x3008, 1, 256, 64, 0x4000, None) == 1
     assert f16(0x1000, 0x3000, 0, 256, 64, None, None) == 0
     assert twd._lib_last_error()
+
+
+def test_kv_commit_rejects_before_launch(twd):
+    f = twd._lib_kv_commit
+    segs = (ctypes.c_void_p * 4)(0x10000, 0x20000, 0x30000, 0x40000)
+    ok = dict(seg=segs, nseg=4, c0=8, layers=30, row=1280, block=0x50000, W=9,
+              nm=0x60000, nn=0x60010, si=0x70000, so=0x70010)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["seg"], a["nseg"], a["c0"], a["layers"], a["row"], a["block"], a["W"],
+                 a["nm"], a["nn"], a["si"], a["so"], None)
+
+    assert call(nseg=0) == 2 and call(nseg=25) == 2
+    assert call(W=0) == 1 and call(W=65) == 1
+    assert call(row=24) == 1 and call(row=0) == 1 and call(c0=0) == 1
+    assert call(c0=1 << 30, nseg=2) == 2                 # capacity >= 2^31
+    assert call(layers=40000) == 2
+    assert call(block=None) == 1 and call(si=None) == 1
+    assert call(block=0x50008) == 1                       # alignment
+    assert call(so=0x70008) == 1                          # overlapping state words
+    bad = (ctypes.c_void_p * 4)(0x10000, 0x20008, 0x30000, 0x40000)
+    assert call(seg=bad) == 1
+    nul = (ctypes.c_void_p * 4)(0x10000, None, 0x30000, 0x40000)
+    assert call(seg=nul) == 1
+    assert twd._lib_last_error()

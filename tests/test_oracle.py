@@ -471,6 +471,9 @@ def test_kv_commit_invariants_and_errors():
     bad = kv.KVStore(c0=4, nseg=5, layers=2, row=3, state=(5, 2, 2, 0))
     bad.commit(np.ones((2, 2, 2, 3), np.uint16), 1, 1)
     assert bad.state == [5, 2, 2, kv.ERR_IDENTITY] and not any(s.any() for s in bad.segs)
+    neg = kv.KVStore(c0=4, nseg=5, layers=2, row=3, state=(1, -2, 3, 0))
+    neg.commit(np.ones((2, 2, 2, 3), np.uint16), 1, 1)
+    assert neg.state[3] == kv.ERR_IDENTITY and not any(s.any() for s in neg.segs)
     full = kv.KVStore(c0=2, nseg=3, layers=1, row=2, state=(14, 13, 1, 0))
     full.commit(np.ones((1, 2, 2, 2), np.uint16), 2, 1)
     assert full.state == [14, 13, 1, kv.ERR_CAPACITY]
