@@ -211,6 +211,68 @@ def output_projection_bench(twd, torch, widths, reps):
     return out
 
 
+def kv_commit_bench(twd, torch, ls, reps, D=8, steps=64, c0=256, nseg=8, start=1000):
+    """Accepted-prefix KV commits on the 2B-class KV geometry (30 layers, K
+    and V rows of 640 bf16 = 1280 bytes; segments of 256 * 2^s positions,
+    8 segments, 65280 positions): one captured graph of 64 verification
+    commits of width D + 1 = 9, the state words alternating, with seeded
+    acceptance lengths a ~ uniform{0..D} (n_mat = 1 + a, n_new = a + 1).
+    Each replay continues from the state the last one left.  Beside it: the
+    time of copying the whole history once (what graphs without a shared KV
+    view would pay), as a plain copy of the same bytes."""
+    layers, row_bytes = ls.layers, ls.projs[0].segs[1] * 2
+    W = D + 1
+    pos_bytes = layers * 2 * row_bytes
+    segs = [torch.zeros(layers * 2 * cap * row_bytes, dtype=torch.uint8, device="cuda")
+            for cap in twd.kv_segment_positions(c0, nseg)]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(13)
+    blocks = [torch.randint(0, 256, (layers * 2 * W * row_bytes,), dtype=torch.uint8,
+                            device="cuda", generator=gen) for _ in range(4)]
+    rng = np.random.default_rng(2027)
+    acc = rng.integers(0, D + 1, steps)
+    nm = torch.from_numpy((1 + acc).astype(np.int32)).cuda()
+    nn = torch.from_numpy((acc + 1).astype(np.int32)).cuda()
+    state = torch.zeros((2, 4), dtype=torch.int32, device="cuda")
+    state[0] = torch.tensor([start + 1, start, 1, 0], dtype=torch.int32)
+
+    def seq():
+        for i in range(steps):
+            twd.kv_commit(segs, c0, layers, row_bytes, blocks[i % 4], W, nm[i:i + 1],
+                          nn[i:i + 1], state[i % 2], state[(i + 1) % 2])
+
+    per_replay = int((1 + acc).sum())
+    reps = max(1, min(reps, (c0 * (2 ** nseg - 1) - start) // per_replay - 2))
+    g = capture(torch, seq)   # capture() runs the sequence once eagerly first
+    g.replay()
+    _, sec = time_replays(torch, g, reps)
+    torch.cuda.synchronize()
+    final = state[0].cpu().tolist()
+    expect_L = start + per_replay * (reps + 2)
+    if final[3] != 0 or final[1] != expect_L or final[0] != final[1] + final[2]:
+        raise SystemExit(f"kv commit state {final}, expected L={expect_L}")
+    us = sec / (reps * steps) * 1e6
+    moved = 2 * pos_bytes * per_replay / steps  # bytes read + written per commit
+    hist_bytes = final[1] * pos_bytes
+    src = torch.empty(hist_bytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    gc = capture(torch, lambda: twd.stream_copy(src, dst, hist_bytes))
+    gc.replay()
+    _, csec = time_replays(torch, gc, 5)
+    del segs, blocks, src, dst
+    torch.cuda.empty_cache()
+    return {"geometry": f"{layers} layers x K,V rows of {row_bytes} B; segments of {c0}*2^s "
+                        f"positions, {nseg} segments ({c0 * (2 ** nseg - 1)} positions)",
+            "width": W, "commits_timed": reps * steps,
+            "mean_rows_per_commit": round(per_replay / steps, 3),
+            "us_per_commit": round(us, 3),
+            "bytes_moved_per_commit": round(moved),
+            "gbs": round(moved / us / 1e3, 1),
+            "final_state": final,
+            "full_history_copy_us": round(csec / 5 * 1e6, 1),
+            "full_history_bytes": hist_bytes}
+
+
 def kernel_map(twd, ls, M, kernel, bf16_input=True):
     """Kernel family each projection of the set runs at width M, for bf16
     activations (one launch) or int8 ones (the linear of the two-launch
@@ -665,6 +727,8 @@ def main():
                     help="1: time each projection shape on its own, cold (default)")
     ap.add_argument("--projection-widths", default="1,4,8,16",
                     help="widths of the fast / critical output-projection table ('' skips it)")
+    ap.add_argument("--kv-commit", type=int, default=1,
+                    help="time the accepted-prefix KV commit (1) or not (0)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with plain copies of 256 MiB (byte-counter calibration)")
     ap.add_argument("--summarize-profile", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
@@ -780,6 +844,7 @@ def main():
             torch.cuda.empty_cache()
 
     proj_table = per_projection(twd, torch, ls, M, kernel, reps) if args.per_proj else None
+    kvc = kv_commit_bench(twd, torch, ls, reps) if args.kv_commit else None
     head = None
     if args.projection_widths:
         head = output_projection_bench(
@@ -830,6 +895,7 @@ def main():
         "widths": widths,
         "per_projection_cold": proj_table,
         "output_projection": head,
+        "kv_commit": kvc,
         "cpu_baseline": cpu,
         "cpu_single_thread": cpu1,
     }
