@@ -18,9 +18,9 @@
 //
 // Arithmetic.  Every E4M3 value is exactly a bf16 value, so both roles run
 // on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16, fp32 accumulation):
-// a fast-role weight code is widened exactly (v_cvt_pk_f32_fp8, then the
-// high halves of the fp32 results are the bf16 bits), and the activation
-// codes are staged in LDS as the bf16 values they decode to.  The gfx950
+// a fast-role weight code pair is widened exactly by one
+// v_cvt_scalef32_pk_bf16_fp8 (scale 1), and the activation codes are staged
+// in LDS as the bf16 values they decode to.  The gfx950
 // FP8 matrix instruction was not used: on random codes its sums differ
 // from the exact ones by up to ~1e-4 of the sum of |products|, more than
 // fp32 accumulation of the same products allows.
@@ -43,41 +43,43 @@ using namespace kern;
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
-typedef float v2f __attribute__((ext_vector_type(2)));
 
 constexpr int kRawBufferFlags = 0x00020000;
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
-constexpr int kProjWaves = 16;            // waves per workgroup
-constexpr int kThreadsP = 64 * kProjWaves;    // threads per workgroup
-constexpr int kLoadsP = 8;                // 16-byte weight loads per lane per chunk
 constexpr int kPieceP = 512;              // activation elements per wave load pass
 constexpr int kPasses = 8;                // passes: K <= 4096
 constexpr int kScaleTiles = 4;            // weight-scale tiles per wave staged in LDS
 
-template <bool FP8>
+// Launch shape: NWV waves per workgroup, LD 16-byte weight loads per lane
+// per chunk.
+constexpr int kShapeWaves = 16;
+constexpr int kShapeLoads = 8;
+template <bool FP8, int NWV, int LD>
 struct Role {
     static constexpr int kElemBytes = FP8 ? 1 : 2;
     static constexpr int kPerLoad = FP8 ? 64 : 32;  // row elements per 64-byte load step
-    static constexpr int kChunk = kLoadsP * kPerLoad;
+    static constexpr int kChunk = LD * kPerLoad;
+    static constexpr int kThreads = 64 * NWV;
+    static_assert(NWV * 64 == NWV * kScaleTiles * 16, "one weight scale per thread");
 };
 
 // LDS: M staged token rows of Kp bf16 values (stride 2 Kp + 16 bytes, so
 // that the 16 token rows of one B read fall on different banks) | a 16-byte
 // zero block | token scales [16] | weight scales of each wave's first
-// kScaleTiles tiles [kProjWaves][kScaleTiles][16].
+// kScaleTiles tiles [waves][kScaleTiles][16].
 __host__ __device__ constexpr int stage_stride(int Kp) { return 2 * Kp + 16; }
-__host__ __device__ constexpr int stage_bytes(int M, int Kp) {
-    return M * stage_stride(Kp) + 16 + 16 * 4 + kProjWaves * kScaleTiles * 16 * 4;
+__host__ __device__ constexpr int stage_bytes(int M, int Kp, int waves) {
+    return M * stage_stride(Kp) + 16 + 16 * 4 + waves * kScaleTiles * 16 * 4;
 }
 
-// Two E4M3 codes (the low or high 16 bits of w) widened exactly to a bf16
-// pair: exact fp32 values whose low 16 bits are zero, so their high halves
-// are the bf16 bits.
+// Two E4M3 codes (the low or high 16 bits of w) widened to a bf16 pair:
+// every E4M3 value is a bf16 value, so the conversion (scale 1) is exact.
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 template <bool HI>
 __device__ __forceinline__ uint32_t fp8x2_bf16(uint32_t w) {
-    const v2f f = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), HI);
-    return __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
+    const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w), 1.0f, HI);
+    return __builtin_bit_cast(uint32_t, b);
 }
 
 __device__ __forceinline__ v8bf as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
@@ -85,8 +87,8 @@ __device__ __forceinline__ v8bf as_bf16x8(uint32_t a, uint32_t b, uint32_t c, ui
     return __builtin_bit_cast(v8bf, u);
 }
 
-template <bool FP8>
-__device__ __forceinline__ void load_chunk(uint4 (&buf)[kLoadsP], const uint8_t *W, int tile,
+template <int LD>
+__device__ __forceinline__ void load_chunk(uint4 (&buf)[LD], const uint8_t *W, int tile,
                                            int tile_end, int N, int row_bytes, int c, int r, int g) {
     // tiles at or past tile_end (this wave's range) load nothing
     const int n0 = tile * 16;
@@ -95,22 +97,22 @@ __device__ __forceinline__ void load_chunk(uint4 (&buf)[kLoadsP], const uint8_t 
         const_cast<uint8_t *>(W + static_cast<int64_t>(tile < tile_end ? n0 : 0) * row_bytes), 0,
         __builtin_amdgcn_readfirstlane(rows * row_bytes), kRawBufferFlags);
 #pragma unroll
-    for (int j = 0; j < kLoadsP; ++j) {
-        const int col = (c * kLoadsP + j) * 64 + 16 * g;
+    for (int j = 0; j < LD; ++j) {
+        const int col = (c * LD + j) * 64 + 16 * g;
         const uint32_t off = col < row_bytes ? static_cast<uint32_t>(r * row_bytes + col) : kOutOfRange;
         const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
         buf[j] = make_uint4(v[0], v[1], v[2], v[3]);
     }
 }
 
-template <bool FP8>
-__device__ __forceinline__ v4f compute_chunk(const uint4 (&buf)[kLoadsP], v4f acc, const uint8_t *bsrc,
+template <bool FP8, int LD>
+__device__ __forceinline__ v4f compute_chunk(const uint4 (&buf)[LD], v4f acc, const uint8_t *bsrc,
                                              int estep, int c, int g) {
 #pragma unroll
-    for (int j = 0; j < kLoadsP; ++j) {
+    for (int j = 0; j < LD; ++j) {
         const uint4 w = buf[j];
         if constexpr (FP8) {
-            const int e0 = (c * kLoadsP + j) * 64 + 16 * g;
+            const int e0 = (c * LD + j) * 64 + 16 * g;
             const v8bf a0 = as_bf16x8(fp8x2_bf16<false>(w.x), fp8x2_bf16<true>(w.x),
                                       fp8x2_bf16<false>(w.y), fp8x2_bf16<true>(w.y));
             const v8bf a1 = as_bf16x8(fp8x2_bf16<false>(w.z), fp8x2_bf16<true>(w.z),
@@ -120,7 +122,7 @@ __device__ __forceinline__ v4f compute_chunk(const uint4 (&buf)[kLoadsP], v4f ac
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b0, a0, acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b1, a1, acc, 0, 0, 0);
         } else {
-            const int e0 = (c * kLoadsP + j) * 32 + 8 * g;
+            const int e0 = (c * LD + j) * 32 + 8 * g;
             const v8bf a = __builtin_bit_cast(v8bf, w);
             const v8bf b = *reinterpret_cast<const v8bf *>(bsrc + 2 * e0 * estep);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, a, acc, 0, 0, 0);
@@ -129,12 +131,13 @@ __device__ __forceinline__ v4f compute_chunk(const uint4 (&buf)[kLoadsP], v4f ac
     return acc;
 }
 
-template <bool FP8>
-__global__ __launch_bounds__(kThreadsP) void projection_kernel(
+template <bool FP8, int NWV, int LD>
+__global__ __launch_bounds__(64 * NWV) void projection_kernel(
     const uint8_t *__restrict__ W, const float *__restrict__ wscale,
     const uint16_t *__restrict__ x, int M, int K, int N, int Kp, float *__restrict__ y, int ldy,
     uint8_t *__restrict__ xq_out, float *__restrict__ xs_out) {
-    using R = Role<FP8>;
+    using R = Role<FP8, NWV, LD>;
+    constexpr int kRows = (TWD_MAX_M + NWV - 1) / NWV;  // token rows staged per wave
     extern __shared__ __align__(16) uint8_t smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -147,14 +150,14 @@ __global__ __launch_bounds__(kThreadsP) void projection_kernel(
     float *st_ws = st_scale + 16;  // [wave][kScaleTiles][16]
     const int row_bytes = K * R::kElemBytes;
     const int tiles = (N + 15) / 16;
-    const int nwaves = gridDim.x * kProjWaves;
+    const int nwaves = gridDim.x * NWV;
     const int C = Kp / R::kChunk;  // chunks per tile
     // each wave owns a contiguous, even-sized range of tiles: it writes the
     // outputs of two neighbouring tiles together, so that every 128-byte
     // line of y leaves the L2 whole (a half-written line would be evicted
     // by the weight stream before its other half arrived)
     const int tpw = 2 * ((tiles + 2 * nwaves - 1) / (2 * nwaves));
-    const int first = (blockIdx.x * kProjWaves + wave) * tpw;
+    const int first = (blockIdx.x * NWV + wave) * tpw;
     const int ntiles = max(0, min(tpw, tiles - first));
     const int tile_end = first + ntiles;
     const int total = ntiles * C;
@@ -166,26 +169,28 @@ __global__ __launch_bounds__(kThreadsP) void projection_kernel(
     float wsv = 0.0f;
     if constexpr (FP8) {
         const int w = tid >> 6;
-        const int n = ((blockIdx.x * kProjWaves + w) * tpw + ((tid >> 4) & 3)) * 16 + (tid & 15);
+        const int n = ((blockIdx.x * NWV + w) * tpw + ((tid >> 4) & 3)) * 16 + (tid & 15);
         const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<float *>(wscale), 0, N * 4, kRawBufferFlags);
         wsv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
             sr, n < N ? static_cast<uint32_t>(4 * n) : kOutOfRange, 0, 0));
     }
     __builtin_amdgcn_sched_barrier(0);
-    // lane l takes elements 512 p + 8 l .. + 7 of pass p (zeros past K)
-    uint4 xv[kPasses];
-    {
-        const int m = wave < M ? wave : 0;
+    // wave w stages token rows w, w + NWV, ...; lane l takes elements
+    // 512 p + 8 l .. + 7 of pass p (zeros past K)
+    uint4 xv[kRows][kPasses];
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+        const int m = wave + NWV * i;
         const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t *>(x + static_cast<int64_t>(m) * K), 0,
-            __builtin_amdgcn_readfirstlane(wave < M ? K * 2 : 0), kRawBufferFlags);
+            const_cast<uint16_t *>(x + static_cast<int64_t>(m < M ? m : 0) * K), 0,
+            __builtin_amdgcn_readfirstlane(m < M ? K * 2 : 0), kRawBufferFlags);
 #pragma unroll
         for (int p = 0; p < kPasses; ++p) {
             const int k0 = kPieceP * p + 8 * lane;
             const uint32_t off = k0 < K ? static_cast<uint32_t>(2 * k0) : kOutOfRange;
             const auto v = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
-            xv[p] = make_uint4(v[0], v[1], v[2], v[3]);
+            xv[i][p] = make_uint4(v[0], v[1], v[2], v[3]);
         }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -194,10 +199,10 @@ __global__ __launch_bounds__(kThreadsP) void projection_kernel(
     // and the load counter waits stay exact, one chunk always in flight.
     const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
         y, 0, M * ldy * 4, kRawBufferFlags);
-    uint4 bA[kLoadsP], bB[kLoadsP];
+    uint4 bA[LD], bB[LD];
     int t_ld = first, c_ld = 0;  // next item to load
-    auto next_load = [&](uint4 (&buf)[kLoadsP]) {
-        load_chunk<FP8>(buf, W, t_ld, tile_end, N, row_bytes, c_ld, r, g);
+    auto next_load = [&](uint4 (&buf)[LD]) {
+        load_chunk<LD>(buf, W, t_ld, tile_end, N, row_bytes, c_ld, r, g);
         if (++c_ld == C) {
             c_ld = 0;
             ++t_ld;
@@ -227,20 +232,23 @@ __global__ __launch_bounds__(kThreadsP) void projection_kernel(
     put(zero4, zero4, 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
 
-    // 2. stage the activations as bf16 (wave m owns token row m)
+    // 2. stage the activations as bf16 (wave w owns token rows w, w + NWV)
     if constexpr (FP8)
         st_ws[tid] = wsv;
-    if (wave < M) {
-        const int m = wave;
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+        const int m = wave + NWV * i;
+        if (m >= M)
+            break;
         uint8_t *row = smem + m * stride;
         if constexpr (FP8) {
             u16x2 am2 = {0, 0};
 #pragma unroll
             for (int p = 0; p < kPasses; ++p) {
-                am2 = absmax_pair(am2, xv[p].x);
-                am2 = absmax_pair(am2, xv[p].y);
-                am2 = absmax_pair(am2, xv[p].z);
-                am2 = absmax_pair(am2, xv[p].w);
+                am2 = absmax_pair(am2, xv[i][p].x);
+                am2 = absmax_pair(am2, xv[i][p].y);
+                am2 = absmax_pair(am2, xv[i][p].z);
+                am2 = absmax_pair(am2, xv[i][p].w);
             }
             const float a = __uint_as_float(wave_umax(absmax_bits(am2)));
             // correctly rounded fp32 divisions (build flag)
@@ -254,7 +262,7 @@ __global__ __launch_bounds__(kThreadsP) void projection_kernel(
 #pragma unroll
             for (int p = 0; p < kPasses; ++p) {
                 const int k0 = kPieceP * p + 8 * lane;
-                const uint32_t w4[4] = {xv[p].x, xv[p].y, xv[p].z, xv[p].w};
+                const uint32_t w4[4] = {xv[i][p].x, xv[i][p].y, xv[i][p].z, xv[i][p].w};
                 uint32_t q[2];
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
@@ -282,7 +290,7 @@ __global__ __launch_bounds__(kThreadsP) void projection_kernel(
             for (int p = 0; p < kPasses; ++p) {
                 const int k0 = kPieceP * p + 8 * lane;
                 if (k0 < Kp)
-                    *reinterpret_cast<uint4 *>(row + 2 * k0) = xv[p];
+                    *reinterpret_cast<uint4 *>(row + 2 * k0) = xv[i][p];
             }
         }
     }
@@ -303,8 +311,8 @@ __global__ __launch_bounds__(kThreadsP) void projection_kernel(
         sx[i] = FP8 && 4 * g + i < M ? st_scale[4 * g + i] : 1.0f;
     int t_cp = first, c_cp = 0, ord = 0;  // item being computed, its tile ordinal
     v4f acc = zero4, held = zero4;
-    auto step = [&](uint4 (&buf)[kLoadsP]) {
-        acc = compute_chunk<FP8>(buf, acc, bsrc, estep, c_cp, g);
+    auto step = [&](uint4 (&buf)[LD]) {
+        acc = compute_chunk<FP8, LD>(buf, acc, bsrc, estep, c_cp, g);
         next_load(buf);
         v4f v = acc;
         if constexpr (FP8) {
@@ -363,20 +371,23 @@ int compute_units() {
 }  // namespace
 
 int projection_padded_k(bool fp8, int K) {
-    const int chunk = fp8 ? Role<true>::kChunk : Role<false>::kChunk;
+    const int chunk = fp8 ? Role<true, kShapeWaves, kShapeLoads>::kChunk
+                          : Role<false, kShapeWaves, kShapeLoads>::kChunk;
     return (K + chunk - 1) / chunk * chunk;
 }
 
 int projection_lds_bytes(bool fp8, int M, int K) {
-    return stage_bytes(M, projection_padded_k(fp8, K));
+    return stage_bytes(M, projection_padded_k(fp8, K), kShapeWaves);
 }
 
 hipError_t launch_projection(bool fp8, const uint8_t *w, const float *wscale,
                              const uint16_t *x, int M, int K, int N, float *y,
                              uint8_t *xq_out, float *xs_out, hipStream_t stream) {
+    constexpr int NWV = kShapeWaves;
     const int Kp = projection_padded_k(fp8, K);
-    const int lds = stage_bytes(M, Kp);
-    const ProjFn fn = fp8 ? &projection_kernel<true> : &projection_kernel<false>;
+    const int lds = stage_bytes(M, Kp, NWV);
+    const ProjFn fn = fp8 ? &projection_kernel<true, NWV, kShapeLoads>
+                          : &projection_kernel<false, NWV, kShapeLoads>;
     hipError_t e = ensure_lds_limit(reinterpret_cast<const void *>(fn), lds);
     if (e != hipSuccess)
         return e;
@@ -386,13 +397,13 @@ hipError_t launch_projection(bool fp8, const uint8_t *w, const float *wscale,
     // one launch per span of rows in which every wave has at most
     // kScaleTiles tiles (the weight scales it keeps in LDS)
     const int64_t row_bytes = static_cast<int64_t>(K) * (fp8 ? 1 : 2);
-    const int span = kScaleTiles * kProjWaves * cus * 16;
+    const int span = kScaleTiles * NWV * cus * 16;
     for (int n0 = 0; n0 < N; n0 += span) {
         const int rows = N - n0 < span ? N - n0 : span;
         const int tiles = (rows + 15) / 16;
-        const int want = (tiles + kProjWaves - 1) / kProjWaves;
+        const int want = (tiles + NWV - 1) / NWV;
         const int grid = want < cus ? want : cus;
-        hipLaunchKernelGGL(fn, dim3(grid), dim3(kThreadsP), lds, stream, w + n0 * row_bytes,
+        hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * NWV), lds, stream, w + n0 * row_bytes,
                            wscale ? wscale + n0 : nullptr, x, M, K, rows, Kp, y + n0, N,
                            n0 == 0 ? xq_out : nullptr, n0 == 0 ? xs_out : nullptr);
         e = hipGetLastError();
