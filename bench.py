@@ -211,6 +211,59 @@ def output_projection_bench(twd, torch, widths, reps):
     return out
 
 
+def cpu_projection_baseline(budget_s, M=1, rows=1024):
+    """The CPU oracle of both projection roles (single-threaded C loops:
+    E4M3 decode, exact int64 sums / double sums) on a sample of the output
+    projection's rows, repeated until budget_s; throughput in weight bytes/s
+    of each role."""
+    import oracle
+    oracle.build(force=False)
+    W = wl.head_weight_block(0)[:rows]
+    x = wl.head_activations(M)
+    out = {}
+    for role, bpw in (("fast_fp8", 1), ("critical_bf16", 2)):
+        if role == "fast_fp8":
+            wq, _ = oracle.quantize_fp8_rows(W)
+            xq, _ = oracle.quantize_act_fp8(x)
+            fn = lambda: oracle.fp8_linear(xq, wq)  # noqa: E731
+        else:
+            wb = wl.f32_to_bf16_bits(W)
+            fn = lambda: oracle.bf16_linear(x, wb)  # noqa: E731
+        spent, n = 0.0, 0
+        while n == 0 or spent < budget_s:
+            t0 = time.perf_counter()
+            fn()
+            spent += time.perf_counter() - t0
+            n += 1
+        out[role] = {"value": round(rows * wl.HEAD_K * bpw * n / spent / 1e9, 4), "unit": "GB/s",
+                     "cores": 1, "kind": "oracle",
+                     "sample": f"{n} pass(es) over {rows} rows of the output projection at M={M} "
+                               f"({spent:.1f} s; weight bytes/s)"}
+    return out
+
+
+def cpu_kv_baseline(budget_s, D=8, c0=256, nseg=8, start=1000):
+    """The CPU oracle of the KV commit (oracle/kv_commit.py) on the bench's
+    geometry and acceptance draws, timed per commit on one thread."""
+    from oracle import kv_commit as okv
+    ls = wl.SET_2B
+    layers, row = ls.layers, ls.projs[0].segs[1]
+    store = okv.KVStore(c0, nseg, layers, row, state=(start + 1, start, 1, 0))
+    rng = np.random.default_rng(2027)
+    block = rng.integers(0, 65536, (layers, 2, D + 1, row)).astype(np.uint16)
+    spent, n, moved = 0.0, 0, 0
+    while n == 0 or spent < budget_s:
+        a = int(rng.integers(0, D + 1))
+        t0 = time.perf_counter()
+        store.commit(block, 1 + a, a + 1)
+        spent += time.perf_counter() - t0
+        n += 1
+        moved += 2 * (1 + a) * layers * 2 * row * 2
+    return {"value": round(spent / n * 1e6, 1), "unit": "us per commit", "cores": 1,
+            "kind": "oracle", "gbs": round(moved / spent / 1e9, 3),
+            "sample": f"{n} commits of width {D + 1} on the 2B-class KV geometry ({spent:.1f} s)"}
+
+
 def kv_commit_bench(twd, torch, ls, reps, D=8, steps=64, c0=256, nseg=8, start=1000):
     """Accepted-prefix KV commits on the 2B-class KV geometry (30 layers, K
     and V rows of 640 bf16 = 1280 bytes; segments of 256 * 2^s positions,
@@ -855,6 +908,11 @@ def main():
     if args.projection_widths:
         head = output_projection_bench(
             twd, torch, [int(v) for v in args.projection_widths.split(",") if v], reps)
+    if args.cpu_seconds > 0:
+        if head is not None:
+            head["cpu_baseline"] = cpu_projection_baseline(args.cpu_seconds / 5)
+        if kvc is not None:
+            kvc["cpu_baseline"] = cpu_kv_baseline(args.cpu_seconds / 10)
     calib = copy_calibration(twd, torch) if args.copy_calibration else None
 
     cpu = cpu1 = None
