@@ -505,6 +505,15 @@ def _linear_fused(name):
             and short.endswith("true>"))
 
 
+# The counter calibration copies 256 MiB: 16384 workgroups of 256 threads
+# (the benchmark's other copies, e.g. the KV history copy, differ in size).
+COPY_GRID_THREADS = (256 << 20) // 16 // 4
+
+
+def grid(r):
+    return int(_col(r, "Grid_Size", "Grid_Size_X", "grid_size"))
+
+
 def summarize_profiles(args):
     trace_dir, fetch_dir, write_dir = args.summarize_profile
     cmds = args.profile_commands or ("?", "?", "?")
@@ -600,7 +609,8 @@ def summarize_profiles(args):
     copy_bytes = 256 << 20
 
     def copy_factor(agg):
-        vals = [v for (n, _), vs in agg.items() if "stream_copy_kernel" in n for v in vs]
+        vals = [v for (n, g), vs in agg.items()
+                if "stream_copy_kernel" in n and g == COPY_GRID_THREADS for v in vs]
         return copy_bytes / (sum(vals) / len(vals) * 1024.0), sum(vals) / len(vals)
 
     f_fetch, copy_fetch_kib = copy_factor(fetch)
@@ -650,8 +660,8 @@ def summarize_projection(args):
     trace_dir, fetch_dir, write_dir = args.summarize_projection
     cmds = args.profile_commands or ("?", "?", "?")
     K, N = wl.HEAD_K, wl.HEAD_N
-    roles = (("projection_kernel<true>", "fast (E4M3 weights)", N * K),
-             ("projection_kernel<false>", "critical (bf16 weights)", 2 * N * K))
+    roles = (("projection_kernel<true", "fast (E4M3 weights)", N * K),
+             ("projection_kernel<false", "critical (bf16 weights)", 2 * N * K))
     trace = _csv_rows(trace_dir, "kernel_trace.csv")
     lines = ["# output projection 2560 -> 128256, M=1: rocprofv3 kernel trace and HBM counters",
              "", "Commands (from the repository root):", "", "    " + cmds[0], "",
@@ -663,17 +673,17 @@ def summarize_projection(args):
              " % of 8 TB/s |", "|---|---|---|---|---|---|---|---|"]
     avg = {}
     for kname, role, nbytes in roles:
+        names = {_short(_col(r, "Kernel_Name")) for r in trace
+                 if _short(_col(r, "Kernel_Name")).startswith(kname)}
         d = [int(_col(r, "End_Timestamp")) - int(_col(r, "Start_Timestamp"))
-             for r in trace if _short(_col(r, "Kernel_Name")) == kname]
+             for r in trace if _short(_col(r, "Kernel_Name")).startswith(kname)]
         a = sum(d) / len(d)
         avg[kname] = a
-        lines.append(f"| {role} | `{kname}` | {len(d)} | {a / 1e3:.2f} | {min(d) / 1e3:.2f} | "
+        shown = ", ".join(f"`{n}`" for n in sorted(names))
+        lines.append(f"| {role} | {shown} | {len(d)} | {a / 1e3:.2f} | {min(d) / 1e3:.2f} | "
                      f"{nbytes:,} | {nbytes / a:.1f} | {100 * nbytes / a / HBM_PEAK_GBS:.1f} |")
     # the streaming reads over the projection's weight copies (the largest
     # grids of that kernel in the run; the layer sweep's are far smaller)
-    def grid(r):
-        return int(_col(r, "Grid_Size", "Grid_Size_X", "grid_size"))
-
     sr = [r for r in trace if _short(_col(r, "Kernel_Name")) == "stream_read_kernel"]
     big = max((grid(r) for r in sr), default=0)
     reads = {}
@@ -686,8 +696,13 @@ def summarize_projection(args):
         agg = {}
         for r in _csv_rows(d, "counter_collection.csv"):
             if _col(r, "Counter_Name") == counter:
-                agg.setdefault(_short(_col(r, "Kernel_Name")), []).append(
-                    float(_col(r, "Counter_Value")))
+                name = _short(_col(r, "Kernel_Name"))
+                for kname, _, _ in roles:
+                    if name.startswith(kname):
+                        name = kname
+                if name == "stream_copy_kernel" and grid(r) != COPY_GRID_THREADS:
+                    continue  # only the calibration copy of known size
+                agg.setdefault(name, []).append(float(_col(r, "Counter_Value")))
         return {k: sum(v) / len(v) for k, v in agg.items()}
 
     fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
