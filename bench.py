@@ -203,6 +203,20 @@ def output_projection_bench(twd, torch, widths, reps):
         out["fast_fp8"][str(M)] = timed(lambda c: twd.projection_fp8(w8[c], ws, x, y=y), N * K)
         out["critical_bf16"][str(M)] = timed(lambda c: twd.projection_bf16(w16[c], x, y=y),
                                              2 * N * K)
+    rec = None
+    path = os.path.join(PROFILES, "output_projection_counters_2b_m1.json")
+    if os.path.exists(path):
+        with open(path) as f:
+            rec = json.load(f)
+        if rec.get("source_hash") != kernel_source_hash(PROJECTION_SOURCES):
+            rec = None
+    for role, nbytes in (("fast_fp8", N * K), ("critical_bf16", 2 * N * K)):
+        one = out[role].get("1")
+        if one:
+            out[role]["roofline_m1"] = {
+                "bound": "hbm", "achieved": one["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": one["frac"],
+                "traffic": rec[role]["hbm_bytes_per_launch"] if rec else None}
     out["stream_read_fp8_bytes"] = timed(lambda c: twd.stream_read(w8[c], N * K, sink), N * K)
     out["stream_read_bf16_bytes"] = timed(lambda c: twd.stream_read(w16[c], 2 * N * K, sink),
                                           2 * N * K)
@@ -400,10 +414,13 @@ LINEAR_SOURCES = ("dispatch.hip", "kernel_common.h", "quantize_act.hip", "ternar
                   "ternary_rows.hip", "ternary_staged.hip", "ternary_tile.hip")
 
 
-def kernel_source_hash():
+PROJECTION_SOURCES = ("kernel_common.h", "projection.hip")
+
+
+def kernel_source_hash(names=LINEAR_SOURCES):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "ternary_weight_decode_amd", "csrc")
-    for name in LINEAR_SOURCES:
+    for name in names:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -714,11 +731,18 @@ def summarize_projection(args):
               f"WRITE_SIZE {write['stream_copy_kernel']:.1f} KiB (factor {fw:.4f}).", "",
               "| role | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes read (calibrated) | "
               "over algorithmic | HBM bytes written |", "|---|---|---|---|---|---|"]
+    rec = {"source_hash": kernel_source_hash(PROJECTION_SOURCES), "M": 1,
+           "fetch_factor": round(ff, 5), "write_factor": round(fw, 5)}
     for kname, role, nbytes in roles:
         rd = fetch[kname] * 1024 * ff
         wr = write[kname] * 1024 * fw
         lines.append(f"| {role} | {fetch[kname]:.1f} | {write[kname]:.1f} | {rd:,.0f} | "
                      f"{rd / nbytes:.3f}x | {wr:,.0f} |")
+        rec["fast_fp8" if "true" in kname else "critical_bf16"] = {
+            "hbm_bytes_per_launch": round(rd + wr), "algorithmic_bytes_per_launch": nbytes,
+            "kernel_trace_avg_us": round(avg[kname] / 1e3, 3)}
+    with open(os.path.join(args.profile_out, "output_projection_counters_2b_m1.json"), "w") as f:
+        json.dump(rec, f, indent=1)
     for g, d in sorted(reads.items()):
         nbytes = g * 16 * 4  # 256 threads x 4 loads x 16 bytes per workgroup
         a = sum(d) / len(d)
