@@ -418,11 +418,19 @@ PROJECTION_SOURCES = ("kernel_common.h", "projection.hip")
 
 
 def kernel_source_hash(names=LINEAR_SOURCES):
+    """Hash of the code (comments and blank space removed) of the given
+    kernel sources: counter records stay valid across comment edits and
+    lapse when the code changes."""
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "ternary_weight_decode_amd", "csrc")
     for name in names:
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(csrc, name)) as f:
+            code = f.read()
+        code = re.sub(r"/\*.*?\*/", " ", code, flags=re.S)
+        code = re.sub(r"//[^\n]*", " ", code)
+        code = " ".join(code.split())
+        h.update(name.encode() + code.encode())
     return h.hexdigest()[:16]
 
 

@@ -20,10 +20,10 @@
 // on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16, fp32 accumulation):
 // a fast-role weight code pair is widened exactly by one
 // v_cvt_scalef32_pk_bf16_fp8 (scale 1), and the activation codes are staged
-// in LDS as the bf16 values they decode to.  The gfx950
-// FP8 matrix instruction was not used: on random codes its sums differ
-// from the exact ones by up to ~1e-4 of the sum of |products|, more than
-// fp32 accumulation of the same products allows.
+// in LDS as the bf16 values they decode to.  The gfx950 FP8 matrix
+// instruction was not used: on random codes its sums differ from the exact
+// ones by up to ~1e-4 of the sum of |products|, more than fp32 accumulation
+// of the same products allows.
 //
 // Layout.  In load j of chunk c, lane l (row r = l % 16, K group g = l / 16)
 // reads the 16 bytes at byte (8 c + j) 64 + 16 g of weight row r of its
@@ -50,6 +50,7 @@ constexpr uint32_t kOutOfRange = 0x80000000u;
 constexpr int kPieceP = 512;              // activation elements per wave load pass
 constexpr int kPasses = 8;                // passes: K <= 4096
 constexpr int kScaleTiles = 4;            // weight-scale tiles per wave staged in LDS
+static_assert(kScaleTiles * 16 == 64, "one weight scale per thread");
 
 // Launch shape: NWV waves per workgroup, LD 16-byte weight loads per lane
 // per chunk.
@@ -60,8 +61,6 @@ struct Role {
     static constexpr int kElemBytes = FP8 ? 1 : 2;
     static constexpr int kPerLoad = FP8 ? 64 : 32;  // row elements per 64-byte load step
     static constexpr int kChunk = LD * kPerLoad;
-    static constexpr int kThreads = 64 * NWV;
-    static_assert(NWV * 64 == NWV * kScaleTiles * 16, "one weight scale per thread");
 };
 
 // LDS: M staged token rows of Kp bf16 values (stride 2 Kp + 16 bytes, so
@@ -194,9 +193,10 @@ __global__ __launch_bounds__(64 * NWV) void projection_kernel(
         }
     }
     __builtin_amdgcn_sched_barrier(0);
-    // Every step issues 8 loads and then 4 stores (out of range, and so
-    // dropped, unless a tile has just finished): the body is straight-line
-    // and the load counter waits stay exact, one chunk always in flight.
+    // Every step issues LD loads and then 8 stores (out of range, and so
+    // dropped, unless a tile pair has just finished): the body is
+    // straight-line and the load counter waits stay exact, one chunk always
+    // in flight.
     const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
         y, 0, M * ldy * 4, kRawBufferFlags);
     uint4 bA[LD], bB[LD];
