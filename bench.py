@@ -340,6 +340,76 @@ def kv_commit_bench(twd, torch, ls, reps, D=8, steps=64, c0=256, nseg=8, start=1
             "full_history_bytes": hist_bytes}
 
 
+def atlas_bench(twd, torch, dev_set, kernel, reps, D=8, c0=256, nseg=8, start=1000):
+    """The hot path as a finite set of captured graphs, one per (role,
+    width), all sharing the weights and the KV segments: a decode iteration
+    is the ternary sweep over every layer at width M, the output projection
+    in the iteration's role, and (when tokens are committed) the KV commit.
+    States: autoregressive (M = 1, critical projection, commit 1 row),
+    drafting (M = D + 1, fast projection, nothing committed) and
+    verification (M = D + 1, critical projection, commit 1 + a rows, a drawn
+    uniform{0..D}).  Each graph is replayed in turn; per-iteration times."""
+    ls = dev_set.ls
+    K, N = wl.HEAD_K, wl.HEAD_N
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(17)
+    w8 = torch.randint(0, 256, (N, K), dtype=torch.uint8, device="cuda", generator=gen)
+    w8[(w8 & 0x7F) == 0x7F] = 0x38
+    ws = torch.rand(N, device="cuda", generator=gen) * 1e-3
+    w16 = (torch.randn((N, K), device="cuda", generator=gen) * 0.02).to(torch.bfloat16)
+    layers, row_bytes = ls.layers, ls.projs[0].segs[1] * 2
+    segs = [torch.zeros(layers * 2 * cap * row_bytes, dtype=torch.uint8, device="cuda")
+            for cap in twd.kv_segment_positions(c0, nseg)]
+    W = D + 1
+    block = torch.randint(0, 256, (layers * 2 * W * row_bytes,), dtype=torch.uint8,
+                          device="cuda", generator=gen)
+    rng = np.random.default_rng(2028)
+    a = int(rng.integers(0, D + 1))
+    counts = torch.tensor([1, 1, 1 + a, a + 1], dtype=torch.int32, device="cuda")
+    state = torch.zeros((2, 4), dtype=torch.int32, device="cuda")
+    state[0] = torch.tensor([start + 1, start, 1, 0], dtype=torch.int32)
+    steps = {M: Step(twd, torch, dev_set, "2b_verify", M, kernel) for M in (1, W)}
+    heads = {M: torch.empty((M, N), dtype=torch.float32, device="cuda") for M in (1, W)}
+
+    def iteration(M, role, commit):
+        def run():
+            st = steps[M]
+            st.fused()
+            xh = st.x[(layers - 1, 0)]  # the last layer's hidden rows stand in
+            if role == "fast":
+                twd.projection_fp8(w8, ws, xh, y=heads[M])
+            else:
+                twd.projection_bf16(w16, xh, y=heads[M])
+            if commit:
+                i = 0 if M == 1 else 2
+                # two commits per graph keep the state on the first word
+                for j in range(2):
+                    twd.kv_commit(segs, c0, layers, row_bytes, block, W, counts[i:i + 1],
+                                  counts[i + 1:i + 2], state[j], state[1 - j])
+        return run
+
+    entries = {"autoregressive_m1": (1, "critical", True),
+               f"draft_m{W}": (W, "fast", False),
+               f"verify_m{W}": (W, "critical", True)}
+    graphs = {k: capture(torch, iteration(*v)) for k, v in entries.items()}
+    out = {"states": "autoregressive: M=1, critical projection, 2 commits of 1 row; drafting: "
+                     f"M={W}, fast projection; verification: M={W}, critical projection, "
+                     f"2 commits of {1 + a} rows",
+           "sweep_bytes": dev_set.bytes_per_sweep}
+    for k, g in graphs.items():
+        g.replay()
+        _, sec = time_replays(torch, g, reps)
+        out[k] = {"us_per_iteration": round(sec / reps * 1e6, 1)}
+    torch.cuda.synchronize()
+    fin = state[0].cpu().tolist()
+    if fin[3] != 0 or fin[0] != fin[1] + fin[2]:
+        raise SystemExit(f"atlas KV state {fin}")
+    out["final_kv_state"] = fin
+    del steps, heads, segs, w8, w16, graphs
+    torch.cuda.empty_cache()
+    return out
+
+
 def kernel_map(twd, ls, M, kernel, bf16_input=True):
     """Kernel family each projection of the set runs at width M, for bf16
     activations (one launch) or int8 ones (the linear of the two-launch
@@ -833,6 +903,8 @@ def main():
                     help="1: time each projection shape on its own, cold (default)")
     ap.add_argument("--projection-widths", default="1,4,8,16",
                     help="widths of the fast / critical output-projection table ('' skips it)")
+    ap.add_argument("--atlas", type=int, default=1,
+                    help="time the per-(role, width) iteration graphs (1) or not (0)")
     ap.add_argument("--kv-commit", type=int, default=1,
                     help="time the accepted-prefix KV commit (1) or not (0)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -951,6 +1023,7 @@ def main():
 
     proj_table = per_projection(twd, torch, ls, M, kernel, reps) if args.per_proj else None
     kvc = kv_commit_bench(twd, torch, ls, reps) if args.kv_commit else None
+    atlas = atlas_bench(twd, torch, dev_set, kernel, reps) if args.atlas else None
     head = None
     if args.projection_widths:
         head = output_projection_bench(
@@ -1007,6 +1080,7 @@ def main():
         "per_projection_cold": proj_table,
         "output_projection": head,
         "kv_commit": kvc,
+        "graph_atlas": atlas,
         "cpu_baseline": cpu,
         "cpu_single_thread": cpu1,
     }
