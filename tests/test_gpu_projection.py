@@ -174,3 +174,39 @@ def test_full_output_projection_sampled(env, M):
     check_bound(y.cpu().numpy()[:, rows], dot * s, absdot * s, K, f"fast full M={M}")
     dot, absdot = orc.bf16_linear(x, wb[rows])
     check_bound(yc.cpu().numpy()[:, rows], dot, absdot, K, f"critical full M={M}")
+
+
+def test_graph_replays_match_eager(env):
+    """Both roles captured into one graph: three replays, with eager work and
+    synchronization between them, each bit-identical to the eager results."""
+    torch, twd, orc = env
+    M, K, N = 5, 2560, 1000
+    W, _, x = wl.random_case(11, M, K, (N,), w_sigma=0.02)
+    wq, ws = orc.quantize_fp8_rows(W)
+    wq_d, ws_d = torch.from_numpy(wq).cuda(), torch.from_numpy(ws).cuda()
+    wb = dev_bf16(torch, wl.f32_to_bf16_bits(W))
+    xd = dev_bf16(torch, x)
+    y8 = torch.empty((M, N), device="cuda")
+    y16 = torch.empty((M, N), device="cuda")
+
+    def both():
+        twd.projection_fp8(wq_d, ws_d, xd, y=y8)
+        twd.projection_bf16(wb, xd, y=y16)
+
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        both()
+    torch.cuda.synchronize()
+    ref8, ref16 = y8.clone(), y16.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            both()
+    for rep in range(3):
+        y8.fill_(float("nan"))
+        y16.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y8.view(torch.int32), ref8.view(torch.int32)), f"fast replay {rep}"
+        assert torch.equal(y16.view(torch.int32), ref16.view(torch.int32)), f"critical replay {rep}"
+        _ = (y8.sum() + y16.sum()).item()  # eager work between replays
