@@ -819,6 +819,7 @@ def summarize_projection(args):
         rec["fast_fp8" if "true" in kname else "critical_bf16"] = {
             "hbm_bytes_per_launch": round(rd + wr), "algorithmic_bytes_per_launch": nbytes,
             "kernel_trace_avg_us": round(avg[kname] / 1e3, 3)}
+    os.makedirs(args.profile_out, exist_ok=True)
     with open(os.path.join(args.profile_out, "output_projection_counters_2b_m1.json"), "w") as f:
         json.dump(rec, f, indent=1)
     for g, d in sorted(reads.items()):
@@ -828,7 +829,6 @@ def summarize_projection(args):
                   f"average {a / 1e3:.2f} us over {len(d)} dispatches ({nbytes / a:.1f} GB/s)."]
     lines.append("")
     path = os.path.join(args.profile_out, "output_projection_2b_m1_trace_and_counters.md")
-    os.makedirs(args.profile_out, exist_ok=True)
     with open(path, "w") as f:
         f.write("\n".join(lines))
     print(path)

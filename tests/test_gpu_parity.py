@@ -132,6 +132,8 @@ SMALL_SHAPES = [
 # matrix-core kernel where its registers allow and KERNEL_MFMA_TILE the
 # tile-owner one for K <= 3072; both run the staged kernel otherwise
 FAMILIES = [("dot", 4), ("mfma", 16), ("mfma_staged", 16), ("mfma_tile", 16)]
+# every (family, width) pair a family takes
+FAMILY_WIDTHS = [(fam, M) for fam, max_m in FAMILIES for M in range(1, max_m + 1)]
 
 
 def family(twd, name):
@@ -141,11 +143,8 @@ def family(twd, name):
 
 @pytest.mark.parametrize("fused", [False, True], ids=["int8", "bf16"])
 @pytest.mark.parametrize("K,segs", SMALL_SHAPES)
-@pytest.mark.parametrize("M", list(range(1, 17)))
-@pytest.mark.parametrize("fam,max_m", FAMILIES)
-def test_kernel_parity(env, fam, max_m, M, K, segs, fused):
-    if M > max_m:
-        pytest.skip(f"{fam} takes M <= {max_m}")
+@pytest.mark.parametrize("fam,M", FAMILY_WIDTHS)
+def test_kernel_parity(env, fam, M, K, segs, fused):
     torch, twd, orc = env
     W, segs, x = wl.random_case(seed=1, M=M, K=K, seg_rows=segs)
     run_case(env, W, segs, x, family(twd, fam), ("rand", 1, K, segs), fused=fused)
@@ -365,12 +364,11 @@ def _random_shapes(seed=2024):
     return shapes
 
 
-@pytest.mark.parametrize("M,K,segs", _random_shapes())
-@pytest.mark.parametrize("fam,max_m", FAMILIES)
-def test_random_shapes(env, fam, max_m, M, K, segs):
+@pytest.mark.parametrize("fam,M,K,segs",
+                         [(fam, M, K, segs) for fam, max_m in FAMILIES
+                          for M, K, segs in _random_shapes() if M <= max_m])
+def test_random_shapes(env, fam, M, K, segs):
     """Random shapes through every family, both forms, against the oracle."""
-    if M > max_m:
-        pytest.skip(f"{fam} takes M <= {max_m}")
     torch, twd, orc = env
     W, segs, x = wl.random_case(seed=11, M=M, K=K, seg_rows=segs)
     ref = orc.forward(W, segs, x)
