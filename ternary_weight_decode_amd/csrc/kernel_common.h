@@ -12,6 +12,20 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kLoadsPerLane = 8;  // 16-byte weight loads in flight per lane
 
+// Cache policy of the weight-stream loads: non-temporal.  Each launch reads
+// its weights exactly once, so they are marked for early eviction instead
+// of pushing the code, kernel arguments and activations of the launches
+// that follow out of the caches.
+constexpr int kWeightPolicy = 2;  // the nt bit of a gfx950 buffer load
+
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+// A 16-byte weight load through a plain pointer, with the same policy.
+__device__ __forceinline__ uint4 load_weight16(const uint4 *p) {
+    const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kPlane0 = 0x03030303u;

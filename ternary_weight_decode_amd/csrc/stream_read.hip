@@ -1,6 +1,7 @@
 // Measurement references.  stream_read: the achievable-bandwidth reference,
-// a plain streaming read with the linear kernels' load shape (16-byte loads,
-// four in flight per lane, 256-thread workgroups); it reduces what it reads
+// a plain streaming read with the linear kernels' load shape and cache
+// policy (16-byte non-temporal loads, four in flight per lane, 256-thread
+// workgroups); it reduces what it reads
 // to one word and stores it only when it equals a guard value, so the loads
 // cannot be removed.  stream_copy: a plain copy of known size, the
 // calibration for the HBM byte counters (bytes read = bytes written = size).
@@ -12,6 +13,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kLoads = 4;
 
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
 __global__ __launch_bounds__(kThreads) void stream_read_kernel(
     const uint4 *__restrict__ p, int64_t n16, uint32_t *__restrict__ sink) {
     const int64_t base = static_cast<int64_t>(blockIdx.x) * kThreads * kLoads + threadIdx.x;
@@ -19,7 +22,12 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(
 #pragma unroll
     for (int u = 0; u < kLoads; ++u) {
         const int64_t i = base + static_cast<int64_t>(u) * kThreads;
-        v[u] = i < n16 ? p[i] : make_uint4(0u, 0u, 0u, 0u);
+        if (i < n16) {
+            const v4u w = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p + i));
+            v[u] = make_uint4(w[0], w[1], w[2], w[3]);
+        } else {
+            v[u] = make_uint4(0u, 0u, 0u, 0u);
+        }
     }
     uint32_t h = 0;
 #pragma unroll

@@ -133,7 +133,7 @@ __global__ __launch_bounds__(64 * NW) void mfma_kernel(
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const auto v = __builtin_amdgcn_raw_buffer_load_b128(
-            wr, wbase + 64u * static_cast<uint32_t>(wave + NW * u), 0, 0);
+            wr, wbase + 64u * static_cast<uint32_t>(wave + NW * u), 0, kWeightPolicy);
         a[u] = make_uint4(v[0], v[1], v[2], v[3]);
     }
     // keep every load issued before any use (the scheduler would otherwise

@@ -137,7 +137,7 @@ __global__ __launch_bounds__(64 * NW) void rows_kernel(
         const int col = 16 * (u * L + p);
         const uint32_t off = col < row_bytes ? static_cast<uint32_t>(r * row_bytes + col)
                                              : kOutOfRange;
-        const auto w = __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 0);
+        const auto w = __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, kWeightPolicy);
         a[u] = make_uint4(w[0], w[1], w[2], w[3]);
     }
     __builtin_amdgcn_sched_barrier(0);

@@ -182,7 +182,7 @@ __global__ __launch_bounds__(block_threads<M>()) void staged_kernel(
                 const int kcc = kc < CPR ? kc : 0;
 #pragma unroll
                 for (int t = 0; t < TW; ++t)
-                    a[u][t] = W[rowbase[t] + kcc];
+                    a[u][t] = load_weight16(W + rowbase[t] + kcc);
             }
         }
     };
