@@ -489,10 +489,13 @@ PROJECTION_SOURCES = ("kernel_common.h", "projection.hip")
 
 def kernel_source_hash(names=LINEAR_SOURCES):
     """Hash of the code (comments and blank space removed) of the given
-    kernel sources: counter records stay valid across comment edits and
-    lapse when the code changes."""
+    kernel sources and of the compile flags: counter records stay valid
+    across comment edits and lapse when the code or its build changes."""
     import re
+    from ternary_weight_decode_amd import build as twd_build
     h = hashlib.sha256()
+    flags = [f for f in twd_build.FLAGS if f != "-I" and not os.path.isabs(f)]
+    h.update(" ".join(flags).encode())
     csrc = os.path.join(ROOT, "ternary_weight_decode_amd", "csrc")
     for name in names:
         with open(os.path.join(csrc, name)) as f:

@@ -145,6 +145,15 @@ __device__ __forceinline__ uint32_t absmax_bits(u16x2 m) {
     return static_cast<uint32_t>(m.x > m.y ? m.x : m.y) << 16;
 }
 
+// Pin a value where it is computed.  Left alone, the compiler sinks values
+// that only the epilogue uses (kernel arguments, the scale division, the
+// segment scale) past the weight-load waits, onto the path that runs after
+// the last weight lands; an empty asm that reads and rewrites the value keeps
+// its computation here, in the shadow of the loads.
+__device__ __forceinline__ void settle_v(float &v) { asm volatile("" : "+v"(v)); }
+template <typename P>
+__device__ __forceinline__ void settle_s(P &p) { asm volatile("" : "+s"(p)); }
+
 __device__ __forceinline__ float row_gamma(const Segments &sg, int n) {
     float g = sg.gamma[0];
 #pragma unroll

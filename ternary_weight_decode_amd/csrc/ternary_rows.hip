@@ -80,8 +80,8 @@ __device__ __forceinline__ int group_sum(int v) {
 template <int M, int R, int NW, int U, bool FUSED>
 __global__ __launch_bounds__(64 * NW) void rows_kernel(
     const uint8_t *__restrict__ W, const void *__restrict__ act,
-    const float *__restrict__ xscale, int K, int N, Segments segs,
-    int32_t *__restrict__ acc, float *__restrict__ y) {
+    const float *__restrict__ xscale, int32_t *__restrict__ acc, float *__restrict__ y, int K,
+    int N, Segments segs) {
     constexpr int L = lanes_per_row<R>();
     constexpr int S = act_stride<R, U>();  // LDS row stride
     constexpr int SL = act_len<R, U>();    // staged elements per row
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(64 * NW) void rows_kernel(
     }
     __syncthreads();  // staged rows and row sums
     const int n = n_wave + r;
-    const float gam = row_gamma(segs, n);
+    float gam = row_gamma(segs, n);
     int qsum[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) {
@@ -218,6 +218,13 @@ __global__ __launch_bounds__(64 * NW) void rows_kernel(
         for (int w = 0; w < NW; ++w)
             qsum[m] += st_sum[w * M + m];
     }
+    settle_v(gam);
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+        settle_v(scale[m]);
+    settle_s(acc);
+    settle_s(y);
+    __builtin_amdgcn_sched_barrier(0);
 
     // 4. decode + dot, one load at a time as it arrives
     int tot[M];
@@ -266,8 +273,8 @@ __global__ __launch_bounds__(64 * NW) void rows_kernel(
     }
 }
 
-using Fn = void (*)(const uint8_t *, const void *, const float *, int, int, Segments,
-                    int32_t *, float *);
+using Fn = void (*)(const uint8_t *, const void *, const float *, int32_t *, float *, int, int,
+                    Segments);
 
 template <int M, int R, int NW, bool FUSED, int... Us>
 bool pick_u(int U, Fn *fn, int *lds) {
@@ -343,7 +350,7 @@ hipError_t launch_rows(const uint8_t *w, const void *act, bool fused, const floa
         return e;
     const int per_block = NW * R;
     hipLaunchKernelGGL(fn, dim3((N + per_block - 1) / per_block), dim3(64 * NW), lds, stream,
-                       w, act, xscale, K, N, segs, acc, y);
+                       w, act, xscale, acc, y, K, N, segs);
     return hipGetLastError();
 }
 
