@@ -151,6 +151,7 @@ __device__ __forceinline__ uint32_t absmax_bits(u16x2 m) {
 // the last weight lands; an empty asm that reads and rewrites the value keeps
 // its computation here, in the shadow of the loads.
 __device__ __forceinline__ void settle_v(float &v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void settle_v(int &v) { asm volatile("" : "+v"(v)); }
 template <typename P>
 __device__ __forceinline__ void settle_s(P &p) { asm volatile("" : "+s"(p)); }
 

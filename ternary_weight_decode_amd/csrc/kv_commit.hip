@@ -26,9 +26,9 @@ namespace {
 constexpr int kKvThreads = 256;
 
 __global__ __launch_bounds__(kKvThreads) void kv_commit_kernel(
-    KvSegments segs, int C0, int layers, int row16, const uint4 *__restrict__ block, int W,
-    const int32_t *__restrict__ n_mat_p, const int32_t *__restrict__ n_new_p,
-    const int32_t *__restrict__ state_in, int32_t *__restrict__ state_out) {
+    const uint4 *__restrict__ block, const int32_t *__restrict__ n_mat_p,
+    const int32_t *__restrict__ n_new_p, const int32_t *__restrict__ state_in,
+    int32_t *__restrict__ state_out, int C0, int row16, int W, KvSegments segs) {
     const int j = blockIdx.x;       // block row
     const int lk = blockIdx.y;      // layer * 2 + (K, V)
     const int P = state_in[0], L = state_in[1], S = state_in[2], err = state_in[3];
@@ -74,9 +74,9 @@ hipError_t launch_kv_commit(const KvSegments &segs, int C0, int layers, int row_
                             const void *block, int W, const int32_t *n_mat,
                             const int32_t *n_new, const int32_t *state_in, int32_t *state_out,
                             hipStream_t stream) {
-    hipLaunchKernelGGL(kv_commit_kernel, dim3(W, 2 * layers), dim3(kKvThreads), 0, stream, segs,
-                       C0, layers, row_bytes / 16, static_cast<const uint4 *>(block), W, n_mat,
-                       n_new, state_in, state_out);
+    hipLaunchKernelGGL(kv_commit_kernel, dim3(W, 2 * layers), dim3(kKvThreads), 0, stream,
+                       static_cast<const uint4 *>(block), n_mat, n_new, state_in, state_out, C0,
+                       row_bytes / 16, W, segs);
     return hipGetLastError();
 }
 

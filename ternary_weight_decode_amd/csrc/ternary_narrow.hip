@@ -60,13 +60,12 @@ __host__ __device__ constexpr int wave_bytes() { return M * row_stride<U>() + 64
 
 // LDS: per-wave regions | partials [M][17][wave] (16 rows, padded so that
 // the 16 token columns a write touches fall on different banks) | absmax
-// partials [wave, DPP row][M] | row-sum partials [wave, DPP row][M] |
-// scales [M].
+// partials [wave, DPP row][M] | row-sum partials [wave, DPP row][M].
 constexpr int kRedStride = 17;
 
 template <int M, int NW, int U>
 __host__ __device__ constexpr int lds_bytes() {
-    return NW * wave_bytes<M, U>() + M * kRedStride * NW * 4 + 2 * 4 * NW * M * 4 + M * 4;
+    return NW * wave_bytes<M, U>() + M * kRedStride * NW * 4 + 2 * 4 * NW * M * 4;
 }
 
 // Where lane l's activation word (elements 4l..4l+3 of the slice) is staged:
@@ -79,8 +78,8 @@ __device__ __forceinline__ int staged_word(int lane) {
 template <int M, int NW, int U, bool FUSED>
 __global__ __launch_bounds__(64 * NW) void mfma_kernel(
     const uint8_t *__restrict__ W, const void *__restrict__ act,
-    const float *__restrict__ xscale, int K, int N, Segments segs,
-    int32_t *__restrict__ acc, float *__restrict__ y) {
+    const float *__restrict__ xscale, int32_t *__restrict__ acc, float *__restrict__ y, int K,
+    int N, Segments segs) {
     constexpr int P = NW;  // partial sums per output
     extern __shared__ __align__(16) uint8_t smem[];
     const int tid = threadIdx.x;
@@ -95,7 +94,6 @@ __global__ __launch_bounds__(64 * NW) void mfma_kernel(
     int32_t *red = reinterpret_cast<int32_t *>(smem + NW * wave_bytes<M, U>());
     uint32_t *st_max = reinterpret_cast<uint32_t *>(red + M * kRedStride * P);  // [4 NW][M]
     int32_t *st_sum = reinterpret_cast<int32_t *>(st_max + 4 * NW * M);  // [4 NW][M]
-    float *st_scale = reinterpret_cast<float *>(st_sum + 4 * NW * M);    // [M]
     const int part = wave * 4 + (lane >> 4);  // this lane's DPP row in the workgroup
 
     // 1. activation loads: lane l takes elements 256 s + 4 l .. + 3 of each
@@ -140,8 +138,13 @@ __global__ __launch_bounds__(64 * NW) void mfma_kernel(
     // hoist activation math, and its wait, above the weight loads)
     __builtin_amdgcn_sched_barrier(0);
 
-    // 3. own activation slices -> LDS as int8, with this wave's row sums
+    // 3. own activation slices -> LDS as int8, with this wave's row sums;
+    //    the dequantization factors of this thread's output (step 5) are
+    //    settled here, in the shadow of the weight loads
     const int slot = 4 * staged_word(lane);
+    float scale_o = 0.0f;
+    if constexpr (!FUSED)
+        scale_o = xscale[min(tid >> 4, M - 1)];
     int sq[M];
 #pragma unroll
     for (int m = 0; m < M; ++m)
@@ -178,8 +181,11 @@ __global__ __launch_bounds__(64 * NW) void mfma_kernel(
         }
         const float a_l = __uint_as_float(am_l);
         const float inv_l = a_l > 0.0f ? 127.0f / a_l : 0.0f;
-        if (wave == 0 && lane < M)
-            st_scale[lane] = a_l / 127.0f;
+        // the scale of this thread's output row (step 5), from lane
+        // tid / 16 of this wave, which holds that row's absmax
+        const float a_o = __int_as_float(
+            __builtin_amdgcn_ds_bpermute(4 * ((tid >> 4) & 15), __float_as_int(a_l)));
+        scale_o = a_o / 127.0f;
 #pragma unroll
         for (int m = 0; m < M; ++m) {
             const float inv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(inv_l), m));
@@ -207,6 +213,13 @@ __global__ __launch_bounds__(64 * NW) void mfma_kernel(
         for (int m = 0; m < M; ++m)
             st_sum[part * M + m] = sq[m];
     }
+    const int n_o = n0 + (tid & 15);
+    float gam_o = row_gamma(segs, n_o);
+    settle_v(gam_o);
+    settle_v(scale_o);
+    settle_s(acc);
+    settle_s(y);
+    __builtin_amdgcn_sched_barrier(0);
     // the wave reads back only its own LDS region: its writes are ordered
     // before its reads, no workgroup barrier needed
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -252,31 +265,27 @@ __global__ __launch_bounds__(64 * NW) void mfma_kernel(
         }
     }
 
-    // 5. one thread per output adds its partials, takes off the row sum and
-    //    dequantizes
+    // 5. one thread per output (M * 16 <= 256 <= 64 NW) adds its partials,
+    //    takes off the row sum and dequantizes
     __syncthreads();
-    for (int idx = tid; idx < M * 16; idx += 64 * NW) {
-        const int m = idx >> 4;
-        const int n = n0 + (idx & 15);
-        if (n >= N)
-            continue;
+    if (tid < M * 16 && n_o < N) {
+        const int m = tid >> 4;
         int total = 0;
 #pragma unroll
         for (int p = 0; p < P; p += 4) {
-            const int4 v = *reinterpret_cast<const int4 *>(red + (m * kRedStride + (idx & 15)) * P + p);
+            const int4 v = *reinterpret_cast<const int4 *>(red + (m * kRedStride + (tid & 15)) * P + p);
             total += v.x + v.y + v.z + v.w;
         }
-        const float scale = FUSED ? st_scale[m] : xscale[m];
-        const int64_t o = static_cast<int64_t>(m) * N + n;
+        const int64_t o = static_cast<int64_t>(m) * N + n_o;
         if (acc)
             acc[o] = total;
         if (y)
-            y[o] = static_cast<float>(total) * scale * row_gamma(segs, n);
+            y[o] = static_cast<float>(total) * scale_o * gam_o;
     }
 }
 
-using Fn = void (*)(const uint8_t *, const void *, const float *, int, int, Segments,
-                    int32_t *, float *);
+using Fn = void (*)(const uint8_t *, const void *, const float *, int32_t *, float *, int, int,
+                    Segments);
 
 template <int M, int NW, bool FUSED, int... Us>
 bool pick_u(int U, Fn *fn, int *lds) {
@@ -344,7 +353,7 @@ hipError_t launch_narrow(const uint8_t *w, const void *act, bool fused,
     if (e != hipSuccess)
         return e;
     hipLaunchKernelGGL(fn, dim3((N + 15) / 16), dim3(64 * NW), lds, stream, w, act,
-                       xscale, K, N, segs, acc, y);
+                       xscale, acc, y, K, N, segs);
     return hipGetLastError();
 }
 

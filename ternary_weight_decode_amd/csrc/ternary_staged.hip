@@ -135,8 +135,8 @@ __device__ __forceinline__ void stage_rows(const void *__restrict__ act,
 template <int M, int TW, bool FUSED>
 __global__ __launch_bounds__(block_threads<M>()) void staged_kernel(
     const uint4 *__restrict__ W, const void *__restrict__ act,
-    const float *__restrict__ xscale, int K, int N, Segments segs,
-    int32_t *__restrict__ acc, float *__restrict__ y) {
+    const float *__restrict__ xscale, int32_t *__restrict__ acc, float *__restrict__ y, int K,
+    int N, Segments segs) {
     constexpr int UB = kLoadsPerLane / TW;  // super chunks per batch per wave
     constexpr int NS = staging_waves<M>();
     constexpr int NT = block_threads<M>();
@@ -271,8 +271,8 @@ __global__ __launch_bounds__(block_threads<M>()) void staged_kernel(
     }
 }
 
-using Fn = void (*)(const uint4 *, const void *, const float *, int, int, Segments,
-                    int32_t *, float *);
+using Fn = void (*)(const uint4 *, const void *, const float *, int32_t *, float *, int, int,
+                    Segments);
 
 template <int TW, bool FUSED, int... Ms>
 struct Table {
@@ -313,8 +313,8 @@ hipError_t launch_staged(int tiles, const uint8_t *w, const void *act, bool fuse
         return e;
     const int grid = (N + 16 * tiles - 1) / (16 * tiles);
     hipLaunchKernelGGL(fn, dim3(grid), dim3(threads), lds, stream,
-                       reinterpret_cast<const uint4 *>(w), act, xscale, K, N, segs,
-                       acc, y);
+                       reinterpret_cast<const uint4 *>(w), act, xscale, acc, y, K, N,
+                       segs);
     return hipGetLastError();
 }
 

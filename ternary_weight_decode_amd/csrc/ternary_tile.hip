@@ -63,8 +63,8 @@ __device__ __forceinline__ int permuted_word(int w) {
 template <int MB, int U, bool FUSED>
 __global__ __launch_bounds__(kThreads) void tile_kernel(
     const uint8_t *__restrict__ W, const void *__restrict__ act,
-    const float *__restrict__ xscale, int M, int K, int N, Segments segs,
-    int32_t *__restrict__ acc, float *__restrict__ y) {
+    const float *__restrict__ xscale, int32_t *__restrict__ acc, float *__restrict__ y, int M,
+    int K, int N, Segments segs) {
     constexpr int S = row_stride<U>();  // staged row stride
     constexpr int VW = stage_words<U>();
     extern __shared__ __align__(16) uint8_t smem[];
@@ -207,8 +207,15 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(
         scale = FUSED ? st_scale[r] : xscale[r];
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
         gam[i] = row_gamma(segs, n_t + 4 * g + i);
+        settle_v(gam[i]);
+    }
+    settle_v(qsum);
+    settle_v(scale);
+    settle_s(acc);
+    settle_s(y);
+    __builtin_amdgcn_sched_barrier(0);
 
     // 4. decode + MFMA, one slice at a time as its weights arrive
     v4i c0 = {0, 0, 0, 0}, c3 = c0, c4 = c0, c16 = c0;
@@ -252,8 +259,8 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(
     }
 }
 
-using Fn = void (*)(const uint8_t *, const void *, const float *, int, int, int, Segments,
-                    int32_t *, float *);
+using Fn = void (*)(const uint8_t *, const void *, const float *, int32_t *, float *, int, int,
+                    int, Segments);
 
 template <int MB, bool FUSED, int... Us>
 bool pick_u(int U, Fn *fn, int *lds) {
@@ -295,7 +302,7 @@ hipError_t launch_tile(const uint8_t *w, const void *act, bool fused, const floa
     if (e != hipSuccess)
         return e;
     hipLaunchKernelGGL(fn, dim3((N + 63) / 64), dim3(kThreads), lds, stream, w, act, xscale,
-                       M, K, N, segs, acc, y);
+                       acc, y, M, K, N, segs);
     return hipGetLastError();
 }
 
