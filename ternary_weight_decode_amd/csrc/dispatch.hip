@@ -6,7 +6,7 @@
 // int8 activations; from there the matrix cores win, since the VALU work
 // grows with M.  A wide output (at least ~200 workgroups of 64 rows) takes
 // the tile-owner kernel, which quantizes the activations once per 64 rows
-// instead of once per 16: from M = 3 with the quantization inside, from
+// instead of once per 16: from M = 2 with the quantization inside, from
 // M = 6 for int8 activations, where the straight-line kernel keeps the lead
 // a little longer.  Otherwise the straight-line MFMA kernel.  That kernel runs four waves per 16 rows while
 // each wave's activation slices fit in registers; past that it splits K over
@@ -26,7 +26,7 @@ LinearPlan plan_linear(int M, int K, int N, bool bf16_input, int forced_kernel) 
     if (k == TWD_KERNEL_AUTO) {
         if (M == 1 || (M == 2 && !bf16_input))
             k = TWD_KERNEL_DOT;
-        else if (M >= (bf16_input ? 3 : 6) && N / 64 >= 200 && tile_supported(M, K))
+        else if (M >= (bf16_input ? 2 : 6) && N / 64 >= 200 && tile_supported(M, K))
             k = TWD_KERNEL_MFMA_TILE;
         else if (bf16_input && narrow_waves(M, K) != 4)
             k = TWD_KERNEL_MFMA_STAGED;

@@ -137,6 +137,15 @@ __global__ __launch_bounds__(64 * NW) void mfma_kernel(
     // keep every load issued before any use (the scheduler would otherwise
     // hoist activation math, and its wait, above the weight loads)
     __builtin_amdgcn_sched_barrier(0);
+    // the segment scale of this thread's output (step 5) and the output
+    // pointers: their kernel-argument loads wait here, in the shadow of the
+    // activation loads
+    const int n_o = n0 + (tid & 15);
+    float gam_o = row_gamma(segs, n_o);
+    settle_v(gam_o);
+    settle_s(acc);
+    settle_s(y);
+    __builtin_amdgcn_sched_barrier(0);
 
     // 3. own activation slices -> LDS as int8, with this wave's row sums;
     //    the dequantization factors of this thread's output (step 5) are
@@ -213,12 +222,7 @@ __global__ __launch_bounds__(64 * NW) void mfma_kernel(
         for (int m = 0; m < M; ++m)
             st_sum[part * M + m] = sq[m];
     }
-    const int n_o = n0 + (tid & 15);
-    float gam_o = row_gamma(segs, n_o);
-    settle_v(gam_o);
     settle_v(scale_o);
-    settle_s(acc);
-    settle_s(y);
     __builtin_amdgcn_sched_barrier(0);
     // the wave reads back only its own LDS region: its writes are ordered
     // before its reads, no workgroup barrier needed

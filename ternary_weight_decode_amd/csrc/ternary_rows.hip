@@ -141,6 +141,14 @@ __global__ __launch_bounds__(64 * NW) void rows_kernel(
         a[u] = make_uint4(w[0], w[1], w[2], w[3]);
     }
     __builtin_amdgcn_sched_barrier(0);
+    // the segment scale of this lane's row and the output pointers: their
+    // kernel-argument loads wait here, in the shadow of the activation loads
+    const int n = n_wave + r;
+    float gam = row_gamma(segs, n);
+    settle_v(gam);
+    settle_s(acc);
+    settle_s(y);
+    __builtin_amdgcn_sched_barrier(0);
 
     // 3. stage the activation rows as int8 (with the row sums of q).
     //    Everything the epilogue needs besides the dot products -- scales,
@@ -208,8 +216,6 @@ __global__ __launch_bounds__(64 * NW) void rows_kernel(
             st_sum[wave * M + m] = s;
     }
     __syncthreads();  // staged rows and row sums
-    const int n = n_wave + r;
-    float gam = row_gamma(segs, n);
     int qsum[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) {
@@ -218,12 +224,9 @@ __global__ __launch_bounds__(64 * NW) void rows_kernel(
         for (int w = 0; w < NW; ++w)
             qsum[m] += st_sum[w * M + m];
     }
-    settle_v(gam);
 #pragma unroll
     for (int m = 0; m < M; ++m)
         settle_v(scale[m]);
-    settle_s(acc);
-    settle_s(y);
     __builtin_amdgcn_sched_barrier(0);
 
     // 4. decode + dot, one load at a time as it arrives

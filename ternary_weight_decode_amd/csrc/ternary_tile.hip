@@ -122,6 +122,18 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(
         a[u] = make_uint4(w[0], w[1], w[2], w[3]);
     }
     __builtin_amdgcn_sched_barrier(0);
+    // the segment scales of the lane's four rows and the output pointers:
+    // their kernel-argument loads wait here, in the shadow of the
+    // activation loads
+    float gam[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        gam[i] = row_gamma(segs, n_t + 4 * g + i);
+        settle_v(gam[i]);
+    }
+    settle_s(acc);
+    settle_s(y);
+    __builtin_amdgcn_sched_barrier(0);
 
     // 3. stage the M rows as int8 in the B layout, with the row sums of q
     if (tid < 16)
@@ -195,26 +207,18 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(
     }
     __syncthreads();  // staged rows, row sums
 
-    // the epilogue's other inputs (row sum of q and scale of token r, segment
-    // scales of the lane's four rows), settled while weights are in flight
+    // the epilogue's other inputs (row sum of q and scale of token r),
+    // settled while weights are in flight
     int qsum = 0;
     float scale = 0.0f;
-    float gam[4];
     if (r < M) {
 #pragma unroll
         for (int i = 0; i < 4 * kWaves; ++i)
             qsum += st_sum[i * MB + r];
         scale = FUSED ? st_scale[r] : xscale[r];
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        gam[i] = row_gamma(segs, n_t + 4 * g + i);
-        settle_v(gam[i]);
-    }
     settle_v(qsum);
     settle_v(scale);
-    settle_s(acc);
-    settle_s(y);
     __builtin_amdgcn_sched_barrier(0);
 
     // 4. decode + MFMA, one slice at a time as its weights arrive

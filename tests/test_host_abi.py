@@ -174,7 +174,7 @@ def test_select_kernel(twd):
         assert twd.select_kernel(1, 2560, 2560, bf16) == twd.KERNEL_DOT
         assert twd.select_kernel(16, 1024, 2560, bf16) == twd.KERNEL_MFMA
         assert twd.select_kernel(16, 2560, 2560, bf16) == twd.KERNEL_MFMA
-        # wide outputs take the tile-owner kernel (K <= 3072): from M = 3
+        # wide outputs take the tile-owner kernel (K <= 3072): from M = 2
         # with the bf16 quantization inside, from M = 6 for int8 activations
         assert twd.select_kernel(3, 2560, 13824, bf16) == (
             twd.KERNEL_MFMA_TILE if bf16 else twd.KERNEL_MFMA)
@@ -182,11 +182,13 @@ def test_select_kernel(twd):
             twd.KERNEL_MFMA_TILE if bf16 else twd.KERNEL_MFMA)
         assert twd.select_kernel(6, 2560, 13824, bf16) == twd.KERNEL_MFMA_TILE
         assert twd.select_kernel(4, 8192, 2560, bf16) == twd.KERNEL_MFMA
-        # M = 2: matrix cores with the quantization inside, the dot kernel
-        # for int8 activations
-        for N in (2560, 13824):
-            assert twd.select_kernel(2, 2560, N, bf16) == (
-                twd.KERNEL_MFMA if bf16 else twd.KERNEL_DOT)
+        # M = 2: the tile kernel for a wide output and the straight-line one
+        # otherwise with the quantization inside, the dot kernel for int8
+        # activations
+        assert twd.select_kernel(2, 2560, 13824, bf16) == (
+            twd.KERNEL_MFMA_TILE if bf16 else twd.KERNEL_DOT)
+        assert twd.select_kernel(2, 2560, 2560, bf16) == (
+            twd.KERNEL_MFMA if bf16 else twd.KERNEL_DOT)
         # a long K past four waves' register budget: int8 activations split
         # K over more waves of the straight-line kernel; with the bf16
         # quantization inside, the staged kernel is faster
