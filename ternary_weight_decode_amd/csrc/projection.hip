@@ -25,15 +25,25 @@
 // ones by up to ~1e-4 of the sum of |products|, more than fp32 accumulation
 // of the same products allows.
 //
-// Layout.  In load j of chunk c, lane l (row r = l % 16, K group g = l / 16)
-// reads the 16 bytes at byte (8 c + j) 64 + 16 g of weight row r of its
-// tile: one load covers 64 contiguous bytes of each of 16 rows.  As an MFMA
-// B operand the lane's bf16 values are elements e0 .. e0 + 7 (+ 8 .. 15 for
-// FP8 codes, a second MFMA) of weight column r; the A operand of token row
-// r reads the same elements of staged token row r, so the contraction
-// covers every k exactly once, and lane (g, r) ends with tokens 4g .. 4g+3
-// of weight row r.  Loads past the row end or past N fall outside the
-// buffer descriptor and return zeros; token rows past M read a zero block.
+// Layout.  As an MFMA B operand, lane l (row r = l % 16, K group g = l / 16)
+// needs, for step j of chunk c, the 16 bytes at byte (8 c + j) 64 + 16 g of
+// weight row r of its tile: 64 bytes of each of 16 rows per step.  Loaded
+// that way, every 128-byte line is split over two loads, which streams
+// markedly slower (and far slower still with non-temporal loads) than whole
+// lines.  So steps j and j + 1 (j even) load the 128-byte segment s = 4 c +
+// j / 2 of all 16 rows as two whole-line loads: X covers rows 0-7, Y rows
+// 8-15, 16-byte piece p of the segment of row q going to
+//     X: lane (g, r) <- row r % 8,     piece g + 4 (r / 8)
+//     Y: lane (g, r) <- row 8 + r % 8, piece g + 4 (1 - r / 8).
+// Then step j's operand is X where r < 8 and Y elsewhere -- row r, piece g,
+// already in place -- and step j + 1's is the other of the two rotated by 8
+// lanes within each 16-lane row (one DPP move): row r, piece g + 4.  The
+// lane's bf16 values are elements e0 .. e0 + 7 (+ 8 .. 15 for FP8 codes, a
+// second MFMA) of weight column r; the A operand of token row r reads the
+// same elements of staged token row r, so the contraction covers every k
+// exactly once, and lane (g, r) ends with tokens 4g .. 4g+3 of weight row r.
+// Loads past the row end or past N fall outside the buffer descriptor and
+// return zeros; token rows past M read a zero block.
 #include "kernel_common.h"
 
 namespace twd {
@@ -89,27 +99,43 @@ __device__ __forceinline__ v8bf as_bf16x8(uint32_t a, uint32_t b, uint32_t c, ui
 template <int LD>
 __device__ __forceinline__ void load_chunk(uint4 (&buf)[LD], const uint8_t *W, int tile,
                                            int tile_end, int N, int row_bytes, int c, int r, int g) {
+    static_assert(LD % 2 == 0, "loads come in X, Y pairs");
     // tiles at or past tile_end (this wave's range) load nothing
     const int n0 = tile * 16;
     const int rows = tile < tile_end ? min(16, N - n0) : 0;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t *>(W + static_cast<int64_t>(tile < tile_end ? n0 : 0) * row_bytes), 0,
         __builtin_amdgcn_readfirstlane(rows * row_bytes), kRawBufferFlags);
+    const int hi = r >> 3;
 #pragma unroll
     for (int j = 0; j < LD; ++j) {
-        const int col = (c * LD + j) * 64 + 16 * g;
-        const uint32_t off = col < row_bytes ? static_cast<uint32_t>(r * row_bytes + col) : kOutOfRange;
-        // default cache policy: marked non-temporal, these loads (each
-        // 128-byte line of a row is read by two of them, 64 bytes each)
-        // measured about 20% slower over the whole projection
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+        const int seg = (c * LD + j) >> 1;
+        const int row = (j & 1) ? 8 + (r & 7) : (r & 7);
+        const int piece = g + 4 * ((j & 1) ? hi ^ 1 : hi);
+        const int col = seg * 128 + 16 * piece;
+        const uint32_t off = col < row_bytes ? static_cast<uint32_t>(row * row_bytes + col) : kOutOfRange;
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kWeightPolicy);
         buf[j] = make_uint4(v[0], v[1], v[2], v[3]);
     }
 }
 
+// The X, Y pair of loads j, j + 1 -> the operands of steps j and j + 1.
+__device__ __forceinline__ uint32_t ror8(uint32_t v) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x128, 0xf, 0xf, false));
+}
+__device__ __forceinline__ void unpair(uint4 &x, uint4 &y, bool lo) {
+    const uint4 t0 = lo ? x : y;
+    const uint4 z = lo ? y : x;
+    x = t0;
+    y = make_uint4(ror8(z.x), ror8(z.y), ror8(z.z), ror8(z.w));
+}
+
 template <bool FP8, int LD>
-__device__ __forceinline__ v4f compute_chunk(const uint4 (&buf)[LD], v4f acc, const uint8_t *bsrc,
-                                             int estep, int c, int g) {
+__device__ __forceinline__ v4f compute_chunk(uint4 (&buf)[LD], v4f acc, const uint8_t *bsrc,
+                                             int estep, int c, int g, bool lo) {
+#pragma unroll
+    for (int j = 0; j < LD; j += 2)
+        unpair(buf[j], buf[j + 1], lo);
 #pragma unroll
     for (int j = 0; j < LD; ++j) {
         const uint4 w = buf[j];
@@ -315,7 +341,7 @@ __global__ __launch_bounds__(64 * NWV) void projection_kernel(
     int t_cp = first, c_cp = 0, ord = 0;  // item being computed, its tile ordinal
     v4f acc = zero4, held = zero4;
     auto step = [&](uint4 (&buf)[LD]) {
-        acc = compute_chunk<FP8, LD>(buf, acc, bsrc, estep, c_cp, g);
+        acc = compute_chunk<FP8, LD>(buf, acc, bsrc, estep, c_cp, g, r < 8);
         next_load(buf);
         v4f v = acc;
         if constexpr (FP8) {
