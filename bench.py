@@ -520,6 +520,24 @@ def counter_traffic(workload, M, launches_bytes):
     return rec.get("hbm_bytes_per_launch")
 
 
+def host_cpu():
+    """The host CPU model and the logical CPUs this process may use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        visible = len(os.sched_getaffinity(0))
+    except AttributeError:
+        visible = os.cpu_count() or 1
+    return f"{model}; {visible} logical CPUs visible to the process"
+
+
 def cpu_baseline(ls, workload, M, outliers, budget_s, threads=None):
     """The CPU oracle (quantize, int8 x ternary loops, dequant) over the
     layers of the set in order, repeating whole passes until its compute time
@@ -558,7 +576,7 @@ def cpu_baseline(ls, workload, M, outliers, budget_s, threads=None):
             run(item)
         passes += 1
     return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "host": host_cpu(),
             "sample": f"{passes} pass(es) over all {ls.layers} layers of the {ls.name.upper()} set "
                       f"at M={M} (4 projections each: quantize + int32 contraction + dequant; "
                       f"{spent:.1f} s of CPU time; throughput in packed-weight bytes/s)"}
