@@ -310,16 +310,21 @@ bool pick_u(int U, Fn *fn, int *lds) {
     return found;
 }
 
+// One instance per width: the kernel stages and quantizes exactly M token
+// rows (a rounded-up block would spend VALU time on zero rows, and with one
+// wave per SIMD that time is on the critical path).
+template <bool FUSED, int... Ms>
+bool pick_m(int M, int U, Fn *fn, int *lds) {
+    bool found = false;
+    ((M == Ms ? (found = pick_u<Ms, FUSED, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12>(U, fn, lds))
+              : false),
+     ...);
+    return found;
+}
+
 template <bool FUSED>
 bool pick(int M, int U, Fn *fn, int *lds) {
-    // token blocks of 4: a launch at width M runs the block M rounds up to
-    if (M <= 4)
-        return pick_u<4, FUSED, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12>(U, fn, lds);
-    if (M <= 8)
-        return pick_u<8, FUSED, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12>(U, fn, lds);
-    if (M <= 12)
-        return pick_u<12, FUSED, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12>(U, fn, lds);
-    return pick_u<16, FUSED, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12>(U, fn, lds);
+    return pick_m<FUSED, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>(M, U, fn, lds);
 }
 
 }  // namespace
