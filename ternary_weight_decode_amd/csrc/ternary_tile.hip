@@ -95,18 +95,27 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(
 
     // 1. activation loads: thread t takes words t, t + 256, ... of each of
     //    the M rows (zeros past K; rows past M are never read)
+    //    Each token row has a descriptor of its own (scalar work), so one
+    //    vector offset per word serves every row and the range check ends
+    //    each row at K.
     constexpr int kEl = FUSED ? 2 : 1;
-    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<void *>(act), 0, M * K * kEl, kRawBufferFlags);
+    const int xrow = K * kEl;
+    const uint8_t *xbase = static_cast<const uint8_t *>(act);
+    uint32_t xoff[VW];
+#pragma unroll
+    for (int v = 0; v < VW; ++v) {
+        const int k0 = 4 * (tid + kThreads * v);
+        xoff[v] = k0 < K ? static_cast<uint32_t>(k0 * kEl) : kOutOfRange;
+    }
     uint2 xb[FUSED ? MB : 1][VW];
     uint32_t xi[FUSED ? 1 : MB][VW];
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
+        const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t *>(xbase + m * xrow), 0, xrow, kRawBufferFlags);
 #pragma unroll
         for (int v = 0; v < VW; ++v) {
-            const int k0 = 4 * (tid + kThreads * v);
-            const uint32_t off = (m < M && k0 < K) ? static_cast<uint32_t>((m * K + k0) * kEl)
-                                                   : kOutOfRange;
+            const uint32_t off = xoff[v];
             if constexpr (FUSED) {
                 const auto x = __builtin_amdgcn_raw_buffer_load_b64(xr, off, 0, 0);
                 xb[m][v] = make_uint2(x[0], x[1]);
@@ -233,7 +242,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(
     // settled while weights are in flight
     int qsum = 0;
     float scale = 0.0f;
-    if (r < M) {
+    if (r < MB) {
 #pragma unroll
         for (int i = 0; i < 4 * kWaves; ++i)
             qsum += st_sum[i * MB + r];
@@ -245,8 +254,8 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(
 
     // 4. decode + MFMA, one slice at a time as its weights arrive
     v4i c0 = {0, 0, 0, 0}, c3 = c0, c4 = c0, c16 = c0;
-    const uint8_t *bsrc = r < M ? xs + r * S + 64 * g : zero;
-    const int ustep = r < M ? 256 : 0;
+    const uint8_t *bsrc = r < MB ? xs + r * S + 64 * g : zero;
+    const int ustep = r < MB ? 256 : 0;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const uint8_t *bu = bsrc + u * ustep;
@@ -281,7 +290,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(
 
     // 5. lane (token r, group g) holds rows 4g .. 4g+3 of the tile for token
     //    r: take off the row sum, dequantize, store
-    if (r < M) {
+    if (r < MB) {
         const v4i c = c0 + c3 + (c4 >> 2) + (c16 >> 4);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
