@@ -6,9 +6,9 @@
 // int8 activations; from there the matrix cores win, since the VALU work
 // grows with M.  A wide output (at least ~200 workgroups of 64 rows) takes
 // the tile-owner kernel, which quantizes the activations once per 64 rows
-// instead of once per 16: from M = 2 with the quantization inside, from
-// M = 6 for int8 activations, where the straight-line kernel keeps the lead
-// a little longer.  Otherwise the straight-line MFMA kernel.  That kernel runs four waves per 16 rows while
+// instead of once per 16 and loads whole 128-byte lines: from M = 2 with
+// the quantization inside, from M = 3 for int8 activations (at M = 2 the dot
+// kernel leads there).  Otherwise the straight-line MFMA kernel.  That kernel runs four waves per 16 rows while
 // each wave's activation slices fit in registers; past that it splits K over
 // 8 or 16 waves, which beats the staged kernel on int8 activations but not
 // with the bf16 quantization inside (every one of the extra waves repeats
@@ -26,7 +26,7 @@ LinearPlan plan_linear(int M, int K, int N, bool bf16_input, int forced_kernel) 
     if (k == TWD_KERNEL_AUTO) {
         if (M == 1 || (M == 2 && !bf16_input))
             k = TWD_KERNEL_DOT;
-        else if (M >= (bf16_input ? 2 : 6) && N / 64 >= 200 && tile_supported(M, K))
+        else if (M >= (bf16_input ? 2 : 3) && N / 64 >= 200 && tile_supported(M, K))
             k = TWD_KERNEL_MFMA_TILE;
         else if (bf16_input && narrow_waves(M, K) != 4)
             k = TWD_KERNEL_MFMA_STAGED;

@@ -175,12 +175,9 @@ def test_select_kernel(twd):
         assert twd.select_kernel(16, 1024, 2560, bf16) == twd.KERNEL_MFMA
         assert twd.select_kernel(16, 2560, 2560, bf16) == twd.KERNEL_MFMA
         # wide outputs take the tile-owner kernel (K <= 3072): from M = 2
-        # with the bf16 quantization inside, from M = 6 for int8 activations
-        assert twd.select_kernel(3, 2560, 13824, bf16) == (
-            twd.KERNEL_MFMA_TILE if bf16 else twd.KERNEL_MFMA)
-        assert twd.select_kernel(5, 2560, 13824, bf16) == (
-            twd.KERNEL_MFMA_TILE if bf16 else twd.KERNEL_MFMA)
-        assert twd.select_kernel(6, 2560, 13824, bf16) == twd.KERNEL_MFMA_TILE
+        # with the bf16 quantization inside, from M = 3 for int8 activations
+        for M in (3, 5, 6, 16):
+            assert twd.select_kernel(M, 2560, 13824, bf16) == twd.KERNEL_MFMA_TILE
         assert twd.select_kernel(4, 8192, 2560, bf16) == twd.KERNEL_MFMA
         # M = 2: the tile kernel for a wide output and the straight-line one
         # otherwise with the quantization inside, the dot kernel for int8
