@@ -509,8 +509,13 @@ def kernel_source_hash(names=LINEAR_SOURCES):
 
 def counter_traffic(workload, M, launches_bytes):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
-    it was taken on the current kernel sources; else None."""
+    it was taken on the current kernel sources; else None.  On the 2B layer
+    set the decode (M = 1) and verification (M > 1) workloads launch the same
+    kernels over the same weights, so either record serves a width."""
     path = os.path.join(PROFILES, f"ternary_linear_counters_{workload}_m{M}.json")
+    if not os.path.exists(path) and workload in ("2b_decode", "2b_verify"):
+        other = "2b_verify" if M > 1 else "2b_decode"
+        path = os.path.join(PROFILES, f"ternary_linear_counters_{other}_m{M}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -1031,6 +1036,7 @@ def main():
         for Mw in [int(v) for v in args.widths.split(",") if v]:
             if Mw == M:
                 widths[str(Mw)] = {"gbs": round(lin_gbs, 1), "frac": round(lin_gbs / HBM_PEAK_GBS, 4),
+                                   "traffic": traffic,
                                    "us_per_launch": round(lin_dur * 1e6, 3),
                                    "two_launch_gbs": round(bytes_step * reps / two_wall / 1e9, 1),
                                    "kernels": kname,
@@ -1046,6 +1052,7 @@ def main():
             g2.replay()
             _, sec2 = time_replays(torch, g2, reps)
             widths[str(Mw)] = {"gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                               "traffic": counter_traffic(args.workload, Mw, bytes_step / nlaunch),
                                "us_per_launch": round(sec / (reps * nlaunch) * 1e6, 3),
                                "two_launch_gbs": round(bytes_step * reps / sec2 / 1e9, 1),
                                "kernels": kernel_map(twd, ls, Mw, kernel),
