@@ -278,10 +278,13 @@ def test_extreme_values(env):
 @pytest.mark.parametrize("set_name,workload,layer,M", [
     ("2b", "2b_decode", 0, 1),
     ("2b", "2b_decode", 29, 1),
+    ("2b", "2b_verify", 11, 2),
+    ("2b", "2b_verify", 19, 3),
     ("2b", "2b_verify", 7, 4),
     ("2b", "2b_verify", 7, 8),
     ("2b", "2b_sweep_outlier", 3, 13),
     ("4b", "4b_stack", 35, 1),
+    ("4b", "4b_stack", 17, 4),
     ("4b", "4b_stack", 0, 16),
 ])
 def test_full_size_layer(env, set_name, workload, layer, M):
