@@ -229,17 +229,16 @@ __global__ __launch_bounds__(64 * NW) void rows_kernel(
         settle_v(scale[m]);
     __builtin_amdgcn_sched_barrier(0);
 
-    // 4. decode + dot, one load at a time as it arrives
-    int tot[M];
+    // 4. decode + dot, one load at a time as it arrives.  The x1, x4 and
+    //    x16 sums run over all loads and are combined once: every term of
+    //    d4 (d16) is a multiple of 4 (16), so the shifts are exact, and
+    //    |d16| <= 16 * 2 * 127 * K / 4 < 2^31 for K <= 8192.
+    int d1[M], d4[M], d16[M];
 #pragma unroll
     for (int m = 0; m < M; ++m)
-        tot[m] = 0;
+        d1[m] = d4[m] = d16[m] = 0;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        int d1[M], d4[M], d16[M];
-#pragma unroll
-        for (int m = 0; m < M; ++m)
-            d1[m] = d4[m] = d16[m] = 0;
         const int kb = act_off(64 * (u * L + p));  // first element of this chunk
 #pragma unroll
         for (int dw = 0; dw < 4; ++dw) {
@@ -257,10 +256,11 @@ __global__ __launch_bounds__(64 * NW) void rows_kernel(
                 d1[m] = sdot4(p3, x.w, d1[m]);
             }
         }
-#pragma unroll
-        for (int m = 0; m < M; ++m)
-            tot[m] += d1[m] + (d4[m] >> 2) + (d16[m] >> 4);
     }
+    int tot[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+        tot[m] = d1[m] + (d4[m] >> 2) + (d16[m] >> 4);
 
     // 5. row totals across the row group; its last lane writes the outputs
 #pragma unroll
