@@ -108,13 +108,16 @@ __global__ __launch_bounds__(64 * NW) void rows_kernel(
         const_cast<void *>(act), 0, M * K * kEl, kRawBufferFlags);
     uint2 xb[FUSED ? M : 1][V];
     uint32_t xi[FUSED ? 1 : M][V];
+    //    (U = ceil(K / (64 L)) puts every word of the first V - 1 rounds
+    //    below K: only the last round needs the range test)
 #pragma unroll
     for (int v = 0; v < V; ++v) {
         const int k0 = 4 * (tid + T * v);
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-            const uint32_t off =
-                k0 < K ? static_cast<uint32_t>((m * K + k0) * kEl) : kOutOfRange;
+            const uint32_t off = (v < V - 1 || k0 < K)
+                                     ? static_cast<uint32_t>((m * K + k0) * kEl)
+                                     : kOutOfRange;
             if constexpr (FUSED) {
                 const auto x = __builtin_amdgcn_raw_buffer_load_b64(xr, off, 0, 0);
                 xb[m][v] = make_uint2(x[0], x[1]);
@@ -131,12 +134,14 @@ __global__ __launch_bounds__(64 * NW) void rows_kernel(
     const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t *>(W + static_cast<int64_t>(min(n_wave, N - 1)) * row_bytes), 0,
         wbytes, kRawBufferFlags);
+    //    (likewise only the last load can pass the row end)
     uint4 a[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int col = 16 * (u * L + p);
-        const uint32_t off = col < row_bytes ? static_cast<uint32_t>(r * row_bytes + col)
-                                             : kOutOfRange;
+        const uint32_t off = (u < U - 1 || col < row_bytes)
+                                 ? static_cast<uint32_t>(r * row_bytes + col)
+                                 : kOutOfRange;
         const auto w = __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, kWeightPolicy);
         a[u] = make_uint4(w[0], w[1], w[2], w[3]);
     }
