@@ -635,8 +635,25 @@ def grid(r):
     return int(_col(r, "Grid_Size", "Grid_Size_X", "grid_size"))
 
 
+def _run_source_hash(path, key="kernel_source_hash"):
+    """A kernel-source hash that a bench.py run printed in its JSON line."""
+    if not path or not os.path.exists(path):
+        return None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("{"):
+                return json.loads(line).get(key)
+    return None
+
+
 def summarize_profiles(args):
     trace_dir, fetch_dir, write_dir = args.summarize_profile
+    # a counter record is stamped with the sources the profiled run was built
+    # from; summarizing a run of other sources would mislabel it
+    ran = _run_source_hash(args.profile_run_json)
+    if ran is not None and ran != kernel_source_hash():
+        raise SystemExit(f"the profiled run used kernel sources {ran}, not the current "
+                         f"{kernel_source_hash()}: profile the current sources again")
     cmds = args.profile_commands or ("?", "?", "?")
     ls = wl.LAYER_SETS["4b" if args.workload.startswith("4b") else "2b"]
     M = args.M or wl.workload_widths(args.workload)[0]
@@ -790,6 +807,10 @@ def summarize_projection(args):
     from three rocprofv3 runs of this script with --projection-widths 1
     (trace, FETCH_SIZE, WRITE_SIZE; the counter runs add --copy-calibration)."""
     trace_dir, fetch_dir, write_dir = args.summarize_projection
+    ran = _run_source_hash(args.profile_run_json, "projection_source_hash")
+    if ran is not None and ran != kernel_source_hash(PROJECTION_SOURCES):
+        raise SystemExit(f"the profiled run used projection sources {ran}, not the current "
+                         f"{kernel_source_hash(PROJECTION_SOURCES)}: profile them again")
     cmds = args.profile_commands or ("?", "?", "?")
     K, N = wl.HEAD_K, wl.HEAD_N
     roles = (("projection_kernel<true", "fast (E4M3 weights)", N * K),
@@ -1122,6 +1143,8 @@ def main():
         "graph_atlas": atlas,
         "cpu_baseline": cpu,
         "cpu_single_thread": cpu1,
+        "kernel_source_hash": kernel_source_hash(),
+        "projection_source_hash": kernel_source_hash(PROJECTION_SOURCES),
     }
     if calib:
         out["copy_calibration_bytes"] = calib

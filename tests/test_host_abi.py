@@ -287,3 +287,22 @@ def test_kv_commit_rejects_before_launch(twd):
     nul = (ctypes.c_void_p * 4)(0x10000, None, 0x30000, 0x40000)
     assert call(seg=nul) == 1
     assert twd._lib_last_error()
+
+
+def test_profile_summary_refuses_runs_of_other_sources(tmp_path):
+    """A counter record is stamped with the kernel-source hash of the run it
+    summarizes: a run that printed another hash is refused, so stale counters
+    can never carry the current sources' hash."""
+    import json
+    import subprocess
+    import sys
+    run = tmp_path / "run.json"
+    run.write_text(json.dumps({"kernel_source_hash": "0" * 16,
+                               "projection_source_hash": "0" * 16}) + "\n")
+    d = str(tmp_path)
+    for flag in ("--summarize-profile", "--summarize-projection"):
+        r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), flag, d, d, d,
+                            "--profile-run-json", str(run), "--profile-out", d],
+                           capture_output=True, text=True, cwd=ROOT)
+        assert r.returncode != 0 and "profile" in r.stderr
+        assert not any(p.suffix == ".json" and p.name != "run.json" for p in tmp_path.iterdir())
