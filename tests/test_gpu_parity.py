@@ -302,6 +302,69 @@ def test_full_size_layer(env, set_name, workload, layer, M):
                  fused=True)
 
 
+# ------------------------------------------------------------ graph replay
+
+def test_linear_graph_replays_match_eager(env):
+    """Every linear kernel family, in the one-launch bf16 form and in the
+    two-launch form (quantize_act, then the int8 linear), captured into one
+    graph: three replays, with eager work and synchronization between them,
+    each bit-identical to the eager results (quantized activations and
+    scales included)."""
+    torch, twd, orc = env
+    cases = [("dot", 1, 2560, (96,)), ("dot", 3, 768, (40, 24)),
+             ("mfma", 2, 2560, (64, 32, 32)), ("mfma", 9, 6912, (33,)),
+             ("mfma_tile", 5, 1536, (130,)), ("mfma_staged", 16, 8192, (20,))]
+    runs = []
+    for i, (fam, M, K, segs) in enumerate(cases):
+        W, segs, x = wl.random_case(seed=40 + i, M=M, K=K, seg_rows=segs)
+        packed, gammas = twd.prepare_weights(W, segs)
+        N = int(sum(segs))
+        runs.append(dict(
+            fam=family(twd, fam), segs=segs, gammas=gammas,
+            wp=torch.from_numpy(packed).cuda(), x=to_dev_bf16(torch, x),
+            acc_f=torch.empty((M, N), dtype=torch.int32, device="cuda"),
+            y_f=torch.empty((M, N), device="cuda"),
+            xq=torch.empty((M, K), dtype=torch.int8, device="cuda"),
+            xs=torch.empty(M, device="cuda"),
+            acc_i=torch.empty((M, N), dtype=torch.int32, device="cuda"),
+            y_i=torch.empty((M, N), device="cuda")))
+    outs = ("acc_f", "y_f", "xq", "xs", "acc_i", "y_i")
+
+    def all_cases():
+        for r in runs:
+            twd.ternary_linear_bf16(r["wp"], r["segs"], r["gammas"], r["x"], acc=r["acc_f"],
+                                    y=r["y_f"], kernel=r["fam"])
+            twd.quantize_act(r["x"], xq=r["xq"], xscale=r["xs"])
+            twd.ternary_linear_fused(r["wp"], r["segs"], r["gammas"], r["xq"], r["xs"],
+                                     acc=r["acc_i"], y=r["y_i"], kernel=r["fam"])
+
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        all_cases()
+    torch.cuda.synchronize()
+    refs = [{k: r[k].clone() for k in outs} for r in runs]
+    for r, ref in zip(runs, refs):  # the two forms agree with each other
+        assert torch.equal(ref["acc_f"], ref["acc_i"])
+        assert torch.equal(ref["y_f"].view(torch.int32), ref["y_i"].view(torch.int32))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            all_cases()
+    for rep in range(3):
+        for r in runs:
+            for k in outs:
+                r[k].fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (r, ref) in enumerate(zip(runs, refs)):
+            for k in outs:
+                a, b = r[k], ref[k]
+                if a.dtype == torch.float32:
+                    a, b = a.view(torch.int32), b.view(torch.int32)
+                assert torch.equal(a, b), f"replay {rep}, case {cases[i]}, {k}"
+        _ = sum(float(r["y_f"].sum()) for r in runs)  # eager work between replays
+
+
 # ------------------------------------------------------------- error paths
 
 def test_fused_errors_on_gpu(env):
