@@ -146,6 +146,17 @@ def time_replays(torch, g, reps):
     return t1 - t0, start.elapsed_time(end) * 1e-3
 
 
+def time_eager(torch, fn, reps):
+    """Wall seconds for `reps` eager calls of fn (no graph), synchronized on
+    both sides."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        fn()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
 def stream_read_reference(twd, torch, dev_set, reps):
     """The plain streaming-read kernel over each projection's weight buffer,
     launched back to back in the same order as the linear sweep."""
@@ -1047,6 +1058,8 @@ def main():
     reps = max(10, args.steps // 2)
     g_two.replay()
     two_wall, _ = time_replays(torch, g_two, reps)
+    step.fused()
+    eager_wall = time_eager(torch, step.fused, reps)
     ref_gbs, ref_dur = stream_read_reference(twd, torch, dev_set, reps)
     traffic = counter_traffic(args.workload, M, bytes_step / nlaunch)
     kname = kernel_map(twd, ls, M, kernel)
@@ -1136,6 +1149,10 @@ def main():
         "stream_read_ref": {"gbs": round(ref_gbs, 1), "avg_launch_us": round(ref_dur * 1e6, 3),
                             "linear_over_ref": round(lin_gbs / ref_gbs, 4)},
         "two_launch_step_gbs": round(bytes_step * reps / two_wall / 1e9, 1),
+        "eager_step": {"gbs": round(bytes_step * reps / eager_wall / 1e9, 1),
+                       "us_per_launch": round(eager_wall / (reps * nlaunch) * 1e6, 3),
+                       "note": "the same step without graph capture: each call goes through "
+                               "the Python binding and is launched on the stream directly"},
         "widths": widths,
         "per_projection_cold": proj_table,
         "output_projection": head,
