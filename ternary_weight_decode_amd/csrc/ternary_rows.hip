@@ -238,6 +238,23 @@ __global__ __launch_bounds__(64 * NW) void rows_kernel(
     //    x16 sums run over all loads and are combined once: every term of
     //    d4 (d16) is a multiple of 4 (16), so the shifts are exact, and
     //    |d16| <= 16 * 2 * 127 * K / 4 < 2^31 for K <= 8192.
+    //    Where they fit in registers (M U <= 8), the staged activation words
+    //    of every load are read from LDS right after the barrier, so their
+    //    latency passes while the weights are awaited instead of after each
+    //    weight load lands.
+    constexpr bool kPre = M * U <= 8;
+    uint4 xa[kPre ? U : 1][kPre ? M : 1][4];
+    if constexpr (kPre) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int dw = 0; dw < 4; ++dw)
+                    xa[u][m][dw] = *reinterpret_cast<const uint4 *>(
+                        xs + m * S + act_off(64 * (u * L + p)) + 16 * dw);
+        __builtin_amdgcn_sched_barrier(0);
+    }
     int d1[M], d4[M], d16[M];
 #pragma unroll
     for (int m = 0; m < M; ++m)
@@ -254,7 +271,8 @@ __global__ __launch_bounds__(64 * NW) void rows_kernel(
             const uint32_t p3 = (w >> 6) & kPlane0;
 #pragma unroll
             for (int m = 0; m < M; ++m) {
-                const uint4 x = *reinterpret_cast<const uint4 *>(xs + m * S + kb + 16 * dw);
+                const uint4 x = kPre ? xa[kPre ? u : 0][kPre ? m : 0][dw]
+                                     : *reinterpret_cast<const uint4 *>(xs + m * S + kb + 16 * dw);
                 d1[m] = sdot4(p0, x.x, d1[m]);
                 d4[m] = sdot4(p1, x.y, d4[m]);
                 d16[m] = sdot4(p2, x.z, d16[m]);
@@ -327,10 +345,12 @@ bool pick(int M, int R, int NW, int U, Fn *fn, int *lds) {
 // still leaves about one workgroup per compute unit -- fewer workgroups
 // quantize the activations fewer times, but under ~200 of them the loads in
 // flight no longer fill the chip.  Measured on the 2B shapes at M = 1.
-void rows_shape(int M, int N, int *rows_per_wave, int *waves) {
+void rows_shape(int M, int K, int N, int *rows_per_wave, int *waves) {
     *rows_per_wave = 4;
     *waves = 4;
-    if (M > 2)
+    // 8 rows per wave at M = 2 holds 8 or more loads per lane past K = 3584,
+    // more than the registers of two waves per SIMD: those shapes would spill
+    if (M > 2 || (M == 2 && K > 7 * 512))
         return;
     if (N / 64 >= 200) {
         *rows_per_wave = 8;
@@ -345,7 +365,7 @@ hipError_t launch_rows(const uint8_t *w, const void *act, bool fused, const floa
                        int M, int K, int N, const Segments &segs, int32_t *acc, float *y,
                        hipStream_t stream) {
     int R = 4, NW = 4;
-    rows_shape(M, N, &R, &NW);
+    rows_shape(M, K, N, &R, &NW);
     const int L = 64 / R;
     const int U = (K + 64 * L - 1) / (64 * L);
     Fn fn = nullptr;

@@ -55,7 +55,7 @@ hipError_t launch_narrow(const uint8_t *w, const void *act, bool fused,
                          hipStream_t stream, int waves = 0);
 // Row-owner VALU dot kernel (ternary_rows.hip): M <= 4, any K; the launch
 // shape (rows per wave, waves per workgroup) comes from rows_shape.
-void rows_shape(int M, int N, int *rows_per_wave, int *waves);
+void rows_shape(int M, int K, int N, int *rows_per_wave, int *waves);
 hipError_t launch_rows(const uint8_t *w, const void *act, bool fused, const float *xscale,
                        int M, int K, int N, const Segments &segs, int32_t *acc, float *y,
                        hipStream_t stream);
