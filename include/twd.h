@@ -267,6 +267,72 @@ twd_status twd_kv_commit(void *const *segments, int nseg, int64_t seg0_positions
                          int64_t W, const int32_t *n_mat, const int32_t *n_new,
                          const int32_t *state_in, int32_t *state_out, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Multi-projection sweep: one persistent launch over many independent
+ * ternary projections (each the one-launch bf16 form above: per-token absmax
+ * int8 quantization inside, W2A8 contraction, dequant epilogue).  M1 picks
+ * packed low-bit operators by replay width ("Methodology in Plain English",
+ * paragraph 3); a decode step's layer set at one width is a fixed list of
+ * such operators, and graph replay needs fixed shapes and addresses (the same
+ * paragraph), so the list is planned once and replayed.  Where the
+ * projections of the list do not consume each other's outputs (the
+ * synthetic layer sets, or independent projections of one layer), one launch
+ * streams all their packed weights without a kernel boundary between them.
+ * Results are those of twd_ternary_linear_bf16 on each projection: acc
+ * bit-identical, y within the fp32 evaluation of acc * s_m * gamma.
+ * ---------------------------------------------------------------------- */
+
+/* One projection of a sweep.  wpacked: device [N][K/4] (16-byte aligned);
+ * x_bf16: device [M][K] bf16 bit patterns (16-byte aligned); acc: device
+ * int32 [M][N] or NULL; y: device fp32 [M][N] or NULL (not both NULL; 4-byte
+ * aligned); segments as in twd_ternary_linear_fused (N = sum of seg_rows,
+ * which may be 0).  64 <= K <= TWD_MAX_K, K % 64 == 0.  Outputs of different
+ * projections must not overlap each other or any input. */
+typedef struct {
+    const uint8_t *wpacked;
+    const uint16_t *x_bf16;
+    int32_t *acc;
+    float *y;
+    int64_t K;
+    int64_t nseg;
+    int64_t seg_rows[TWD_MAX_SEGMENTS];
+    float seg_gamma[TWD_MAX_SEGMENTS];
+} twd_sweep_proj;
+
+/* A planned sweep (filled by twd_sweep_encode; the caller keeps it). */
+typedef struct {
+    const void *table;      /* device copy of the table image */
+    int64_t table_bytes;
+    int64_t weight_bytes;   /* sum of N K / 4 over the projections */
+    int32_t nproj, M, nwg, lds_bytes;
+    uint32_t check;         /* also stored in the table; the kernel compares */
+    int32_t reserved[3];
+} twd_sweep_plan;
+
+/* Bytes of the table image for this list (host only, launches nothing).
+ * Errors as twd_sweep_encode. */
+twd_status twd_sweep_table_bytes(const twd_sweep_proj *projs, int nproj, int64_t M,
+                                 int64_t *bytes);
+
+/* Plan the sweep and write its table image into HOST memory table_host
+ * (table_bytes from twd_sweep_table_bytes); the plan records table_dev, the
+ * DEVICE buffer (16-byte aligned, table_bytes long, owned by the caller) into
+ * which the caller copies the image before the first twd_ternary_sweep.  Host
+ * only.  1 <= M <= TWD_MAX_M, 1 <= nproj <= 65536.
+ * Errors: INVALID_ARG (null or misaligned pointers, bad segments, a table
+ * that is too small), UNSUPPORTED (K or M outside the limits). */
+twd_status twd_sweep_encode(const twd_sweep_proj *projs, int nproj, int64_t M,
+                            const void *table_dev, void *table_host, int64_t table_bytes,
+                            twd_sweep_plan *plan);
+
+/* Run every projection of the plan in one launch, asynchronously on stream.
+ * The device table, weights, activations and outputs must stay unchanged in
+ * place (inputs) and alive until the stream's work completes.  The kernel
+ * writes nothing if the device table does not carry the plan's check value.
+ * Allocates nothing, reads no device memory on the host: capturable into a
+ * HIP graph.  Errors: INVALID_ARG (null plan, bad plan fields), HIP. */
+twd_status twd_ternary_sweep(const twd_sweep_plan *plan, void *stream);
+
 /* Measurement helper: a plain streaming read of `bytes` device bytes
  * (16-byte aligned, bytes % 16 == 0) that stores nothing but a guard word
  * into sink (device, >= 1024 bytes).  Its launch duration is the

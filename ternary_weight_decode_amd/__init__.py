@@ -9,7 +9,8 @@ Names follow the C ABI in ``include/twd.h``: ``quantize_act``,
 ``ternary_linear``, ``ternary_linear_fused``, ``ternary_linear_bf16``,
 ``pack_ternary``,
 ``unpack_ternary``, ``ternarize_absmean``, ``select_kernel``,
-``stream_read``, ``stream_copy``.
+``stream_read``, ``stream_copy``; ``Sweep`` wraps ``twd_sweep_table_bytes``,
+``twd_sweep_encode`` and ``twd_ternary_sweep``.
 """
 from __future__ import annotations
 
@@ -72,6 +73,26 @@ _lib_proj_bf16 = _sig("twd_projection_bf16", [_p, _p, _i64, _i64, _i64, _p, _p])
 _lib_kv_commit = _sig("twd_kv_commit",
                       [_p, _int, _i64, _i64, _i64, _p, _i64, _p, _p, _p, _p, _p])
 _lib_stream_read = _sig("twd_stream_read", [_p, _i64, _p, _p])
+
+
+class SweepProjDesc(ctypes.Structure):
+    """twd_sweep_proj (include/twd.h)."""
+    _fields_ = [("wpacked", _p), ("x_bf16", _p), ("acc", _p), ("y", _p),
+                ("K", _i64), ("nseg", _i64), ("seg_rows", _i64 * MAX_SEGMENTS),
+                ("seg_gamma", _f32 * MAX_SEGMENTS)]
+
+
+class SweepPlan(ctypes.Structure):
+    """twd_sweep_plan (include/twd.h)."""
+    _fields_ = [("table", _p), ("table_bytes", _i64), ("weight_bytes", _i64),
+                ("nproj", ctypes.c_int32), ("M", ctypes.c_int32), ("nwg", ctypes.c_int32),
+                ("lds_bytes", ctypes.c_int32), ("check", ctypes.c_uint32),
+                ("reserved", ctypes.c_int32 * 3)]
+
+
+_lib_sweep_bytes = _sig("twd_sweep_table_bytes", [_p, _int, _i64, _p])
+_lib_sweep_encode = _sig("twd_sweep_encode", [_p, _int, _i64, _p, _p, _i64, _p])
+_lib_sweep = _sig("twd_ternary_sweep", [_p, _p])
 _lib_stream_copy = _sig("twd_stream_copy", [_p, _p, _i64, _p])
 
 EXPORTS = ("twd_version", "twd_last_error", "twd_ternarize_absmean",
@@ -79,7 +100,8 @@ EXPORTS = ("twd_version", "twd_last_error", "twd_ternarize_absmean",
            "twd_ternary_linear", "twd_ternary_linear_fused",
            "twd_ternary_linear_fused_kernel", "twd_ternary_linear_bf16",
            "twd_select_kernel", "twd_quantize_fp8_rows", "twd_projection_fp8",
-           "twd_projection_bf16", "twd_kv_commit", "twd_stream_read", "twd_stream_copy")
+           "twd_projection_bf16", "twd_kv_commit", "twd_stream_read", "twd_stream_copy",
+           "twd_sweep_table_bytes", "twd_sweep_encode", "twd_ternary_sweep")
 
 
 class TwdError(RuntimeError):
@@ -382,3 +404,83 @@ def stream_copy(src, dst, nbytes: int, stream=None):
     _need(_nbytes(src) >= nbytes and _nbytes(dst) >= nbytes, "buffers smaller than nbytes")
     _check(_lib_stream_copy(_dev_ptr(src, "src"), _dev_ptr(dst, "dst"), int(nbytes),
                             _stream(stream)))
+
+
+# ------------------------------------------------------ multi-projection sweep
+
+def sweep_descs(projs, M: int):
+    """ctypes array of twd_sweep_proj from (wpacked_ptr, x_ptr, acc_ptr, y_ptr,
+    K, seg_rows, seg_gamma) tuples of plain integers (host-side planning)."""
+    arr = (SweepProjDesc * len(projs))()
+    for i, (w, x, acc, y, K, seg_rows, seg_gamma) in enumerate(projs):
+        seg_rows = [int(r) for r in seg_rows]
+        if not 1 <= len(seg_rows) <= MAX_SEGMENTS or len(seg_gamma) != len(seg_rows):
+            raise ValueError("1..4 segments, one gamma each")
+        d = arr[i]
+        d.wpacked, d.x_bf16, d.acc, d.y = w, x, acc, y
+        d.K, d.nseg = int(K), len(seg_rows)
+        for s, (r, g) in enumerate(zip(seg_rows, seg_gamma)):
+            d.seg_rows[s] = r
+            d.seg_gamma[s] = float(g)
+    return arr
+
+
+def sweep_encode(descs, M: int, table_dev_ptr: int):
+    """Plan a sweep on the host: returns (table image as uint8 numpy, plan)."""
+    n = ctypes.c_int64(0)
+    _check(_lib_sweep_bytes(descs, len(descs), int(M), ctypes.byref(n)))
+    img = np.zeros(n.value, np.uint8)
+    plan = SweepPlan()
+    _check(_lib_sweep_encode(descs, len(descs), int(M), ctypes.c_void_p(table_dev_ptr),
+                             _np_ptr(img), n.value, ctypes.byref(plan)))
+    return img, plan
+
+
+class Sweep:
+    """One launch over a list of independent projections at width M.
+
+    projs: sequence of (wpacked, seg_rows, seg_gamma, x, acc, y) with device
+    tensors wpacked (uint8, N*K/4 bytes), x (bf16 [M, K]), acc (int32 [M, N]
+    or None), y (fp32 [M, N] or None).  The table is planned on the host,
+    copied once to a device buffer held by this object, and every run() is a
+    single asynchronous launch on the stream (capturable into a graph).  The
+    tensors must stay alive and in place while the object is used."""
+
+    def __init__(self, projs):
+        torch = _torch()
+        if not projs:
+            raise ValueError("empty projection list")
+        M = None
+        rows = []
+        keep = []
+        for (w, seg_rows, seg_gamma, x, acc, y) in projs:
+            _need(x.dim() == 2, "x must be [M, K]")
+            m, K = x.shape
+            M = m if M is None else M
+            _need(m == M, "every projection takes the same M")
+            N = int(sum(int(r) for r in seg_rows))
+            _need(_nbytes(w) >= N * K // 4, "wpacked holds fewer than N*K/4 bytes")
+            _need(acc is None or tuple(acc.shape) == (M, N), "acc must be [M, N]")
+            _need(y is None or tuple(y.shape) == (M, N), "y must be [M, N]")
+            ptr = lambda t, name, dt: (_dev_ptr(t, name, dt).value if t is not None else None)
+            rows.append((ptr(w, "wpacked", (torch.uint8,)),
+                         ptr(x, "x", (torch.bfloat16, torch.int16)),
+                         ptr(acc, "acc", (torch.int32,)), ptr(y, "y", (torch.float32,)),
+                         K, seg_rows, seg_gamma))
+            keep.append((w, x, acc, y))
+        descs = sweep_descs(rows, M)
+        n = ctypes.c_int64(0)
+        _check(_lib_sweep_bytes(descs, len(descs), int(M), ctypes.byref(n)))
+        self.table = torch.empty(n.value, dtype=torch.uint8, device=projs[0][3].device)
+        img, self.plan = sweep_encode(descs, M, self.table.data_ptr())
+        self.table.copy_(torch.from_numpy(img))
+        torch.cuda.synchronize()
+        self._keep = keep
+        self.M = M
+
+    @property
+    def weight_bytes(self) -> int:
+        return int(self.plan.weight_bytes)
+
+    def run(self, stream=None):
+        _check(_lib_sweep(ctypes.byref(self.plan), _stream(stream)))

@@ -1,0 +1,435 @@
+// Multi-projection sweep: one persistent launch runs a planned list of
+// ternary projections (W2A8, per-token absmax int8 quantization of bf16
+// activations inside), gfx950.
+//
+// What it computes (BitMTP page, ai.info AI summary): per projection, the
+// packed low-bit operator of M1 ("Methodology in Plain English", paragraph
+// 3) on ternary BitNet b1.58 weights ("What This Paper Is About") and 8-bit
+// activations ("Main Findings", first bullet): q = per-token absmax int8 of
+// x, acc[m][n] = sum_k q[m][k] t[n][k] in int32, y = acc * s_m * gamma(n).
+// The result equals the one-launch bf16 linear on each projection.
+//
+// Why one launch.  On this chip a dependent kernel boundary costs more than
+// streaming a whole small projection (a 2B-class O projection is 1.6 MB, a
+// fifth of a microsecond of HBM time), so the launches of a layer set cost
+// more than its weights.  Here the 16-row tiles of every projection of the
+// list form one sequence, cut by the host planner into workgroup ranges of
+// about equal bytes; each workgroup stages (quantizes) the activations of the
+// at most four projections its range touches, once, and its waves then
+// stream their tiles with the next passes' weight loads always in flight,
+// across tile and projection boundaries, with no barrier and no kernel
+// boundary until the list ends.
+//
+// Work split.  Wave w of a workgroup takes tiles w, w + 4, ... of the
+// workgroup's range.  A tile (16 weight rows, all of K) is read in passes of
+// four 256-wide K slices: per lane four 16-byte loads, issued as two whole
+// 128-byte lines per row pair (the tile kernel's layout: loads X of rows 0-7
+// and Y of rows 8-15, rebuilt into the matrix-core A operand by a lane
+// select and a DPP rotation).  A three-slot register ring holds the pass
+// being computed and the next two passes' loads.  Each slice is decoded into
+// four byte planes (codes c = t + 1 scaled 1, 4, 16, 1), the A operands of
+// four v_mfma_i32_16x16x64_i8 with their own accumulators; B is the staged
+// int8 activation block (token columns at or past M read a zero block).
+// After a tile's last pass, lane (token r, group g) holds rows 4g..4g+3 for
+// token r: sum q t = sum q c - sum q, then the dequant epilogue.
+#include "kernel_common.h"
+
+namespace twd {
+namespace {
+
+using namespace kern;
+
+constexpr int kRawBufferFlags = 0x00020000;  // raw buffer, 32-bit format
+constexpr uint32_t kOutOfRange = 0x80000000u;
+constexpr int kS = 3;  // register ring slots: the pass computed + two in flight
+
+// The table is read-only for the whole launch: reading it through the
+// constant address space gives scalar loads, which wait on the scalar
+// counter instead of the vector-memory counter that tracks the weight ring.
+template <typename T>
+using cptr = const __attribute__((address_space(4))) T *;
+
+// Field-wise copies out of the constant address space.
+__device__ __forceinline__ SweepSpan span_at(cptr<SweepWork> wk, int s) {
+    SweepSpan sp;
+    sp.q = wk->span[s].q;
+    sp.t0 = wk->span[s].t0;
+    sp.t1 = wk->span[s].t1;
+    sp.xoff = wk->span[s].xoff;
+    return sp;
+}
+
+__device__ __forceinline__ Segments segs_of(cptr<SweepProj> P) {
+    Segments sg;
+    sg.nseg = P->segs.nseg;
+#pragma unroll
+    for (int i = 0; i < TWD_MAX_SEGMENTS; ++i) {
+        sg.bound[i] = P->segs.bound[i];
+        sg.gamma[i] = P->segs.gamma[i];
+    }
+    return sg;
+}
+
+// Rotate a value by 8 lanes within each 16-lane row (DPP row_ror:8).
+__device__ __forceinline__ uint32_t ror8(uint32_t v) {
+    return static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x128, 0xf, 0xf, false));
+}
+
+// Staged activation layout: word 16 g + 4 d + j of a 64-word slice is stored
+// at 16 g + 4 j + d, so one 16-byte read gives the B operand of plane j.
+__device__ __forceinline__ int permuted_word(int w) {
+    return (w & ~63) | (w & 48) | ((w & 3) << 2) | ((w >> 2) & 3);
+}
+
+// A pass: tile t of the span's projection, 256-wide slices kSweepLP p ..
+// kSweepLP p + kSweepLP - 1.  The wave walks its tiles t0 + wave, t0 + wave
+// + NW, ... and each tile's passes in order; two counters (tile, pass) stand
+// for the pass index, so no division is needed.
+struct PassPos {
+    int t;
+    int p;
+};
+
+template <int NW>
+__device__ __forceinline__ void step(PassPos &c, int passes) {
+    if (++c.p == passes) {
+        c.p = 0;
+        c.t += NW;
+    }
+}
+
+// Weights of a span's projection, as the loads need them.
+struct SpanW {
+    const uint8_t *w;
+    int RB;  // bytes per weight row, K / 4
+    int N;
+    int t1;  // end tile of the span
+};
+
+// Issue one pass's weight loads (kSweepLP slices) into ring slot a; a pass
+// past the span's last tile issues loads with an empty descriptor (zeros, no
+// memory traffic), which keeps the count of loads in flight fixed.
+__device__ __forceinline__ void issue(const SpanW &sw, const PassPos &c, int r, int g,
+                                      uint4 (&a)[kSweepLP]) {
+    const bool valid = c.t < sw.t1;
+    const int n0 = 16 * c.t;
+    const int rows = valid ? min(16, sw.N - n0) : 0;
+    const uint8_t *base = valid ? sw.w + static_cast<int64_t>(n0) * sw.RB : sw.w;
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(base), 0, rows * sw.RB, kRawBufferFlags);
+    const int hi = r >> 3;
+#pragma unroll
+    for (int i = 0; i < kSweepLP; ++i) {
+        const int u = kSweepLP * c.p + i;
+        const int row = (i & 1) ? 8 + (r & 7) : (r & 7);
+        const int col = 128 * (u >> 1) + 16 * (g + 4 * ((i & 1) ? 1 - hi : hi));
+        const uint32_t off =
+            col < sw.RB ? static_cast<uint32_t>(row * sw.RB + col) : kOutOfRange;
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, kWeightPolicy);
+        a[i] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+}
+
+// Multiply one pass.  Every slice is multiplied, also those past K (their
+// weights were loaded as zeros and their B operand is the zero block):
+// consuming every ring register on every path keeps the compiler's
+// vector-memory waits exact, so two passes stay in flight.
+__device__ __forceinline__ void compute(int p, int slices, const uint8_t *bsrc, int ustep,
+                                        const uint8_t *zero, int r,
+                                        const uint4 (&a)[kSweepLP], v4i &c0, v4i &c3,
+                                        v4i &c4, v4i &c16) {
+    if (p == 0) {
+        c0 = v4i{0, 0, 0, 0};
+        c3 = c0;
+        c4 = c0;
+        c16 = c0;
+    }
+    const int hi = r >> 3;
+#pragma unroll
+    for (int i = 0; i < kSweepLP; ++i) {
+        const int u = kSweepLP * p + i;
+        const uint8_t *bu = u < slices ? bsrc + u * ustep : zero;
+        const v4i b0 = *reinterpret_cast<const v4i *>(bu);
+        const v4i b1 = *reinterpret_cast<const v4i *>(bu + 16);
+        const v4i b2 = *reinterpret_cast<const v4i *>(bu + 32);
+        const v4i b3 = *reinterpret_cast<const v4i *>(bu + 48);
+        // even slice of a pair: X (rows 0-7) where r < 8, else Y; odd
+        // slice: the other load, rotated 8 lanes along the 16-lane row
+        uint4 au;
+        const uint4 x = a[i & ~1], yv = a[i | 1];
+        if ((i & 1) == 0) {
+            au = hi ? yv : x;
+        } else {
+            const uint4 z = hi ? x : yv;
+            au = make_uint4(ror8(z.x), ror8(z.y), ror8(z.z), ror8(z.w));
+        }
+        const v4i w = {static_cast<int>(au.x), static_cast<int>(au.y),
+                       static_cast<int>(au.z), static_cast<int>(au.w)};
+        const v4i p0 = w & static_cast<int>(kPlane0);
+        const v4i p1 = w & static_cast<int>(kPlane1);
+        const v4i p2 = w & static_cast<int>(kPlane2);
+        const v4i p3 = (w >> 6) & static_cast<int>(kPlane0);
+        c0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(p0, b0, c0, 0, 0, 0);
+        c4 = __builtin_amdgcn_mfma_i32_16x16x64_i8(p1, b1, c4, 0, 0, 0);
+        c16 = __builtin_amdgcn_mfma_i32_16x16x64_i8(p2, b2, c16, 0, 0, 0);
+        c3 = __builtin_amdgcn_mfma_i32_16x16x64_i8(p3, b3, c3, 0, 0, 0);
+    }
+}
+
+// Outputs of a span's projection, and this lane's token terms.
+struct SpanOut {
+    int32_t *acc;
+    float *y;
+    Segments segs;
+    int N;
+    int qs;     // row sum of q for token r
+    float sc;   // scale of token r
+};
+
+// After a tile's last pass: lane (token r, group g) holds rows 4g .. 4g+3.
+template <int M>
+__device__ __forceinline__ void epilogue(const SpanOut &so, int t, int r, int g, const v4i &c0,
+                                         const v4i &c3, const v4i &c4, const v4i &c16) {
+    const v4i cc = c0 + c3 + (c4 >> 2) + (c16 >> 4);
+    const int n0 = 16 * t + 4 * g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int n = n0 + i;
+        const int total = cc[i] - so.qs;
+        const float yv = static_cast<float>(total) * so.sc * row_gamma(so.segs, n);
+        if (r < M && n < so.N) {
+            const int64_t o = static_cast<int64_t>(r) * so.N + n;
+            if (so.acc)
+                so.acc[o] = total;
+            if (so.y)
+                so.y[o] = yv;
+        }
+    }
+}
+
+template <int M, int NW>
+__global__ __launch_bounds__(64 * NW) void sweep_kernel(const SweepHeader *header_g,
+                                                        const SweepProj *projs_g,
+                                                        const SweepWork *work_g,
+                                                        uint32_t check) {
+    constexpr int T = 64 * NW;
+    // chunks of 8 activations per thread and token row: K <= 8192
+    constexpr int kRounds = (TWD_MAX_K / 8 + T - 1) / T;
+    extern __shared__ __align__(16) uint8_t smem[];
+    uint8_t *zero = smem;  // 64 zero bytes
+    uint32_t *st_max = reinterpret_cast<uint32_t *>(smem + 64);  // [span][16]
+    int32_t *st_sum = reinterpret_cast<int32_t *>(st_max + kSweepMaxSpans * 16);
+    float *st_scale = reinterpret_cast<float *>(st_sum + kSweepMaxSpans * 16);
+    uint8_t *xbase = smem + kSweepLdsHeader;
+
+    const cptr<SweepHeader> header = (cptr<SweepHeader>)header_g;
+    const cptr<SweepProj> projs = (cptr<SweepProj>)projs_g;
+    if (header->check != check)
+        return;  // the table does not belong to this plan: write nothing
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 15;
+    const int g = lane >> 4;
+    const cptr<SweepWork> wk = (cptr<SweepWork>)work_g + blockIdx.x;
+    const int nspan = wk->nspan;
+
+    // 1. stage the activations of every span: absmax per token row, then
+    //    the int8 rows in the permuted B layout and their row sums
+    if (tid < 16 + 2 * kSweepMaxSpans * 16)
+        reinterpret_cast<uint32_t *>(smem)[tid] = 0u;
+    __syncthreads();
+    for (int s = 0; s < nspan; ++s) {
+        const cptr<SweepProj> P = projs + wk->span[s].q;
+        const int K = P->K;
+        const int C = K >> 3;
+        const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(P->x), 0, M * K * 2, kRawBufferFlags);
+        // token rows in groups whose loads are all issued before any is used
+        constexpr int G = M < 4 ? M : 4;
+        for (int m0 = 0; m0 < M; m0 += G) {
+            uint4 v[G][kRounds];
+#pragma unroll
+            for (int gm = 0; gm < G; ++gm)
+#pragma unroll
+                for (int i = 0; i < kRounds; ++i) {
+                    const int ch = tid + T * i;
+                    const int m = m0 + gm;
+                    const uint32_t off = ch < C && m < M
+                                             ? static_cast<uint32_t>((m * K + 8 * ch) * 2)
+                                             : kOutOfRange;
+                    const auto x = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
+                    v[gm][i] = make_uint4(x[0], x[1], x[2], x[3]);
+                }
+            __builtin_amdgcn_sched_barrier(0);
+            uint32_t mv[G];
+#pragma unroll
+            for (int gm = 0; gm < G; ++gm) {
+                u16x2 am = {0, 0};
+#pragma unroll
+                for (int i = 0; i < kRounds; ++i) {
+                    am = absmax_pair(am, v[gm][i].x);
+                    am = absmax_pair(am, v[gm][i].y);
+                    am = absmax_pair(am, v[gm][i].z);
+                    am = absmax_pair(am, v[gm][i].w);
+                }
+                mv[gm] = absmax_bits(am);
+            }
+            row_max16<G>(mv);
+            if ((lane & 15) == 15) {
+#pragma unroll
+                for (int gm = 0; gm < G; ++gm)
+                    if (m0 + gm < M)
+                        __hip_atomic_fetch_max(&st_max[s * 16 + m0 + gm], mv[gm],
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+        }
+    }
+    __syncthreads();  // absmax of every token row
+    for (int s = 0; s < nspan; ++s) {
+        const SweepSpan sp = span_at(wk, s);
+        const cptr<SweepProj> P = projs + sp.q;
+        const int K = P->K;
+        const int C = K >> 3;
+        const int stride = P->stride;
+        const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(P->x), 0, M * K * 2, kRawBufferFlags);
+        constexpr int G = M < 4 ? M : 4;
+        for (int m0 = 0; m0 < M; m0 += G) {
+            uint4 v[G][kRounds];
+#pragma unroll
+            for (int gm = 0; gm < G; ++gm)
+#pragma unroll
+                for (int i = 0; i < kRounds; ++i) {
+                    const int ch = tid + T * i;
+                    const int m = m0 + gm;
+                    const uint32_t off = ch < C && m < M
+                                             ? static_cast<uint32_t>((m * K + 8 * ch) * 2)
+                                             : kOutOfRange;
+                    const auto x = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
+                    v[gm][i] = make_uint4(x[0], x[1], x[2], x[3]);
+                }
+            __builtin_amdgcn_sched_barrier(0);
+            int sq[G];
+#pragma unroll
+            for (int gm = 0; gm < G; ++gm) {
+                const int m = m0 + gm;
+                const float a_m = __uint_as_float(st_max[s * 16 + (m < M ? m : 0)]);
+                // correctly rounded fp32 divisions (build flag), as in the
+                // stand-alone quantizer; an all-zero row quantizes to zeros
+                const float inv = a_m > 0.0f ? 127.0f / a_m : 0.0f;
+                if (tid == 0 && m < M)
+                    st_scale[s * 16 + m] = a_m / 127.0f;
+                uint8_t *row = xbase + sp.xoff + m * stride;
+                sq[gm] = 0;
+#pragma unroll
+                for (int i = 0; i < kRounds; ++i) {
+                    const int ch = tid + T * i;
+                    const uint32_t q0 = quant4(v[gm][i].x, v[gm][i].y, inv);
+                    const uint32_t q1 = quant4(v[gm][i].z, v[gm][i].w, inv);
+                    if (ch < C && m < M) {
+                        *reinterpret_cast<uint32_t *>(row + 4 * permuted_word(2 * ch)) = q0;
+                        *reinterpret_cast<uint32_t *>(row + 4 * permuted_word(2 * ch + 1)) = q1;
+                    }
+                    sq[gm] = sdot4(q0, kOnes, sq[gm]);
+                    sq[gm] = sdot4(q1, kOnes, sq[gm]);
+                }
+            }
+            row_sum16<G>(sq);
+            if ((lane & 15) == 15) {
+#pragma unroll
+                for (int gm = 0; gm < G; ++gm)
+                    if (m0 + gm < M)
+                        __hip_atomic_fetch_add(&st_sum[s * 16 + m0 + gm], sq[gm],
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+        }
+    }
+    __syncthreads();  // staged rows, row sums and scales
+
+    // 2. stream each span's tiles: compute the pass in one ring slot while
+    //    the next two passes' loads are in flight
+    uint4 ring[kS][kSweepLP];
+    v4i c0 = {0, 0, 0, 0}, c3 = c0, c4 = c0, c16 = c0;
+    for (int s = 0; s < nspan; ++s) {
+        const SweepSpan sp = span_at(wk, s);
+        const cptr<SweepProj> P = projs + sp.q;
+        SpanW sw;
+        sw.w = P->w;
+        sw.RB = P->K >> 2;
+        sw.N = P->N;
+        sw.t1 = sp.t1;
+        const int passes = P->passes;
+        const int slices = P->slices;
+        SpanOut so;
+        so.acc = P->acc;
+        so.y = P->y;
+        so.segs = segs_of(P);
+        so.N = P->N;
+        so.qs = st_sum[s * 16 + r];
+        so.sc = st_scale[s * 16 + r];
+        const uint8_t *bsrc = r < M ? xbase + sp.xoff + r * P->stride + 64 * g : zero;
+        const int ustep = r < M ? 256 : 0;
+
+        // passes of this wave in the span: tiles t0 + wave, t0 + wave + NW, ...
+        const int tiles = sp.t0 + wave < sp.t1 ? (sp.t1 - sp.t0 - wave + NW - 1) / NW : 0;
+        int left = tiles * passes;
+        PassPos c{sp.t0 + wave, 0};
+        PassPos f = c;
+        issue(sw, f, r, g, ring[0]);
+        step<NW>(f, passes);
+        issue(sw, f, r, g, ring[1]);
+        step<NW>(f, passes);
+#define TWD_SWEEP_STEP(NEXT, CUR)                                              \
+    issue(sw, f, r, g, ring[NEXT]);                                            \
+    step<NW>(f, passes);                                                       \
+    compute(c.p, slices, bsrc, ustep, zero, r, ring[CUR], c0, c3, c4, c16);    \
+    if (c.p == passes - 1)                                                     \
+        epilogue<M>(so, c.t, r, g, c0, c3, c4, c16);                           \
+    step<NW>(c, passes);
+        for (; left >= 3; left -= 3) {
+            TWD_SWEEP_STEP(2, 0)
+            TWD_SWEEP_STEP(0, 1)
+            TWD_SWEEP_STEP(1, 2)
+        }
+        if (left >= 1) {
+            TWD_SWEEP_STEP(2, 0)
+        }
+        if (left >= 2) {
+            TWD_SWEEP_STEP(0, 1)
+        }
+#undef TWD_SWEEP_STEP
+    }
+}
+
+using Fn = void (*)(const SweepHeader *, const SweepProj *, const SweepWork *, uint32_t);
+
+template <int... Ms>
+Fn pick(int M) {
+    Fn fn = nullptr;
+    ((M == Ms ? (void)(fn = &sweep_kernel<Ms, kSweepWaves>) : (void)0), ...);
+    return fn;
+}
+
+}  // namespace
+
+hipError_t launch_sweep(const twd_sweep_plan &plan, hipStream_t stream) {
+    Fn fn = pick<1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>(plan.M);
+    if (!fn)
+        return hipErrorInvalidValue;
+    hipError_t e = ensure_lds_limit(reinterpret_cast<const void *>(fn), plan.lds_bytes);
+    if (e != hipSuccess)
+        return e;
+    const uint8_t *t = static_cast<const uint8_t *>(plan.table);
+    const SweepHeader *h = reinterpret_cast<const SweepHeader *>(t);
+    const SweepProj *p = reinterpret_cast<const SweepProj *>(t + kSweepHeaderBytes);
+    const SweepWork *w = reinterpret_cast<const SweepWork *>(
+        t + kSweepHeaderBytes + static_cast<int64_t>(plan.nproj) * sizeof(SweepProj));
+    hipLaunchKernelGGL(fn, dim3(plan.nwg), dim3(64 * kSweepWaves), plan.lds_bytes, stream, h, p,
+                       w, plan.check);
+    return hipGetLastError();
+}
+
+}  // namespace twd

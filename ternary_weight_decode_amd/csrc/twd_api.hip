@@ -331,3 +331,29 @@ extern "C" twd_status twd_stream_copy(const void *src, void *dst, int64_t bytes,
     return hip_status(launch_stream_copy(src, dst, bytes, as_stream(stream)),
                       "stream_copy launch");
 }
+
+extern "C" twd_status twd_sweep_table_bytes(const twd_sweep_proj *projs, int nproj, int64_t M,
+                                            int64_t *bytes) {
+    if (!bytes)
+        return set_error(TWD_ERR_INVALID_ARG, "sweep_table_bytes: null bytes");
+    return sweep_plan(projs, nproj, M, nullptr, nullptr, 0, bytes, nullptr);
+}
+
+extern "C" twd_status twd_sweep_encode(const twd_sweep_proj *projs, int nproj, int64_t M,
+                                       const void *table_dev, void *table_host,
+                                       int64_t table_bytes, twd_sweep_plan *plan) {
+    if (!table_host)
+        return set_error(TWD_ERR_INVALID_ARG, "sweep_encode: null host table");
+    return sweep_plan(projs, nproj, M, table_dev, table_host, table_bytes, nullptr, plan);
+}
+
+extern "C" twd_status twd_ternary_sweep(const twd_sweep_plan *plan, void *stream) {
+    if (!plan || !plan->table || !aligned(plan->table, 16))
+        return set_error(TWD_ERR_INVALID_ARG, "sweep: null plan or misaligned table");
+    if (plan->M < 1 || plan->M > TWD_MAX_M || plan->nproj < 1 || plan->nproj > 65536 ||
+        plan->nwg < 1 || plan->lds_bytes < kSweepLdsHeader || plan->lds_bytes > 160 * 1024 ||
+        plan->table_bytes < kSweepHeaderBytes + int64_t(plan->nproj) * int64_t(sizeof(SweepProj)) +
+                                int64_t(plan->nwg) * int64_t(sizeof(SweepWork)))
+        return set_error(TWD_ERR_INVALID_ARG, "sweep: plan fields out of range");
+    return hip_status(launch_sweep(*plan, as_stream(stream)), "sweep launch");
+}

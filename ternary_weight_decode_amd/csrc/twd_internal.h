@@ -99,4 +99,59 @@ hipError_t launch_stream_read(const void *buf, int64_t bytes, uint32_t *sink,
 hipError_t launch_stream_copy(const void *src, void *dst, int64_t bytes,
                               hipStream_t stream);
 
+
+// Multi-projection sweep (ternary_sweep.hip, planned by sweep_plan.cpp).  The
+// device table is a header, one SweepProj per projection and one SweepWork per
+// workgroup; its layout is private to the library.
+constexpr int kSweepMaxSpans = 4;      // projections one workgroup stages
+constexpr int kSweepLP = 4;            // 256-wide K slices per pass
+constexpr int kSweepWaves = 4;         // waves per workgroup
+constexpr int kSweepHeaderBytes = 64;  // table header
+constexpr uint32_t kSweepMagic = 0x53445754u;  // "TWDS"
+// LDS: zero block (64 B), then per-span absmax, row-sum and scale words
+// (kSweepMaxSpans x 16 each), then the staged activation rows.
+constexpr int kSweepLdsHeader = 64 + 3 * kSweepMaxSpans * 16 * 4;
+
+struct SweepProj {       // 96 bytes
+    const uint8_t *w;    // packed [N][K/4]
+    const uint16_t *x;   // bf16 [M][K]
+    int32_t *acc;        // [M][N] or null
+    float *y;            // [M][N] or null
+    int K;
+    int N;
+    int passes;          // passes per 16-row tile (kSweepLP slices each)
+    int slices;          // 256-wide K slices, ceil(K / 256)
+    int stride;          // LDS bytes per staged token row
+    Segments segs;
+    int pad[2];
+};
+static_assert(sizeof(SweepProj) == 96, "SweepProj layout");
+
+struct SweepSpan {       // tiles [t0, t1) of projection q, activations at xoff
+    int q, t0, t1, xoff;
+};
+
+struct SweepWork {       // 80 bytes: one workgroup's spans, in order
+    int nspan;
+    int pad[3];
+    SweepSpan span[kSweepMaxSpans];
+};
+static_assert(sizeof(SweepWork) == 80, "SweepWork layout");
+
+struct SweepHeader {     // 64 bytes
+    uint32_t magic, check;
+    int nproj, nwg, M, lds;
+    int proj_off, work_off;
+    int64_t weight_bytes;
+    int pad[6];
+};
+static_assert(sizeof(SweepHeader) == kSweepHeaderBytes, "SweepHeader layout");
+
+// Host planner: checks every projection, splits the tiles over workgroups and
+// writes the table image.  table_host == nullptr only sizes the table.
+twd_status sweep_plan(const twd_sweep_proj *projs, int nproj, int64_t M, const void *table_dev,
+                      void *table_host, int64_t table_bytes, int64_t *bytes_needed,
+                      twd_sweep_plan *plan);
+hipError_t launch_sweep(const twd_sweep_plan &plan, hipStream_t stream);
+
 }  // namespace twd

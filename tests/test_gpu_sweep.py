@@ -1,0 +1,255 @@
+"""GPU parity of the multi-projection sweep (twd_ternary_sweep) against the
+CPU oracle, through the C ABI.
+
+Bar, as for the one-launch linear: int32 accumulators bit-exact, fp32 outputs
+within 1e-6 relative of the oracle's double-precision value.  Cases: random
+projection lists at every width M = 1..16 (ragged K and N, 1..4 segments,
+empty projections, K = 64 and K = 8192), one full-size 2B-class layer at
+every width on the outlier workload, the whole 30-layer 2B set at M = 1 in
+the benchmark's launch (sampled rows against the oracle, every row against
+the per-projection launches), graph replays checked against the oracle, and
+a table that does not match its plan (nothing written).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+REL_TOL = 1e-6
+
+
+@pytest.fixture(scope="module")
+def env():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import oracle
+    import ternary_weight_decode_amd as twd
+    oracle.build(force=False)
+    return torch, twd, oracle
+
+
+def log(msg):
+    sys.stdout.write(msg + "\n")
+    sys.stdout.flush()
+
+
+def dev_bf16(torch, x_bits):
+    return torch.from_numpy(x_bits.view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def check_y(y, yref, what=""):
+    y = np.asarray(y, dtype=np.float64)
+    err = np.abs(y - yref)
+    bad = err > REL_TOL * np.abs(yref)
+    assert not bad.any(), f"{what}: {bad.sum()} y values outside 1e-6 relative"
+
+
+class Case:
+    """One projection of a sweep: host inputs, device tensors, oracle."""
+
+    def __init__(self, env, W, segs, x, want_acc=True, want_y=True):
+        torch, twd, orc = env
+        self.W, self.segs, self.x = W, tuple(segs), x
+        M, K = x.shape
+        N = int(sum(segs))
+        packed, self.gammas = twd.prepare_weights(W, segs)
+        self.wp = torch.from_numpy(packed).cuda()
+        self.xd = dev_bf16(torch, x)
+        self.acc = (torch.full((M, N), -7, dtype=torch.int32, device="cuda")
+                    if want_acc else None)
+        self.y = torch.full((M, N), -7.0, device="cuda") if want_y else None
+
+    def entry(self):
+        return (self.wp, self.segs, self.gammas, self.xd, self.acc, self.y)
+
+    def check(self, orc, ref=None):
+        ref = ref if ref is not None else orc.forward(self.W, self.segs, self.x)
+        assert self.gammas == ref["gammas"]
+        if self.acc is not None:
+            np.testing.assert_array_equal(self.acc.cpu().numpy(), ref["acc"])
+        if self.y is not None:
+            check_y(self.y.cpu().numpy(), ref["y"])
+        return ref
+
+
+def random_list(env, M, seed, n=6):
+    rng = np.random.default_rng([91, seed, M])
+    cases = []
+    for i in range(n):
+        K = 64 * int(rng.integers(1, 129))
+        nseg = int(rng.integers(1, 5))
+        segs = tuple(int(v) for v in rng.integers(0 if i == 2 else 1, 300, size=nseg))
+        W, segs, x = wl.random_case(seed=1000 * seed + i, M=M, K=K, seg_rows=segs)
+        cases.append(Case(env, W, segs, x, want_acc=i != 4, want_y=i != 5))
+    # the extremes of K
+    W, segs, x = wl.random_case(seed=1000 * seed + 77, M=M, K=64, seg_rows=(17,))
+    cases.append(Case(env, W, segs, x))
+    W, segs, x = wl.random_case(seed=1000 * seed + 78, M=M, K=8192, seg_rows=(40, 9))
+    cases.append(Case(env, W, segs, x))
+    return cases
+
+
+@pytest.mark.parametrize("M", list(range(1, 17)))
+def test_sweep_random_lists(env, M):
+    torch, twd, orc = env
+    cases = random_list(env, M, seed=M)
+    log(f"sweep random list M={M}: " + ", ".join(
+        f"K={c.x.shape[1]} segs={c.segs}" for c in cases))
+    sw = twd.Sweep([c.entry() for c in cases])
+    sw.run()
+    torch.cuda.synchronize()
+    for c in cases:
+        c.check(orc)
+
+
+@pytest.mark.parametrize("M", [1, 3, 16])
+def test_sweep_zero_rows_and_empty_projections(env, M):
+    """All-zero token rows (scale 0, outputs 0) and projections with N = 0."""
+    torch, twd, orc = env
+    W, segs, x = wl.random_case(seed=5, M=M, K=2560, seg_rows=(70, 3))
+    xf = wl.bf16_bits_to_f32(x).copy()
+    xf[0] = 0.0
+    x = wl.f32_to_bf16_bits(xf)
+    W0, segs0, x0 = wl.random_case(seed=6, M=M, K=512, seg_rows=(0,))
+    cases = [Case(env, W0, segs0, x0), Case(env, W, segs, x), Case(env, W0, segs0, x0)]
+    sw = twd.Sweep([c.entry() for c in cases])
+    sw.run()
+    torch.cuda.synchronize()
+    cases[1].check(orc)
+    assert not cases[1].acc[0].any() and not cases[1].y[0].any()
+
+
+@pytest.mark.parametrize("M", list(range(1, 17)))
+def test_sweep_full_size_layer_every_width(env, M):
+    """One full-size 2B-class layer (all four projections) on the outlier
+    workload, at every width, in one sweep."""
+    torch, twd, orc = env
+    ls = wl.SET_2B
+    layer = (7 * M) % ls.layers
+    cases = []
+    for pi, proj in enumerate(ls.projs):
+        W = wl.layer_weights(ls, layer, pi)
+        x = wl.layer_activations("2b_sweep_outlier", proj.K, M, layer, pi, outliers=True)
+        cases.append(Case(env, W, proj.segs, x))
+    log(f"sweep full-size 2B layer {layer} M={M}")
+    sw = twd.Sweep([c.entry() for c in cases])
+    sw.run()
+    torch.cuda.synchronize()
+    threads = orc.max_threads()
+    for c in cases:
+        c.check(orc, orc.forward(c.W, c.segs, c.x, threads=threads))
+
+
+def test_sweep_whole_2b_set_m1(env):
+    """The benchmark's M = 1 launch: all 120 projections of the 30-layer 2B
+    set in one sweep.  Every output equals the per-projection launch; sampled
+    rows of every projection equal the oracle (ternarized over the whole
+    segment, contracted on the sampled rows)."""
+    torch, twd, orc = env
+    ls = wl.SET_2B
+    M = 1
+    rng = np.random.default_rng(123)
+    entries, refs = [], []
+    for layer in range(ls.layers):
+        for pi, proj in enumerate(ls.projs):
+            W = wl.layer_weights(ls, layer, pi)
+            x = wl.layer_activations("2b_decode", proj.K, M, layer, pi)
+            packed, gammas = twd.prepare_weights(W, proj.segs)
+            # the oracle on sampled rows (gamma over the whole segment)
+            t, gam, grow = orc.ternarize_segments(W, proj.segs)
+            assert gam == list(gammas)
+            rows = np.sort(rng.choice(proj.N, 24, replace=False))
+            q, s = orc.quantize_act(x)
+            ra = orc.linear(q, t[rows])
+            refs.append((layer, pi, rows, ra, orc.dequant(ra, s, grow[rows])))
+            del W, t
+            entries.append((torch.from_numpy(packed).cuda(), proj.segs, gammas,
+                            dev_bf16(torch, x),
+                            torch.full((M, proj.N), -7, dtype=torch.int32, device="cuda"),
+                            torch.full((M, proj.N), -7.0, device="cuda")))
+    log("sweep whole 2B set M=1: planned")
+    sw = twd.Sweep(entries)
+    assert sw.weight_bytes == ls.packed_bytes
+    sw.run()
+    torch.cuda.synchronize()
+    for (wp, segs, gammas, xd, acc, y), (layer, pi, rows, ra, ry) in zip(entries, refs):
+        a2, y2 = twd.ternary_linear_bf16(wp, segs, gammas, xd)
+        torch.cuda.synchronize()
+        assert torch.equal(acc, a2), (layer, pi)
+        assert torch.equal(y, y2), (layer, pi)
+        np.testing.assert_array_equal(acc.cpu().numpy()[:, rows], ra)
+        check_y(y.cpu().numpy()[:, rows], ry, f"{layer},{pi}")
+
+
+def test_sweep_graph_replays_match_oracle(env):
+    """A sweep captured into a graph: three replays, with eager work and
+    synchronization between them, each checked against the oracle."""
+    torch, twd, orc = env
+    cases = random_list(env, 5, seed=50, n=4)
+    refs = [orc.forward(c.W, c.segs, c.x) for c in cases]
+    sw = twd.Sweep([c.entry() for c in cases])
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        sw.run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            sw.run()
+    for rep in range(3):
+        for c in cases:
+            if c.acc is not None:
+                c.acc.fill_(-1)
+            if c.y is not None:
+                c.y.fill_(-1.0)
+        g.replay()
+        torch.cuda.synchronize()
+        for c, ref in zip(cases, refs):
+            c.check(orc, ref)
+        _ = sum(float(c.y.sum()) for c in cases if c.y is not None)  # eager work
+
+
+def test_sweep_table_mismatch_writes_nothing(env):
+    """A plan whose check value is not the table's: the launch returns
+    without writing any output."""
+    torch, twd, orc = env
+    cases = random_list(env, 2, seed=60, n=2)
+    sw = twd.Sweep([c.entry() for c in cases])
+    sw.plan.check ^= 0x5A5A5A5A
+    sw.run()
+    torch.cuda.synchronize()
+    for c in cases:
+        if c.acc is not None:
+            assert bool((c.acc == -7).all())
+        if c.y is not None:
+            assert bool((c.y == -7.0).all())
+    sw.plan.check ^= 0x5A5A5A5A
+    sw.run()
+    torch.cuda.synchronize()
+    for c in cases:
+        c.check(orc)
+
+
+def test_sweep_errors(env):
+    torch, twd, orc = env
+    W, segs, x = wl.random_case(seed=8, M=2, K=256, seg_rows=(16,))
+    c = Case(env, W, segs, x)
+    with pytest.raises(ValueError):
+        twd.Sweep([])
+    bad = wl.random_case(seed=8, M=2, K=100, seg_rows=(16,))
+    with pytest.raises(twd.TwdError) as e:
+        xb = torch.zeros((2, 100), dtype=torch.bfloat16, device="cuda")
+        twd.Sweep([(c.wp, segs, c.gammas, xb, None, c.y)])
+    assert e.value.status == 2
+    with pytest.raises(twd.TwdError) as e:
+        twd.Sweep([(c.wp, segs, c.gammas, c.xd, None, None)])
+    assert e.value.status == 1
+    with pytest.raises(ValueError):
+        x3 = torch.zeros((3, 256), dtype=torch.bfloat16, device="cuda")
+        twd.Sweep([c.entry(), (c.wp, segs, c.gammas, x3, None, None)])
+    del bad

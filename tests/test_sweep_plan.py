@@ -1,0 +1,156 @@
+"""Host logic of the multi-projection sweep (no GPU): the planner's table
+image, decoded field by field, must cover every 16-row tile of every
+projection exactly once, in order, with at most four projections per
+workgroup, consistent LDS offsets and a check value bound to the table's
+device address; bad arguments must be rejected before anything is written.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+
+import ternary_weight_decode_amd as twd
+
+HEADER = np.dtype([("magic", "<u4"), ("check", "<u4"), ("nproj", "<i4"), ("nwg", "<i4"),
+                   ("M", "<i4"), ("lds", "<i4"), ("proj_off", "<i4"), ("work_off", "<i4"),
+                   ("weight_bytes", "<i8"), ("pad", "<i4", 6)])
+PROJ = np.dtype([("w", "<u8"), ("x", "<u8"), ("acc", "<u8"), ("y", "<u8"), ("K", "<i4"),
+                 ("N", "<i4"), ("passes", "<i4"), ("slices", "<i4"), ("stride", "<i4"),
+                 ("nseg", "<i4"), ("bound", "<i4", 4), ("gamma", "<f4", 4), ("pad", "<i4", 2)])
+WORK = np.dtype([("nspan", "<i4"), ("pad", "<i4", 3), ("span", "<i4", (4, 4))])
+LDS_HEADER = 64 + 3 * 4 * 16 * 4
+MAX_SPANS = 4
+
+
+def fake_list(shapes, base=1 << 32):
+    """(K, seg_rows) list -> descriptors with distinct aligned fake pointers
+    (the planner never dereferences them)."""
+    rows = []
+    for i, (K, segs) in enumerate(shapes):
+        p = base + (i << 24)
+        rows.append((p, p + (1 << 20), p + (2 << 20), p + (3 << 20), K, segs,
+                     [0.5 + i] * len(segs)))
+    return rows
+
+
+def decode(img):
+    h = np.frombuffer(img[:64].tobytes(), HEADER)[0]
+    projs = np.frombuffer(img[h["proj_off"]:h["proj_off"] + 96 * h["nproj"]].tobytes(), PROJ)
+    work = np.frombuffer(img[h["work_off"]:h["work_off"] + 80 * h["nwg"]].tobytes(), WORK)
+    return h, projs, work
+
+
+def plan(shapes, M, table_dev=0x7F0000000000):
+    descs = twd.sweep_descs(fake_list(shapes), M)
+    img, p = twd.sweep_encode(descs, M, table_dev)
+    return img, p
+
+
+def stride(K):
+    return -(-K // 256) * 256 + 16
+
+
+SHAPE_LISTS = [
+    [(2560, (2560, 640, 640)), (2560, (2560,)), (2560, (6912, 6912)), (6912, (2560,))] * 3,
+    [(64, (1,)), (8192, (33, 7)), (320, (0,)), (1536, (64, 33, 33, 5)), (256, (700,))],
+    [(256, (16,))] * 40,           # many small projections: span limit
+    [(8192, (5000,)), (64, (3,))],
+]
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+@pytest.mark.parametrize("li", range(len(SHAPE_LISTS)))
+def test_plan_covers_every_tile_once(li, M):
+    shapes = SHAPE_LISTS[li]
+    img, p = plan(shapes, M)
+    h, projs, work = decode(img)
+    assert h["magic"] == 0x53445754 and h["nproj"] == len(shapes) and h["M"] == M
+    assert p.nwg == h["nwg"] == len(work) and p.lds_bytes == h["lds"]
+    assert p.check == h["check"] != 0 and p.table_bytes == img.size
+    total = sum(K * sum(s) // 4 for K, s in shapes)
+    assert h["weight_bytes"] == total == p.weight_bytes
+    for i, (K, segs) in enumerate(shapes):
+        d = projs[i]
+        assert (d["K"], d["N"]) == (K, sum(segs))
+        assert d["slices"] == -(-K // 256) and d["passes"] == -(-d["slices"] // 4)
+        assert d["stride"] == stride(K) and d["nseg"] == len(segs)
+        assert list(d["bound"][:len(segs)]) == list(np.cumsum(segs))
+    seen = []
+    for w in work:
+        n = int(w["nspan"])
+        assert 1 <= n <= MAX_SPANS or (n == 0 and total == 0)
+        lds = LDS_HEADER
+        for s in range(n):
+            q, t0, t1, xoff = (int(v) for v in w["span"][s])
+            assert xoff == lds - LDS_HEADER
+            lds += M * stride(shapes[q][0])
+            assert t0 < t1
+            seen.extend((q, t) for t in range(t0, t1))
+        assert lds <= h["lds"] <= 160 * 1024
+    expect = [(q, t) for q, (K, s) in enumerate(shapes) for t in range(-(-sum(s) // 16))]
+    assert seen == expect
+
+
+def test_plan_balances_bytes():
+    """The 2B-class layer set: workgroups carry about equal weight bytes."""
+    ls = [(2560, (2560, 640, 640)), (2560, (2560,)), (2560, (6912, 6912)), (6912, (2560,))] * 30
+    img, p = plan(ls, 1)
+    h, projs, work = decode(img)
+    sizes = []
+    for w in work:
+        b = 0
+        for s in range(int(w["nspan"])):
+            q, t0, t1, _ = (int(v) for v in w["span"][s])
+            b += (t1 - t0) * 16 * ls[q][0] // 4
+        sizes.append(b)
+    sizes = np.array(sizes)
+    assert sizes.sum() == h["weight_bytes"]
+    assert 1000 <= len(sizes) <= 1200
+    # the cuts fall on tile boundaries; apart from the pieces cut at
+    # projection boundaries no workgroup exceeds the mean by more than a tile
+    assert sizes.max() <= h["weight_bytes"] / 1024 + 16 * 6912 // 4
+
+
+def test_check_binds_device_address():
+    shapes = SHAPE_LISTS[0]
+    img1, p1 = plan(shapes, 2, table_dev=0x7F0000000000)
+    img2, p2 = plan(shapes, 2, table_dev=0x7F0000001000)
+    assert p1.check != p2.check
+    assert p1.table == 0x7F0000000000
+
+
+def test_plan_errors():
+    good = fake_list([(256, (16,))])
+    with pytest.raises(twd.TwdError) as e:
+        plan([(100, (16,))], 1)
+    assert e.value.status == 2
+    with pytest.raises(twd.TwdError) as e:
+        plan([(256, (16,))], 0)
+    assert e.value.status == 2
+    with pytest.raises(twd.TwdError) as e:
+        plan([(256, (16,))], 17)
+    assert e.value.status == 2
+    with pytest.raises(twd.TwdError) as e:
+        plan([(16384, (16,))], 1)
+    assert e.value.status == 2
+    # misaligned weights, missing outputs, negative segment
+    for mutate in (lambda r: (r[0] + 8,) + r[1:], lambda r: r[:2] + (None, None) + r[4:],
+                   lambda r: r[:5] + ((-1,),) + r[6:]):
+        descs = twd.sweep_descs([mutate(good[0])], 1)
+        with pytest.raises(twd.TwdError) as e:
+            twd.sweep_encode(descs, 1, 0x7F0000000000)
+        assert e.value.status == 1
+    # a table too small, a misaligned device table
+    descs = twd.sweep_descs(good, 1)
+    n = ctypes.c_int64(0)
+    assert twd._lib_sweep_bytes(descs, 1, 1, ctypes.byref(n)) == 0
+    img = np.zeros(n.value, np.uint8)
+    pl = twd.SweepPlan()
+    assert twd._lib_sweep_encode(descs, 1, 1, ctypes.c_void_p(0x7F0000000000),
+                                 twd._np_ptr(img), n.value - 1, ctypes.byref(pl)) == 1
+    assert twd._lib_sweep_encode(descs, 1, 1, ctypes.c_void_p(0x7F0000000008),
+                                 twd._np_ptr(img), n.value, ctypes.byref(pl)) == 1
+    # a launch with a plan out of range is refused before anything runs
+    pl.table = 0x7F0000000000
+    pl.M = 0
+    assert twd._lib_sweep(ctypes.byref(pl), None) == 1
