@@ -282,7 +282,26 @@ twd_status twd_kv_commit(void *const *segments, int nseg, int64_t seg0_positions
  * bit-identical, y within the fp32 evaluation of acc * s_m * gamma.
  * ---------------------------------------------------------------------- */
 
-/* One projection of a sweep.  wpacked: device [N][K/4] (16-byte aligned);
+/* Bytes of a projection's weights in the sweep's tiled layout: ceil(N / 16)
+ * tiles of ceil(K / 256) KiB; -1 if N < 0 or K is not a non-negative
+ * multiple of 64. */
+int64_t twd_sweep_tiled_bytes(int64_t N, int64_t K);
+
+/* Reorder packed weights [N][K/4] (the format above; host memory) into the
+ * sweep's tiled layout (host memory, twd_sweep_tiled_bytes(N, K) bytes):
+ * tile t (rows 16 t .. 16 t + 15) is a contiguous run of ceil(K / 256)
+ * blocks of 1 KiB; block u holds, at position l = 16 g + r (16 bytes each),
+ * packed bytes 64 u + 16 g .. 64 u + 16 g + 15 of row 16 t + r.  Zero bytes
+ * pad rows past N and bytes past K / 4; a zero field contributes nothing to
+ * the sweep's sums.  So every 1 KiB block is one whole-line load that is
+ * the matrix-core operand as it stands.  Host, offline, like packing.
+ * Errors: INVALID_ARG (null pointers, N < 0, K not a multiple of 64). */
+twd_status twd_sweep_tile_weights(const uint8_t *packed, int64_t N, int64_t K,
+                                  uint8_t *tiled);
+
+/* One projection of a sweep.  wpacked: device, the projection's packed
+ * weights in the sweep's tiled layout (twd_sweep_tile_weights; 16-byte
+ * aligned);
  * x_bf16: device [M][K] bf16 bit patterns (16-byte aligned); acc: device
  * int32 [M][N] or NULL; y: device fp32 [M][N] or NULL (not both NULL; 4-byte
  * aligned); segments as in twd_ternary_linear_fused (N = sum of seg_rows,

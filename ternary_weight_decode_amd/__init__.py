@@ -90,6 +90,8 @@ class SweepPlan(ctypes.Structure):
                 ("reserved", ctypes.c_int32 * 3)]
 
 
+_lib_tiled_bytes = _sig("twd_sweep_tiled_bytes", [_i64, _i64], _i64)
+_lib_tile = _sig("twd_sweep_tile_weights", [_p, _i64, _i64, _p])
 _lib_sweep_bytes = _sig("twd_sweep_table_bytes", [_p, _int, _i64, _p])
 _lib_sweep_encode = _sig("twd_sweep_encode", [_p, _int, _i64, _p, _p, _i64, _p])
 _lib_sweep = _sig("twd_ternary_sweep", [_p, _p])
@@ -101,6 +103,7 @@ EXPORTS = ("twd_version", "twd_last_error", "twd_ternarize_absmean",
            "twd_ternary_linear_fused_kernel", "twd_ternary_linear_bf16",
            "twd_select_kernel", "twd_quantize_fp8_rows", "twd_projection_fp8",
            "twd_projection_bf16", "twd_kv_commit", "twd_stream_read", "twd_stream_copy",
+           "twd_sweep_tiled_bytes", "twd_sweep_tile_weights",
            "twd_sweep_table_bytes", "twd_sweep_encode", "twd_ternary_sweep")
 
 
@@ -408,6 +411,24 @@ def stream_copy(src, dst, nbytes: int, stream=None):
 
 # ------------------------------------------------------ multi-projection sweep
 
+def sweep_tiled_bytes(N: int, K: int) -> int:
+    """Bytes of [N, K] weights in the sweep's tiled layout."""
+    n = int(_lib_tiled_bytes(int(N), int(K)))
+    if n < 0:
+        raise ValueError("N must be >= 0 and K a multiple of 64")
+    return n
+
+
+def tile_for_sweep(packed: np.ndarray, N: int, K: int) -> np.ndarray:
+    """Packed weights [N, K/4] (host) -> the sweep's tiled layout (host
+    uint8, sweep_tiled_bytes(N, K) bytes)."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint8).reshape(-1)
+    _need(packed.size == N * K // 4, "packed size does not match N*K/4")
+    out = np.empty(sweep_tiled_bytes(N, K), np.uint8)
+    _check(_lib_tile(_np_ptr(packed), int(N), int(K), _np_ptr(out)))
+    return out
+
+
 def sweep_descs(projs, M: int):
     """ctypes array of twd_sweep_proj from (wpacked_ptr, x_ptr, acc_ptr, y_ptr,
     K, seg_rows, seg_gamma) tuples of plain integers (host-side planning)."""
@@ -439,8 +460,9 @@ def sweep_encode(descs, M: int, table_dev_ptr: int):
 class Sweep:
     """One launch over a list of independent projections at width M.
 
-    projs: sequence of (wpacked, seg_rows, seg_gamma, x, acc, y) with device
-    tensors wpacked (uint8, N*K/4 bytes), x (bf16 [M, K]), acc (int32 [M, N]
+    projs: sequence of (wtiled, seg_rows, seg_gamma, x, acc, y) with device
+    tensors wtiled (uint8, the weights in the sweep's tiled layout:
+    tile_for_sweep), x (bf16 [M, K]), acc (int32 [M, N]
     or None), y (fp32 [M, N] or None).  The table is planned on the host,
     copied once to a device buffer held by this object, and every run() is a
     single asynchronous launch on the stream (capturable into a graph).  The
@@ -459,7 +481,9 @@ class Sweep:
             M = m if M is None else M
             _need(m == M, "every projection takes the same M")
             N = int(sum(int(r) for r in seg_rows))
-            _need(_nbytes(w) >= N * K // 4, "wpacked holds fewer than N*K/4 bytes")
+            need = int(_lib_tiled_bytes(N, int(K)))  # -1: a K the library rejects below
+            _need(_nbytes(w) >= need,
+                  "the tiled weights hold fewer than sweep_tiled_bytes(N, K) bytes")
             _need(acc is None or tuple(acc.shape) == (M, N), "acc must be [M, N]")
             _need(y is None or tuple(y.shape) == (M, N), "y must be [M, N]")
             ptr = lambda t, name, dt: (_dev_ptr(t, name, dt).value if t is not None else None)

@@ -194,3 +194,42 @@ extern "C" twd_status twd_quantize_fp8_rows(const float *W, int64_t N, int64_t K
     }
     return TWD_OK;
 }
+
+// The multi-projection sweep's tiled weight layout: 16-row tiles, each a
+// contiguous run of one 1 KiB block per 256-wide K slice; block u of tile t
+// holds, at lane l = 16 g + r (16 bytes each), the packed bytes 64 u + 16 g
+// .. + 15 of row 16 t + r.  Zeros pad rows past N and bytes past K / 4 (a
+// zero byte is code 0 in every field, which the kernels read as "contributes
+// nothing": their sums run over c = t + 1 and subtract the activation sum
+// over the real K only).
+extern "C" int64_t twd_sweep_tiled_bytes(int64_t N, int64_t K) {
+    if (N < 0 || K < 0 || K % 64 != 0)
+        return -1;
+    return ((N + 15) / 16) * ((K + 255) / 256) * 1024;
+}
+
+extern "C" twd_status twd_sweep_tile_weights(const uint8_t *packed, int64_t N, int64_t K,
+                                             uint8_t *tiled) {
+    using twd::set_error;
+    if (N < 0 || K < 0 || K % 64 != 0)
+        return set_error(TWD_ERR_INVALID_ARG,
+                         "sweep_tile_weights: need N >= 0 and K a non-negative multiple of 64");
+    if ((N > 0 && K > 0) && (!packed || !tiled))
+        return set_error(TWD_ERR_INVALID_ARG, "sweep_tile_weights: null pointer");
+    const int64_t RB = K / 4;
+    const int64_t tiles = (N + 15) / 16;
+    const int64_t slices = (K + 255) / 256;
+    for (int64_t t = 0; t < tiles; ++t)
+        for (int64_t u = 0; u < slices; ++u)
+            for (int l = 0; l < 64; ++l) {
+                const int r = l & 15, g = l >> 4;
+                const int64_t row = 16 * t + r;
+                const int64_t col = 64 * u + 16 * g;
+                uint8_t *dst = tiled + ((t * slices + u) * 64 + l) * 16;
+                if (row < N && col < RB)
+                    std::memcpy(dst, packed + row * RB + col, 16);
+                else
+                    std::memset(dst, 0, 16);
+            }
+    return TWD_OK;
+}

@@ -1,7 +1,8 @@
 // Measurement references.  stream_read: the achievable-bandwidth reference,
-// a plain streaming read with the linear kernels' load shape and cache
-// policy (16-byte non-temporal loads, four in flight per lane, 256-thread
-// workgroups); it reduces what it reads
+// a plain streaming read with the linear kernels' cache policy (16-byte
+// non-temporal loads) that fills the chip: at least one 256-thread workgroup
+// per compute unit (four per unit for large buffers), each lane keeping up to
+// eight loads in flight over a grid-stride loop.  It reduces what it reads
 // to one word and stores it only when it equals a guard value, so the loads
 // cannot be removed.  stream_copy: a plain copy of known size, the
 // calibration for the HBM byte counters (bytes read = bytes written = size).
@@ -11,28 +12,30 @@ namespace twd {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kLoads = 4;
+constexpr int kLoads = 4;         // copy kernel: 16-byte words per lane
+constexpr int kReadLoads = 8;     // read kernel: loads in flight per lane
+constexpr int kCUs = 256;         // compute units of an MI355X
+constexpr int kMaxReadGroups = 4 * kCUs;
 
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(kThreads) void stream_read_kernel(
     const uint4 *__restrict__ p, int64_t n16, uint32_t *__restrict__ sink) {
-    const int64_t base = static_cast<int64_t>(blockIdx.x) * kThreads * kLoads + threadIdx.x;
-    uint4 v[kLoads];
-#pragma unroll
-    for (int u = 0; u < kLoads; ++u) {
-        const int64_t i = base + static_cast<int64_t>(u) * kThreads;
-        if (i < n16) {
-            const v4u w = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p + i));
-            v[u] = make_uint4(w[0], w[1], w[2], w[3]);
-        } else {
-            v[u] = make_uint4(0u, 0u, 0u, 0u);
-        }
-    }
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
     uint32_t h = 0;
+    for (int64_t base = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; base < n16;
+         base += stride * kReadLoads) {
+        v4u v[kReadLoads];
 #pragma unroll
-    for (int u = 0; u < kLoads; ++u)
-        h ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+        for (int u = 0; u < kReadLoads; ++u) {
+            const int64_t i = base + u * stride;
+            v[u] = i < n16 ? __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p + i))
+                           : v4u{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < kReadLoads; ++u)
+            h ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    }
     if (h == 0x9E3779B9u)
         sink[threadIdx.x] = h;
 }
@@ -70,7 +73,10 @@ hipError_t launch_stream_copy(const void *src, void *dst, int64_t bytes,
 hipError_t launch_stream_read(const void *buf, int64_t bytes, uint32_t *sink,
                               hipStream_t stream) {
     const int64_t n16 = bytes / 16;
-    const int64_t grid = (n16 + kThreads * kLoads - 1) / (kThreads * kLoads);
+    // one workgroup per compute unit at least; more (up to four per unit)
+    // while each lane still gets all eight of its loads
+    int64_t grid = (n16 + int64_t(kThreads) * kReadLoads - 1) / (int64_t(kThreads) * kReadLoads);
+    grid = grid < kCUs ? kCUs : grid > kMaxReadGroups ? kMaxReadGroups : grid;
     hipLaunchKernelGGL(stream_read_kernel, dim3(static_cast<uint32_t>(grid)),
                        dim3(kThreads), 0, stream,
                        static_cast<const uint4 *>(buf), n16, sink);

@@ -20,15 +20,12 @@ bool aligned(const void *p, uintptr_t a) {
 // that the 16 token rows of a B-operand read fall on different bank groups.
 int stride_bytes(int K) { return ((K + 255) / 256) * 256 + 16; }
 
-// Workgroups the planner aims for: four per compute unit of an MI355X
-// (256 CUs), fewer when the list is small, so that each workgroup still gets
-// several tiles per wave.
-constexpr int64_t kTargetWorkgroups = 1024;
-constexpr int64_t kMinTilesPerWorkgroup = 8;
-// LDS the planner lets one workgroup's staged activations take before it
-// starts a new workgroup at a projection boundary (a single projection may
-// take more, up to the 160 KiB of a compute unit).
-constexpr int kLdsSoftCap = 40 * 1024;
+// Workgroups the planner aims for fill every compute unit with the
+// resident waves the kernel is built for, fewer when the list is small, so that each wave
+// still gets a few tiles.  A workgroup's staged activations may take its
+// share of the compute unit's 160 KiB of LDS before the planner starts a new
+// workgroup at a projection boundary (a single projection may take more).
+constexpr int64_t kMinTilesPerWave = 2;
 constexpr int kLdsHardCap = 160 * 1024;
 
 uint32_t fnv1a(const uint8_t *p, size_t n) {
@@ -121,8 +118,12 @@ twd_status sweep_plan(const twd_sweep_proj *projs, int nproj, int64_t M, const v
     // Cut the tile sequence: a tile goes to the range of its first byte, and
     // a new workgroup also starts where one more projection would exceed the
     // span count or the LDS cap.
-    int64_t groups = tiles_total / kMinTilesPerWorkgroup;
-    groups = groups < 1 ? 1 : groups > kTargetWorkgroups ? kTargetWorkgroups : groups;
+    const int nw = sweep_waves(m);
+    const int cu_waves = 4 * sweep_simd_waves(m);
+    const int64_t target = int64_t(kSweepCUs) * cu_waves / nw;
+    const int lds_soft = kLdsHardCap * nw / cu_waves;
+    int64_t groups = tiles_total / (kMinTilesPerWave * nw);
+    groups = groups < 1 ? 1 : groups > target ? target : groups;
     std::vector<SweepWork> work;
     int lds_max = kSweepLdsHeader;
     SweepWork cur;
@@ -143,16 +144,16 @@ twd_status sweep_plan(const twd_sweep_proj *projs, int nproj, int64_t M, const v
         const SweepProj &d = P[q];
         const int tiles = (d.N + 15) / 16;
         for (int t = 0; t < tiles; ++t) {
-            const int64_t target = total > 0 ? cum * groups / total : 0;
-            if (target != cur_target) {
+            const int64_t range = total > 0 ? cum * groups / total : 0;
+            if (range != cur_target) {
                 close();
-                cur_target = target;
+                cur_target = range;
             }
             SweepSpan *last = cur.nspan ? &cur.span[cur.nspan - 1] : nullptr;
             if (!last || last->q != q) {
                 const int need = m * d.stride;
                 if (cur.nspan == kSweepMaxSpans ||
-                    (cur.nspan > 0 && cur_lds + need > kLdsSoftCap))
+                    (cur.nspan > 0 && cur_lds + need > lds_soft))
                     close();
                 SweepSpan &sp = cur.span[cur.nspan++];
                 sp.q = q;

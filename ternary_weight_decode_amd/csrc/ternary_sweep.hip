@@ -20,18 +20,20 @@
 // across tile and projection boundaries, with no barrier and no kernel
 // boundary until the list ends.
 //
-// Work split.  Wave w of a workgroup takes tiles w, w + 4, ... of the
-// workgroup's range.  A tile (16 weight rows, all of K) is read in passes of
-// four 256-wide K slices: per lane four 16-byte loads, issued as two whole
-// 128-byte lines per row pair (the tile kernel's layout: loads X of rows 0-7
-// and Y of rows 8-15, rebuilt into the matrix-core A operand by a lane
-// select and a DPP rotation).  A three-slot register ring holds the pass
-// being computed and the next two passes' loads.  Each slice is decoded into
-// four byte planes (codes c = t + 1 scaled 1, 4, 16, 1), the A operands of
-// four v_mfma_i32_16x16x64_i8 with their own accumulators; B is the staged
-// int8 activation block (token columns at or past M read a zero block).
-// After a tile's last pass, lane (token r, group g) holds rows 4g..4g+3 for
-// token r: sum q t = sum q c - sum q, then the dequant epilogue.
+// Work split.  The waves of a workgroup take its tiles in turn (the turn
+// carries over from one projection to the next).  A tile (16 weight rows,
+// all of K) is read in passes of four 256-wide K slices.  The weights come in
+// the sweep's tiled layout (twd_sweep_tile_weights): tile t is a contiguous
+// run of ceil(K / 256) blocks of 1 KiB, block u holding, at lane l = 16 g +
+// r, the 16 packed bytes of tile row r at K offset 256 u + 64 g -- so each
+// pass is four whole-line loads of 1 KiB each, and each load is the
+// matrix-core A operand as it stands.  A register ring holds the pass being
+// computed and the next passes' loads.  Each slice is decoded into four byte
+// planes (codes c = t + 1 scaled 1, 4, 16, 1), the A operands of four
+// v_mfma_i32_16x16x64_i8 with their own accumulators; B is the staged int8
+// activation block (token columns at or past M read a zero block).  After a
+// tile's last pass, lane (token r, group g) holds rows 4g..4g+3 for token r:
+// sum q t = sum q c - sum q, then the dequant epilogue.
 #include "kernel_common.h"
 
 namespace twd {
@@ -41,7 +43,6 @@ using namespace kern;
 
 constexpr int kRawBufferFlags = 0x00020000;  // raw buffer, 32-bit format
 constexpr uint32_t kOutOfRange = 0x80000000u;
-constexpr int kS = 3;  // register ring slots: the pass computed + two in flight
 
 // The table is read-only for the whole launch: reading it through the
 // constant address space gives scalar loads, which wait on the scalar
@@ -70,12 +71,6 @@ __device__ __forceinline__ Segments segs_of(cptr<SweepProj> P) {
     return sg;
 }
 
-// Rotate a value by 8 lanes within each 16-lane row (DPP row_ror:8).
-__device__ __forceinline__ uint32_t ror8(uint32_t v) {
-    return static_cast<uint32_t>(
-        __builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x128, 0xf, 0xf, false));
-}
-
 // Staged activation layout: word 16 g + 4 d + j of a 64-word slice is stored
 // at 16 g + 4 j + d, so one 16-byte read gives the B operand of plane j.
 __device__ __forceinline__ int permuted_word(int w) {
@@ -101,31 +96,24 @@ __device__ __forceinline__ void step(PassPos &c, int passes) {
 
 // Weights of a span's projection, as the loads need them.
 struct SpanW {
-    const uint8_t *w;
-    int RB;  // bytes per weight row, K / 4
-    int N;
-    int t1;  // end tile of the span
+    const uint8_t *w;  // tiled weights
+    int tile_bytes;    // 1 KiB per 256-wide slice
+    int t1;            // end tile of the span
 };
 
-// Issue one pass's weight loads (kSweepLP slices) into ring slot a; a pass
-// past the span's last tile issues loads with an empty descriptor (zeros, no
-// memory traffic), which keeps the count of loads in flight fixed.
-__device__ __forceinline__ void issue(const SpanW &sw, const PassPos &c, int r, int g,
+// Issue one pass's weight loads (kSweepLP slices of 1 KiB) into ring slot a;
+// slices past K, and a pass past the span's last tile (an empty descriptor),
+// load zeros without memory traffic, which keeps the count of loads in
+// flight fixed.
+__device__ __forceinline__ void issue(const SpanW &sw, const PassPos &c, int lane,
                                       uint4 (&a)[kSweepLP]) {
     const bool valid = c.t < sw.t1;
-    const int n0 = 16 * c.t;
-    const int rows = valid ? min(16, sw.N - n0) : 0;
-    const uint8_t *base = valid ? sw.w + static_cast<int64_t>(n0) * sw.RB : sw.w;
+    const uint8_t *base = sw.w + static_cast<int64_t>(valid ? c.t : 0) * sw.tile_bytes;
     const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t *>(base), 0, rows * sw.RB, kRawBufferFlags);
-    const int hi = r >> 3;
+        const_cast<uint8_t *>(base), 0, valid ? sw.tile_bytes : 0, kRawBufferFlags);
 #pragma unroll
     for (int i = 0; i < kSweepLP; ++i) {
-        const int u = kSweepLP * c.p + i;
-        const int row = (i & 1) ? 8 + (r & 7) : (r & 7);
-        const int col = 128 * (u >> 1) + 16 * (g + 4 * ((i & 1) ? 1 - hi : hi));
-        const uint32_t off =
-            col < sw.RB ? static_cast<uint32_t>(row * sw.RB + col) : kOutOfRange;
+        const uint32_t off = static_cast<uint32_t>(1024 * (kSweepLP * c.p + i) + 16 * lane);
         const auto v = __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, kWeightPolicy);
         a[i] = make_uint4(v[0], v[1], v[2], v[3]);
     }
@@ -136,7 +124,7 @@ __device__ __forceinline__ void issue(const SpanW &sw, const PassPos &c, int r, 
 // consuming every ring register on every path keeps the compiler's
 // vector-memory waits exact, so two passes stay in flight.
 __device__ __forceinline__ void compute(int p, int slices, const uint8_t *bsrc, int ustep,
-                                        const uint8_t *zero, int r,
+                                        const uint8_t *zero,
                                         const uint4 (&a)[kSweepLP], v4i &c0, v4i &c3,
                                         v4i &c4, v4i &c16) {
     if (p == 0) {
@@ -145,7 +133,6 @@ __device__ __forceinline__ void compute(int p, int slices, const uint8_t *bsrc, 
         c4 = c0;
         c16 = c0;
     }
-    const int hi = r >> 3;
 #pragma unroll
     for (int i = 0; i < kSweepLP; ++i) {
         const int u = kSweepLP * p + i;
@@ -154,18 +141,8 @@ __device__ __forceinline__ void compute(int p, int slices, const uint8_t *bsrc, 
         const v4i b1 = *reinterpret_cast<const v4i *>(bu + 16);
         const v4i b2 = *reinterpret_cast<const v4i *>(bu + 32);
         const v4i b3 = *reinterpret_cast<const v4i *>(bu + 48);
-        // even slice of a pair: X (rows 0-7) where r < 8, else Y; odd
-        // slice: the other load, rotated 8 lanes along the 16-lane row
-        uint4 au;
-        const uint4 x = a[i & ~1], yv = a[i | 1];
-        if ((i & 1) == 0) {
-            au = hi ? yv : x;
-        } else {
-            const uint4 z = hi ? x : yv;
-            au = make_uint4(ror8(z.x), ror8(z.y), ror8(z.z), ror8(z.w));
-        }
-        const v4i w = {static_cast<int>(au.x), static_cast<int>(au.y),
-                       static_cast<int>(au.z), static_cast<int>(au.w)};
+        const v4i w = {static_cast<int>(a[i].x), static_cast<int>(a[i].y),
+                       static_cast<int>(a[i].z), static_cast<int>(a[i].w)};
         const v4i p0 = w & static_cast<int>(kPlane0);
         const v4i p1 = w & static_cast<int>(kPlane1);
         const v4i p2 = w & static_cast<int>(kPlane2);
@@ -208,11 +185,12 @@ __device__ __forceinline__ void epilogue(const SpanOut &so, int t, int r, int g,
     }
 }
 
-template <int M, int NW>
-__global__ __launch_bounds__(64 * NW) void sweep_kernel(const SweepHeader *header_g,
-                                                        const SweepProj *projs_g,
-                                                        const SweepWork *work_g,
-                                                        uint32_t check) {
+// Built for SW resident waves per SIMD (512 / SW registers per lane) with a
+// register ring of kS passes.
+template <int M, int NW, int kS, int SW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(SW)))
+void sweep_kernel(const SweepHeader *header_g, const SweepProj *projs_g,
+                  const SweepWork *work_g, uint32_t check) {
     constexpr int T = 64 * NW;
     // chunks of 8 activations per thread and token row: K <= 8192
     constexpr int kRounds = (TWD_MAX_K / 8 + T - 1) / T;
@@ -350,16 +328,18 @@ __global__ __launch_bounds__(64 * NW) void sweep_kernel(const SweepHeader *heade
     __syncthreads();  // staged rows, row sums and scales
 
     // 2. stream each span's tiles: compute the pass in one ring slot while
-    //    the next two passes' loads are in flight
+    //    the next kS - 1 passes' loads are in flight
     uint4 ring[kS][kSweepLP];
     v4i c0 = {0, 0, 0, 0}, c3 = c0, c4 = c0, c16 = c0;
+    int turn = 0;  // tiles of the spans before, modulo NW
     for (int s = 0; s < nspan; ++s) {
         const SweepSpan sp = span_at(wk, s);
         const cptr<SweepProj> P = projs + sp.q;
+        const int first = (wave - turn + NW) % NW;  // this wave's first tile
+        turn = (turn + sp.t1 - sp.t0) % NW;
         SpanW sw;
         sw.w = P->w;
-        sw.RB = P->K >> 2;
-        sw.N = P->N;
+        sw.tile_bytes = 1024 * P->slices;
         sw.t1 = sp.t1;
         const int passes = P->passes;
         const int slices = P->slices;
@@ -373,32 +353,37 @@ __global__ __launch_bounds__(64 * NW) void sweep_kernel(const SweepHeader *heade
         const uint8_t *bsrc = r < M ? xbase + sp.xoff + r * P->stride + 64 * g : zero;
         const int ustep = r < M ? 256 : 0;
 
-        // passes of this wave in the span: tiles t0 + wave, t0 + wave + NW, ...
-        const int tiles = sp.t0 + wave < sp.t1 ? (sp.t1 - sp.t0 - wave + NW - 1) / NW : 0;
+        // passes of this wave in the span: tiles t0 + first, + NW, ...
+        const int tiles =
+            sp.t0 + first < sp.t1 ? (sp.t1 - sp.t0 - first + NW - 1) / NW : 0;
         int left = tiles * passes;
-        PassPos c{sp.t0 + wave, 0};
+        PassPos c{sp.t0 + first, 0};
         PassPos f = c;
-        issue(sw, f, r, g, ring[0]);
-        step<NW>(f, passes);
-        issue(sw, f, r, g, ring[1]);
-        step<NW>(f, passes);
-#define TWD_SWEEP_STEP(NEXT, CUR)                                              \
-    issue(sw, f, r, g, ring[NEXT]);                                            \
+#pragma unroll
+        for (int k = 0; k < kS - 1; ++k) {
+            issue(sw, f, lane, ring[k]);
+            step<NW>(f, passes);
+        }
+        // one step: issue the pass kS - 1 ahead into the slot freed by the
+        // last step, then compute the pass in slot CUR
+#define TWD_SWEEP_STEP(CUR)                                                    \
+    issue(sw, f, lane, ring[((CUR) + kS - 1) % kS]);                           \
     step<NW>(f, passes);                                                       \
-    compute(c.p, slices, bsrc, ustep, zero, r, ring[CUR], c0, c3, c4, c16);    \
+    compute(c.p, slices, bsrc, ustep, zero, ring[CUR], c0, c3, c4, c16);       \
     if (c.p == passes - 1)                                                     \
         epilogue<M>(so, c.t, r, g, c0, c3, c4, c16);                           \
     step<NW>(c, passes);
-        for (; left >= 3; left -= 3) {
-            TWD_SWEEP_STEP(2, 0)
-            TWD_SWEEP_STEP(0, 1)
-            TWD_SWEEP_STEP(1, 2)
+        for (; left >= kS; left -= kS) {
+#pragma unroll
+            for (int k = 0; k < kS; ++k) {
+                TWD_SWEEP_STEP(k)
+            }
         }
-        if (left >= 1) {
-            TWD_SWEEP_STEP(2, 0)
-        }
-        if (left >= 2) {
-            TWD_SWEEP_STEP(0, 1)
+#pragma unroll
+        for (int k = 0; k < kS - 1; ++k) {
+            if (left > k) {
+                TWD_SWEEP_STEP(k)
+            }
         }
 #undef TWD_SWEEP_STEP
     }
@@ -409,7 +394,10 @@ using Fn = void (*)(const SweepHeader *, const SweepProj *, const SweepWork *, u
 template <int... Ms>
 Fn pick(int M) {
     Fn fn = nullptr;
-    ((M == Ms ? (void)(fn = &sweep_kernel<Ms, kSweepWaves>) : (void)0), ...);
+    ((M == Ms ? (void)(fn = &sweep_kernel<Ms, sweep_waves(Ms), sweep_ring(Ms),
+                                          sweep_simd_waves(Ms)>)
+              : (void)0),
+     ...);
     return fn;
 }
 
@@ -427,7 +415,7 @@ hipError_t launch_sweep(const twd_sweep_plan &plan, hipStream_t stream) {
     const SweepProj *p = reinterpret_cast<const SweepProj *>(t + kSweepHeaderBytes);
     const SweepWork *w = reinterpret_cast<const SweepWork *>(
         t + kSweepHeaderBytes + static_cast<int64_t>(plan.nproj) * sizeof(SweepProj));
-    hipLaunchKernelGGL(fn, dim3(plan.nwg), dim3(64 * kSweepWaves), plan.lds_bytes, stream, h, p,
+    hipLaunchKernelGGL(fn, dim3(plan.nwg), dim3(64 * sweep_waves(plan.M)), plan.lds_bytes, stream, h, p,
                        w, plan.check);
     return hipGetLastError();
 }

@@ -59,13 +59,14 @@ class Case:
         N = int(sum(segs))
         packed, self.gammas = twd.prepare_weights(W, segs)
         self.wp = torch.from_numpy(packed).cuda()
+        self.wt = torch.from_numpy(twd.tile_for_sweep(packed, N, K)).cuda()
         self.xd = dev_bf16(torch, x)
         self.acc = (torch.full((M, N), -7, dtype=torch.int32, device="cuda")
                     if want_acc else None)
         self.y = torch.full((M, N), -7.0, device="cuda") if want_y else None
 
     def entry(self):
-        return (self.wp, self.segs, self.gammas, self.xd, self.acc, self.y)
+        return (self.wt, self.segs, self.gammas, self.xd, self.acc, self.y)
 
     def check(self, orc, ref=None):
         ref = ref if ref is not None else orc.forward(self.W, self.segs, self.x)
@@ -154,7 +155,7 @@ def test_sweep_whole_2b_set_m1(env):
     ls = wl.SET_2B
     M = 1
     rng = np.random.default_rng(123)
-    entries, refs = [], []
+    entries, refs, rowmajor = [], [], []
     for layer in range(ls.layers):
         for pi, proj in enumerate(ls.projs):
             W = wl.layer_weights(ls, layer, pi)
@@ -168,16 +169,18 @@ def test_sweep_whole_2b_set_m1(env):
             ra = orc.linear(q, t[rows])
             refs.append((layer, pi, rows, ra, orc.dequant(ra, s, grow[rows])))
             del W, t
-            entries.append((torch.from_numpy(packed).cuda(), proj.segs, gammas,
-                            dev_bf16(torch, x),
+            entries.append((torch.from_numpy(twd.tile_for_sweep(packed, proj.N, proj.K)).cuda(),
+                            proj.segs, gammas, dev_bf16(torch, x),
                             torch.full((M, proj.N), -7, dtype=torch.int32, device="cuda"),
                             torch.full((M, proj.N), -7.0, device="cuda")))
+            rowmajor.append(torch.from_numpy(packed).cuda())
     log("sweep whole 2B set M=1: planned")
     sw = twd.Sweep(entries)
     assert sw.weight_bytes == ls.packed_bytes
     sw.run()
     torch.cuda.synchronize()
-    for (wp, segs, gammas, xd, acc, y), (layer, pi, rows, ra, ry) in zip(entries, refs):
+    for (wt, segs, gammas, xd, acc, y), wp, (layer, pi, rows, ra, ry) in zip(entries, rowmajor,
+                                                                            refs):
         a2, y2 = twd.ternary_linear_bf16(wp, segs, gammas, xd)
         torch.cuda.synchronize()
         assert torch.equal(acc, a2), (layer, pi)
@@ -244,12 +247,12 @@ def test_sweep_errors(env):
     bad = wl.random_case(seed=8, M=2, K=100, seg_rows=(16,))
     with pytest.raises(twd.TwdError) as e:
         xb = torch.zeros((2, 100), dtype=torch.bfloat16, device="cuda")
-        twd.Sweep([(c.wp, segs, c.gammas, xb, None, c.y)])
+        twd.Sweep([(c.wt, segs, c.gammas, xb, None, c.y)])
     assert e.value.status == 2
     with pytest.raises(twd.TwdError) as e:
-        twd.Sweep([(c.wp, segs, c.gammas, c.xd, None, None)])
+        twd.Sweep([(c.wt, segs, c.gammas, c.xd, None, None)])
     assert e.value.status == 1
     with pytest.raises(ValueError):
         x3 = torch.zeros((3, 256), dtype=torch.bfloat16, device="cuda")
-        twd.Sweep([c.entry(), (c.wp, segs, c.gammas, x3, None, None)])
+        twd.Sweep([c.entry(), (c.wt, segs, c.gammas, x3, None, None)])
     del bad

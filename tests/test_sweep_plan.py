@@ -18,7 +18,7 @@ PROJ = np.dtype([("w", "<u8"), ("x", "<u8"), ("acc", "<u8"), ("y", "<u8"), ("K",
                  ("N", "<i4"), ("passes", "<i4"), ("slices", "<i4"), ("stride", "<i4"),
                  ("nseg", "<i4"), ("bound", "<i4", 4), ("gamma", "<f4", 4), ("pad", "<i4", 2)])
 WORK = np.dtype([("nspan", "<i4"), ("pad", "<i4", 3), ("span", "<i4", (4, 4))])
-LDS_HEADER = 64 + 3 * 4 * 16 * 4
+LDS_HEADER = 64 + 3 * 4 * 16 * 4 + 16
 MAX_SPANS = 4
 
 
@@ -154,3 +154,42 @@ def test_plan_errors():
     pl.table = 0x7F0000000000
     pl.M = 0
     assert twd._lib_sweep(ctypes.byref(pl), None) == 1
+
+
+def tile_reference(packed, N, K):
+    """The tiled layout written out with numpy indexing: tile t, slice u,
+    position l = 16 g + r holds bytes 64 u + 16 g .. + 15 of row 16 t + r."""
+    RB = K // 4
+    T, S = -(-N // 16), -(-K // 256)
+    rows = np.zeros((T * 16, S * 64), np.uint8)
+    rows[:N, :RB] = packed.reshape(N, RB)
+    # [t, r, u, g, b] -> [t, u, g, r, b]
+    v = rows.reshape(T, 16, S, 4, 16).transpose(0, 2, 3, 1, 4)
+    return np.ascontiguousarray(v).reshape(-1)
+
+
+@pytest.mark.parametrize("N,K", [(1, 64), (16, 256), (17, 320), (130, 2560), (33, 6912),
+                                 (20, 8192), (0, 256), (5, 0)])
+def test_tile_weights_layout(N, K):
+    rng = np.random.default_rng([N, K])
+    codes = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    packed = twd.pack_ternary(codes)
+    tiled = twd.tile_for_sweep(packed, N, K)
+    assert tiled.size == twd.sweep_tiled_bytes(N, K) == -(-N // 16) * -(-K // 256) * 1024
+    np.testing.assert_array_equal(tiled, tile_reference(packed, N, K))
+    if tiled.size:
+        # padding (rows past N, bytes past K / 4) is zero
+        T, S = -(-N // 16), -(-K // 256)
+        v = tiled.reshape(T, S, 4, 16, 16)
+        r = np.arange(16)[None, None, None, :] + 16 * np.arange(T)[:, None, None, None]
+        col = 64 * np.arange(S)[None, :, None, None] + 16 * np.arange(4)[None, None, :, None]
+        pad = (r >= N) | (col >= K // 4)
+        assert not v[np.broadcast_to(pad, v.shape[:4])].any()
+
+
+def test_tile_weights_errors():
+    with pytest.raises(ValueError):
+        twd.sweep_tiled_bytes(16, 100)
+    assert twd._lib_tiled_bytes(-1, 64) == -1
+    with pytest.raises(twd.TwdError):
+        twd._check(twd._lib_tile(None, 16, 64, None))
