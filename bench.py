@@ -3,21 +3,24 @@
 
 A step is one pass of the whole hot path over the 2B-class decode layer set
 (30 layers x {fused QKV 2560->3840, O 2560->2560, fused gate/up
-2560->13824, down 6912->2560}) at width M: per projection, one launch that
-quantizes a fresh bf16 activation block per token to int8 and runs the
-fused ternary linear with its dequant epilogue.  All weights (521 MB packed,
-more than the 256 MB Infinity Cache, so every projection streams cold
-weights) and activations are resident in HBM before timing starts.  The step
-is recorded once into a HIP graph and replayed.
+2560->13824, down 6912->2560}) at width M: per projection, the per-token
+absmax int8 quantization of a fresh bf16 activation block and the ternary
+linear with its dequant epilogue.  The step runs as one multi-projection
+sweep launch (twd_ternary_sweep) over the 120 projections, whose inputs are
+independent; it is recorded once into a HIP graph and replayed.  All weights
+(521 MB packed, more than the 256 MB Infinity Cache, so every step streams
+cold weights) and activations are resident in HBM before timing starts.
 
 Output: one JSON line.  `value` is packed-weight bytes per second over the
-timed steps (wall clock between two synchronizations).  The timed graph
-holds only the ternary linear launches, back to back, so two events around
-the timed replays give that kernel's average launch duration (elapsed /
-launches), from which `roofline` rates it against MI355X's 8 TB/s HBM peak.
-Also reported: the two-launch form (stand-alone quantizer + linear), a plain
-streaming read of the same buffers, the per-width table, and `cpu_baseline`,
-the CPU oracle timed on a bounded sample of the same work.
+timed steps (wall clock between two synchronizations).  Two HIP events around
+the timed replays, on the replaying stream, give the sweep kernel's average
+launch duration, from which `roofline` rates it against MI355X's 8 TB/s HBM
+peak (its `trace` entry repeats the rocprofv3 kernel-trace figure of the same
+command, from profiles/, when it was taken on the current sources).  Also
+reported: the same step as one launch per projection (and the two-launch
+form), streaming-read references, every width 1..16 on the outlier workload,
+the 4B-class stack, the per-width graph atlas, the output projection, the KV
+commit, and `cpu_baseline`, the CPU oracle timed on a bounded sample.
 """
 from __future__ import annotations
 
@@ -55,24 +58,29 @@ def host_threads():
 
 
 class LayerSetOnDevice:
-    """Packed weights of every projection, uploaded once."""
+    """Packed weights of every projection, uploaded once: row-major (the
+    per-projection launches) and in the sweep's tiled layout."""
 
-    def __init__(self, twd, torch, ls, layers):
+    def __init__(self, twd, torch, ls, layers, tiled=True):
         self.ls = ls
         self.layers = layers
-        self.w = {}
-        self.gammas = {}
+        self.w, self.wt, self.gammas = {}, {}, {}
 
         def prep(key):
             layer, pi = key
+            p = ls.projs[pi]
             W = wl.layer_weights(ls, layer, pi)
-            return key, twd.prepare_weights(W, ls.projs[pi].segs)
+            packed, gammas = twd.prepare_weights(W, p.segs)
+            t = twd.tile_for_sweep(packed, p.N, p.K) if tiled else None
+            return key, packed, t, gammas
 
         keys = [(l, p) for l in range(layers) for p in range(len(ls.projs))]
         with ThreadPoolExecutor(max_workers=host_threads()) as ex:
-            for (layer, pi), (packed, gammas) in ex.map(prep, keys):
-                self.w[(layer, pi)] = torch.from_numpy(packed).cuda()
-                self.gammas[(layer, pi)] = gammas
+            for key, packed, t, gammas in ex.map(prep, keys):
+                self.w[key] = torch.from_numpy(packed).cuda()
+                if t is not None:
+                    self.wt[key] = torch.from_numpy(t).cuda()
+                self.gammas[key] = gammas
         torch.cuda.synchronize()
 
     @property
@@ -95,13 +103,29 @@ class Step:
                 self.xq[(layer, pi)] = torch.empty((M, p.K), dtype=torch.int8, device="cuda")
                 self.xs[(layer, pi)] = torch.empty((M,), dtype=torch.float32, device="cuda")
                 self.y[(layer, pi)] = torch.empty((M, p.N), dtype=torch.float32, device="cuda")
+        self._sweep = None
         torch.cuda.synchronize()
 
     def keys(self):
         return [(l, p) for l in range(self.ds.layers) for p in range(len(self.ds.ls.projs))]
 
+    @property
+    def plan(self):
+        return self.sweep_obj().plan
+
+    def sweep_obj(self):
+        if self._sweep is None:
+            self._sweep = self.twd.Sweep(
+                [(self.ds.wt[k], self.ds.ls.projs[k[1]].segs, self.ds.gammas[k], self.x[k],
+                  None, self.y[k]) for k in self.keys()])
+        return self._sweep
+
+    def sweep(self):
+        """The step: one multi-projection launch over every projection."""
+        self.sweep_obj().run()
+
     def fused(self):
-        """The step: one launch per projection (quantize + linear)."""
+        """The step as one launch per projection (quantize + linear)."""
         for k in self.keys():
             p = self.ds.ls.projs[k[1]]
             self.twd.ternary_linear_bf16(self.ds.w[k], p.segs, self.ds.gammas[k], self.x[k],
@@ -115,6 +139,17 @@ class Step:
             self.twd.ternary_linear_fused(self.ds.w[k], p.segs, self.ds.gammas[k],
                                           self.xq[k], self.xs[k], y=self.y[k],
                                           want_acc=False, kernel=self.kernel)
+
+    def snapshot(self):
+        return {k: v.clone() for k, v in self.y.items()}
+
+    def equals(self, snap):
+        return all(self.torch.equal(self.y[k].view(self.torch.int32),
+                                    snap[k].view(self.torch.int32)) for k in self.keys())
+
+    def clear(self):
+        for v in self.y.values():
+            v.fill_(-1.0)
 
 
 def capture(torch, fn):
@@ -146,6 +181,22 @@ def time_replays(torch, g, reps):
     return t1 - t0, start.elapsed_time(end) * 1e-3
 
 
+def time_launches(torch, fn, reps):
+    """Wall seconds and event seconds for reps direct calls of fn on the
+    current stream (no graph), synchronized on both sides."""
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(reps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return t1 - t0, start.elapsed_time(end) * 1e-3
+
+
 def time_eager(torch, fn, reps):
     """Wall seconds for `reps` eager calls of fn (no graph), synchronized on
     both sides."""
@@ -158,10 +209,21 @@ def time_eager(torch, fn, reps):
 
 
 def stream_read_reference(twd, torch, dev_set, reps):
-    """The plain streaming-read kernel over each projection's weight buffer,
-    launched back to back in the same order as the linear sweep."""
+    """The plain streaming-read kernel (every compute unit busy, eight loads
+    in flight per lane): once over one contiguous buffer of the step's bytes
+    (the sweep's reference: one launch), and over each projection's weight
+    buffer in turn (the per-projection launches' reference).  Returns
+    ({gbs, us}, {gbs, avg_launch_us})."""
     sink = torch.zeros(256, dtype=torch.int32, device="cuda")
     keys = [(l, p) for l in range(dev_set.layers) for p in range(len(dev_set.ls.projs))]
+    nbytes = dev_set.bytes_per_sweep
+    big = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    big.fill_(1)
+    g = capture(torch, lambda: twd.stream_read(big, nbytes, sink))
+    g.replay()
+    _, sec = time_replays(torch, g, reps)
+    one = {"gbs": round(nbytes * reps / sec / 1e9, 1), "us": round(sec / reps * 1e6, 2)}
+    del g, big
 
     def sweep():
         for k in keys:
@@ -171,7 +233,71 @@ def stream_read_reference(twd, torch, dev_set, reps):
     g = capture(torch, sweep)
     g.replay()
     _, sec = time_replays(torch, g, reps)
-    return dev_set.bytes_per_sweep * reps / sec / 1e9, sec / (reps * len(keys))
+    per = {"gbs": round(nbytes * reps / sec / 1e9, 1),
+           "avg_launch_us": round(sec / (reps * len(keys)) * 1e6, 3)}
+    torch.cuda.empty_cache()
+    return one, per
+
+
+def time_graph(torch, fn, reps):
+    """Capture fn into a graph and time reps replays: (graph, seconds per
+    replay)."""
+    g = capture(torch, fn)
+    g.replay()
+    _, sec = time_replays(torch, g, reps)
+    return g, sec / reps
+
+
+def width_entry(twd, torch, dev_set, workload, M, kernel, reps, outliers=False,
+                forms=("sweep", "fused", "two_launch"), graphs=True):
+    """One width.  The sweep (one launch per step) is timed as launched
+    directly, back to back, and (graphs) also captured into a graph and
+    replayed; the per-projection forms are captured and replayed (graph) and,
+    with graphs, also launched directly -- the launch gaps a graph removes.
+    The sweep's outputs must equal the per-projection launch's bit for bit."""
+    st = Step(twd, torch, dev_set, workload, M, kernel, outliers)
+    nbytes = dev_set.bytes_per_sweep
+    n = len(st.keys())
+    out = {}
+    if "fused" in forms:
+        st.fused()
+        torch.cuda.synchronize()
+        ref = st.snapshot()
+    if "sweep" in forms:
+        st.clear()
+        st.sweep()
+        torch.cuda.synchronize()
+        if "fused" in forms and not st.equals(ref):
+            raise SystemExit(f"sweep differs from the per-projection launches at M={M}")
+        st.sweep()
+        _, sec = time_launches(torch, st.sweep, reps)
+        sec /= reps
+        e = {"gbs": round(nbytes / sec / 1e9, 1), "frac": round(nbytes / sec / 1e9 / HBM_PEAK_GBS, 4),
+             "us": round(sec * 1e6, 2), "workgroups": st.plan.nwg}
+        if graphs:
+            g, gsec = time_graph(torch, st.sweep, reps)
+            e["graph_us"] = round(gsec * 1e6, 2)
+            del g
+        out["sweep"] = e
+    if "fused" in forms:
+        g, sec = time_graph(torch, st.fused, reps)
+        e = {"gbs": round(nbytes / sec / 1e9, 1), "frac": round(nbytes / sec / 1e9 / HBM_PEAK_GBS, 4),
+             "us_per_launch": round(sec / n * 1e6, 3), "kernels": kernel_map(twd, dev_set.ls, M, kernel)}
+        if graphs:
+            k = max(3, reps // 3)
+            esec = time_eager(torch, st.fused, k) / k
+            e["eager_us_per_launch"] = round(esec / n * 1e6, 3)
+            e["graph_saves_us_per_launch"] = round((esec - sec) / n * 1e6, 3)
+        out["per_launch"] = e
+        del g
+    if "two_launch" in forms:
+        g, sec = time_graph(torch, st.two_launch, reps)
+        out["two_launch"] = {"gbs": round(nbytes / sec / 1e9, 1),
+                             "kernels": kernel_map(twd, dev_set.ls, M, kernel, False)}
+        del g
+    del st
+    torch.cuda.empty_cache()
+    return out
 
 
 def output_projection_bench(twd, torch, widths, reps):
@@ -242,7 +368,7 @@ def cpu_projection_baseline(budget_s, M=1, rows=1024):
     projection's rows, repeated until budget_s; throughput in weight bytes/s
     of each role."""
     import oracle
-    oracle.build(force=False)
+    oracle_native()
     W = wl.head_weight_block(0)[:rows]
     x = wl.head_activations(M)
     out = {}
@@ -351,15 +477,15 @@ def kv_commit_bench(twd, torch, ls, reps, D=8, steps=64, c0=256, nseg=8, start=1
             "full_history_bytes": hist_bytes}
 
 
-def atlas_bench(twd, torch, dev_set, kernel, reps, D=8, c0=256, nseg=8, start=1000):
-    """The hot path as a finite set of captured graphs, one per (role,
-    width), all sharing the weights and the KV segments: a decode iteration
-    is the ternary sweep over every layer at width M, the output projection
-    in the iteration's role, and (when tokens are committed) the KV commit.
-    States: autoregressive (M = 1, critical projection, commit 1 row),
-    drafting (M = D + 1, fast projection, nothing committed) and
-    verification (M = D + 1, critical projection, commit 1 + a rows, a drawn
-    uniform{0..D}).  Each graph is replayed in turn; per-iteration times."""
+def atlas_bench(twd, torch, dev_set, reps, widths=range(1, 17), c0=256, nseg=8, start=1000):
+    """The hot path as a finite set of captured graphs, all held at once and
+    sharing the weights and the KV segments, one per (role, width): a decode
+    iteration at width M is the sweep over every layer, the output projection
+    in the iteration's role and, where tokens are committed, the KV commit.
+    For every M: the critical state (M = 1 autoregressive, M > 1 verification:
+    bf16 projection, commit of M rows) and, for M > 1, the drafting state
+    (fast E4M3 projection, nothing committed).  Each graph is replayed in turn;
+    every replay's sweep outputs must equal the eager sweep's."""
     ls = dev_set.ls
     K, N = wl.HEAD_K, wl.HEAD_N
     gen = torch.Generator(device="cuda")
@@ -371,50 +497,62 @@ def atlas_bench(twd, torch, dev_set, kernel, reps, D=8, c0=256, nseg=8, start=10
     layers, row_bytes = ls.layers, ls.projs[0].segs[1] * 2
     segs = [torch.zeros(layers * 2 * cap * row_bytes, dtype=torch.uint8, device="cuda")
             for cap in twd.kv_segment_positions(c0, nseg)]
-    W = D + 1
-    block = torch.randint(0, 256, (layers * 2 * W * row_bytes,), dtype=torch.uint8,
+    Wmax = max(widths)
+    block = torch.randint(0, 256, (layers * 2 * Wmax * row_bytes,), dtype=torch.uint8,
                           device="cuda", generator=gen)
-    rng = np.random.default_rng(2028)
-    a = int(rng.integers(0, D + 1))
-    counts = torch.tensor([1, 1, 1 + a, a + 1], dtype=torch.int32, device="cuda")
+    counts = torch.tensor([[m, m] for m in range(Wmax + 1)], dtype=torch.int32, device="cuda")
     state = torch.zeros((2, 4), dtype=torch.int32, device="cuda")
     state[0] = torch.tensor([start + 1, start, 1, 0], dtype=torch.int32)
-    steps = {M: Step(twd, torch, dev_set, "2b_verify", M, kernel) for M in (1, W)}
-    heads = {M: torch.empty((M, N), dtype=torch.float32, device="cuda") for M in (1, W)}
+    steps = {M: Step(twd, torch, dev_set, "2b_sweep_outlier", M, twd.KERNEL_AUTO, True)
+             for M in widths}
+    heads = {M: torch.empty((M, N), dtype=torch.float32, device="cuda") for M in widths}
+    eager = {}
+    for M, st in steps.items():
+        st.sweep()
+        torch.cuda.synchronize()
+        eager[M] = st.snapshot()
 
     def iteration(M, role, commit):
         def run():
             st = steps[M]
-            st.fused()
+            st.sweep()
             xh = st.x[(layers - 1, 0)]  # the last layer's hidden rows stand in
             if role == "fast":
                 twd.projection_fp8(w8, ws, xh, y=heads[M])
             else:
                 twd.projection_bf16(w16, xh, y=heads[M])
             if commit:
-                i = 0 if M == 1 else 2
                 # two commits per graph keep the state on the first word
                 for j in range(2):
-                    twd.kv_commit(segs, c0, layers, row_bytes, block, W, counts[i:i + 1],
-                                  counts[i + 1:i + 2], state[j], state[1 - j])
+                    twd.kv_commit(segs, c0, layers, row_bytes, block, Wmax, counts[M, 0:1],
+                                  counts[M, 1:2], state[j], state[1 - j])
         return run
 
-    entries = {"autoregressive_m1": (1, "critical", True),
-               f"draft_m{W}": (W, "fast", False),
-               f"verify_m{W}": (W, "critical", True)}
+    entries = {}
+    for M in widths:
+        entries[f"critical_m{M}"] = (M, "critical", True)
+        if M > 1:
+            entries[f"draft_m{M}"] = (M, "fast", False)
     graphs = {k: capture(torch, iteration(*v)) for k, v in entries.items()}
-    out = {"states": "autoregressive: M=1, critical projection, 2 commits of 1 row; drafting: "
-                     f"M={W}, fast projection; verification: M={W}, critical projection, "
-                     f"2 commits of {1 + a} rows",
-           "sweep_bytes": dev_set.bytes_per_sweep}
+    out = {"states": "critical_mM: the sweep at width M, the bf16 output projection and two "
+                     "KV commits of M rows (M = 1: an autoregressive step, M > 1: "
+                     "verification); draft_mM: the sweep and the E4M3 output projection",
+           "graphs_held": len(graphs), "sweep_bytes": dev_set.bytes_per_sweep, "us": {}}
     for k, g in graphs.items():
+        M = entries[k][0]
         g.replay()
         _, sec = time_replays(torch, g, reps)
-        out[k] = {"us_per_iteration": round(sec / reps * 1e6, 1)}
+        out["us"][k] = round(sec / reps * 1e6, 1)
+        steps[M].clear()
+        g.replay()
+        torch.cuda.synchronize()
+        if not steps[M].equals(eager[M]):
+            raise SystemExit(f"atlas graph {k}: replayed sweep differs from the eager one")
     torch.cuda.synchronize()
     fin = state[0].cpu().tolist()
     if fin[3] != 0 or fin[0] != fin[1] + fin[2]:
         raise SystemExit(f"atlas KV state {fin}")
+    out["replays_checked"] = "every graph: a replay's sweep outputs equal the eager sweep's"
     out["final_kv_state"] = fin
     del steps, heads, segs, w8, w16, graphs
     torch.cuda.empty_cache()
@@ -497,6 +635,22 @@ LINEAR_SOURCES = ("dispatch.hip", "kernel_common.h", "quantize_act.hip", "ternar
 
 PROJECTION_SOURCES = ("kernel_common.h", "projection.hip")
 
+SWEEP_SOURCES = ("kernel_common.h", "twd_internal.h", "ternary_sweep.hip", "sweep_plan.cpp")
+
+
+def sweep_record(workload, M):
+    """The sweep's rocprofv3 record (kernel-trace duration, HBM bytes per
+    launch) for this workload and width, if it was taken on the current
+    sources; else None."""
+    path = os.path.join(PROFILES, f"sweep_{workload}_m{M}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != kernel_source_hash(SWEEP_SOURCES):
+        return None
+    return rec
+
 
 def kernel_source_hash(names=LINEAR_SOURCES):
     """Hash of the code (comments and blank space removed) of the given
@@ -554,6 +708,20 @@ def host_cpu():
     return f"{model}; {visible} logical CPUs visible to the process"
 
 
+_NATIVE = None
+
+
+def oracle_native():
+    """Build the oracle for this host (gcc -O3 -march=native, plain loops,
+    no fast-math) once per process and use it for the CPU baselines."""
+    global _NATIVE
+    import oracle
+    if _NATIVE is None:
+        oracle.select(oracle.build_native())
+        _NATIVE = "gcc " + " ".join(oracle.NATIVE_FLAGS) + " -fopenmp -ffp-contract=off"
+    return _NATIVE
+
+
 def cpu_baseline(ls, workload, M, outliers, budget_s, threads=None):
     """The CPU oracle (quantize, int8 x ternary loops, dequant) over the
     layers of the set in order, repeating whole passes until its compute time
@@ -561,7 +729,7 @@ def cpu_baseline(ls, workload, M, outliers, budget_s, threads=None):
     the oracle's own ternarization, in a thread pool, all before timing) is
     not timed."""
     import oracle
-    oracle.build(force=False)
+    native = oracle_native()
     threads = threads or host_threads()
 
     def prep(key):
@@ -592,7 +760,7 @@ def cpu_baseline(ls, workload, M, outliers, budget_s, threads=None):
             run(item)
         passes += 1
     return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle", "host": host_cpu(),
+            "kind": "oracle", "host": host_cpu(), "build": native,
             "sample": f"{passes} pass(es) over all {ls.layers} layers of the {ls.name.upper()} set "
                       f"at M={M} (4 projections each: quantize + int32 contraction + dequant; "
                       f"{spent:.1f} s of CPU time; throughput in packed-weight bytes/s)"}
@@ -813,6 +981,126 @@ def summarize_profiles(args):
     print(cnt_path)
 
 
+def _sweep_kernel(name):
+    return _short(name).startswith("sweep_kernel<")
+
+
+def summarize_sweep(args):
+    """Kernel trace and HBM counters of the headline sweep from three
+    rocprofv3 runs of this script with --headline-only (kernel trace + stats;
+    FETCH_SIZE; WRITE_SIZE, the counter runs with --copy-calibration) ->
+    profiles/sweep_<workload>_m<M>_{kernel_trace,hbm_counters}.md and the
+    record sweep_record() reads."""
+    trace_dir, fetch_dir, write_dir = args.summarize_sweep
+    ran = _run_source_hash(args.profile_run_json, "sweep_source_hash")
+    if ran is not None and ran != kernel_source_hash(SWEEP_SOURCES):
+        raise SystemExit(f"the profiled run used sweep sources {ran}, not the current "
+                         f"{kernel_source_hash(SWEEP_SOURCES)}: profile them again")
+    cmds = args.profile_commands or ("?", "?", "?")
+    ls = wl.LAYER_SETS["4b" if args.workload.startswith("4b") else "2b"]
+    M = args.M or wl.workload_widths(args.workload)[0]
+    alg = ls.packed_bytes
+    tag = f"{args.workload}_m{M}"
+    out_dir = args.profile_out
+    os.makedirs(out_dir, exist_ok=True)
+
+    stats = _csv_rows(trace_dir, "kernel_stats.csv")
+    trace = _csv_rows(trace_dir, "kernel_trace.csv")
+    sw = [r for r in trace if _sweep_kernel(_col(r, "Kernel_Name"))]
+    sw.sort(key=lambda r: int(_col(r, "Start_Timestamp")))
+    timed = sw[-args.steps:]
+    durs = [int(_col(r, "End_Timestamp")) - int(_col(r, "Start_Timestamp")) for r in timed]
+    avg_ns = sum(durs) / len(durs)
+    kname = _short(_col(timed[0], "Kernel_Name"))
+    lines = [f"# multi-projection sweep, {args.workload}, M={M}: rocprofv3 kernel trace", "",
+             "Command (from the repository root):", "", "    " + cmds[0], "",
+             "## Kernel statistics (rocprofv3 --stats)", "",
+             "| kernel | calls | total us | average us | min us | max us |",
+             "|---|---|---|---|---|---|"]
+    stats.sort(key=lambda r: -float(_col(r, "TotalDurationNs")))
+    for r in stats[:10]:
+        lines.append(f"| `{_short(_col(r, 'Name'))}` | {_col(r, 'Calls')} | "
+                     f"{float(_col(r, 'TotalDurationNs')) / 1e3:.1f} | "
+                     f"{float(_col(r, 'AverageNs')) / 1e3:.3f} | {float(_col(r, 'MinNs')) / 1e3:.3f} | "
+                     f"{float(_col(r, 'MaxNs')) / 1e3:.3f} |")
+    lines += ["", f"## The timed region: the last {len(timed)} dispatches of `{kname}`", "",
+              f"Each dispatch runs all {ls.layers * len(ls.projs)} projections of the "
+              f"{ls.name.upper()} set: {alg:,} packed-weight bytes.", "",
+              f"- average duration **{avg_ns / 1e3:.2f} us** (min {min(durs) / 1e3:.2f}, "
+              f"max {max(durs) / 1e3:.2f}) -> {alg / avg_ns:.1f} GB/s, "
+              f"{100 * alg / avg_ns / HBM_PEAK_GBS:.1f}% of 8 TB/s", ""]
+
+    def live(path):
+        if not path or not os.path.exists(path):
+            return None
+        with open(path) as f:
+            for line in f:
+                if line.startswith("{"):
+                    return json.loads(line)["roofline"]["avg_launch_us"]
+        return None
+
+    prof_live, bench_live = live(args.profile_run_json), live(args.bench_json)
+    if prof_live is not None:
+        lines.append(f"- the profiled run's own live figure (HIP events around the timed "
+                     f"launches): {prof_live:.2f} us per launch")
+    if bench_live is not None:
+        lines.append(f"- the unprofiled default run: **{bench_live:.2f} us** per launch "
+                     f"({100 * (avg_ns / 1e3 - bench_live) / bench_live:+.1f}% for the traced "
+                     f"kernel)")
+    lines.append("")
+    trace_path = os.path.join(out_dir, f"sweep_{tag}_kernel_trace.md")
+    with open(trace_path, "w") as f:
+        f.write("\n".join(lines))
+
+    def per_kernel(d, counter):
+        agg = {}
+        for r in _csv_rows(d, "counter_collection.csv"):
+            if _col(r, "Counter_Name") != counter:
+                continue
+            name = _col(r, "Kernel_Name")
+            if _sweep_kernel(name):
+                agg.setdefault("sweep", []).append(float(_col(r, "Counter_Value")))
+            elif "stream_copy_kernel" in name and grid(r) == COPY_GRID_THREADS:
+                agg.setdefault("copy", []).append(float(_col(r, "Counter_Value")))
+        return {k: sum(v) / len(v) for k, v in agg.items()}, len(agg.get("sweep", []))
+
+    fetch, nf = per_kernel(fetch_dir, "FETCH_SIZE")
+    write, _ = per_kernel(write_dir, "WRITE_SIZE")
+    copy_bytes = 256 << 20
+    ff = copy_bytes / (fetch["copy"] * 1024.0)
+    fw = copy_bytes / (write["copy"] * 1024.0)
+    rd = fetch["sweep"] * 1024 * ff
+    wr = write["sweep"] * 1024 * fw
+    lines = [f"# multi-projection sweep, {args.workload}, M={M}: HBM bytes from rocprofv3 "
+             "counters", "", "Commands (from the repository root), one counter per run:", "",
+             "    " + cmds[1], "", "    " + cmds[2], "",
+             f"Calibration: the plain copy kernel (`stream_copy_kernel`) moves {copy_bytes} bytes "
+             f"each way per dispatch; FETCH_SIZE reads {fetch['copy']:.1f} KiB -> factor "
+             f"{ff:.4f}; WRITE_SIZE reads {write['copy']:.1f} KiB -> factor {fw:.4f}.", "",
+             f"`{kname}`, mean over {nf} dispatches: FETCH_SIZE {fetch['sweep']:.1f} KiB, "
+             f"WRITE_SIZE {write['sweep']:.1f} KiB.", "",
+             "| | bytes per launch | over the packed weights |", "|---|---|---|",
+             f"| read (calibrated FETCH_SIZE) | {rd:,.0f} | {rd / alg:.4f}x |",
+             f"| written (calibrated WRITE_SIZE) | {wr:,.0f} | {wr / alg:.4f}x |",
+             f"| **HBM traffic** | **{rd + wr:,.0f}** | **{(rd + wr) / alg:.4f}x** |",
+             f"| algorithmic (packed weights, K N / 4 summed) | {alg:,} | 1x |", "",
+             "Beyond the weights: each workgroup's read of the bf16 activations of the "
+             "projections it stages (L2 misses, so also what the Infinity Cache serves), "
+             "the fp32 outputs, and the plan table.", ""]
+    cnt_path = os.path.join(out_dir, f"sweep_{tag}_hbm_counters.md")
+    with open(cnt_path, "w") as f:
+        f.write("\n".join(lines))
+    rec = {"source_hash": kernel_source_hash(SWEEP_SOURCES), "workload": args.workload, "M": M,
+           "kernel": kname, "kernel_trace_avg_us": round(avg_ns / 1e3, 3),
+           "hbm_bytes_per_launch": round(rd + wr), "hbm_read_bytes_per_launch": round(rd),
+           "algorithmic_bytes_per_launch": alg, "fetch_factor": round(ff, 5),
+           "write_factor": round(fw, 5), "summary": os.path.basename(trace_path)}
+    with open(os.path.join(out_dir, f"sweep_{tag}.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    print(trace_path)
+    print(cnt_path)
+
+
 def summarize_projection(args):
     """Kernel trace and HBM counters of the output projection (both roles)
     from three rocprofv3 runs of this script with --projection-widths 1
@@ -961,13 +1249,16 @@ def main():
                     choices=["2b_decode", "2b_verify", "2b_sweep_outlier", "4b_stack"])
     ap.add_argument("--M", type=int, default=None, help="width (default: the workload's first)")
     ap.add_argument("--kernel", default="auto",
-                    choices=["auto", "dot", "mfma", "mfma_staged", "mfma_tile"])
+                    choices=["auto", "dot", "mfma", "mfma_staged", "mfma_tile"],
+                    help="kernel family of the per-projection launches")
     ap.add_argument("--widths", default="1,2,4,8,16",
-                    help="widths for the per-width linear table ('' to skip)")
+                    help="widths of the headline set's per-width table ('' to skip)")
+    ap.add_argument("--outlier-widths", default=",".join(str(m) for m in range(1, 17)),
+                    help="widths of the 2B outlier workload curve ('' to skip)")
+    ap.add_argument("--set4b-widths", default="1,4,16",
+                    help="widths of the 4B-class stack ('' to skip)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU oracle budget (0 skips the CPU baseline)")
-    ap.add_argument("--check", type=int, default=1,
-                    help="1: check every graph replay against the eager results (default)")
     ap.add_argument("--per-proj", type=int, default=1,
                     help="1: time each projection shape on its own, cold (default)")
     ap.add_argument("--projection-widths", default="1,4,8,16",
@@ -976,12 +1267,16 @@ def main():
                     help="time the per-(role, width) iteration graphs (1) or not (0)")
     ap.add_argument("--kv-commit", type=int, default=1,
                     help="time the accepted-prefix KV commit (1) or not (0)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time the headline step only (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with plain copies of 256 MiB (byte-counter calibration)")
+    ap.add_argument("--summarize-sweep", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU: summarize rocprofv3 runs of the headline sweep into profiles/")
     ap.add_argument("--summarize-profile", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
-                    help="no GPU: summarize rocprofv3 CSV output of this script into profiles/")
+                    help="no GPU: summarize rocprofv3 CSV output of the per-projection launches")
     ap.add_argument("--profile-commands", nargs=3, metavar=("TRACE_CMD", "FETCH_CMD", "WRITE_CMD"),
-                    help="the commands that produced --summarize-profile's inputs")
+                    help="the commands that produced the summarized inputs")
     ap.add_argument("--summarize-projection", nargs=3,
                     metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="summarize rocprofv3 runs of the output-projection table")
@@ -994,6 +1289,9 @@ def main():
                     help="stdout of an unprofiled run of the default command")
     args = ap.parse_args()
 
+    if args.summarize_sweep:
+        summarize_sweep(args)
+        return
     if args.summarize_profile:
         summarize_profiles(args)
         return
@@ -1021,102 +1319,73 @@ def main():
     ls = wl.LAYER_SETS[set_name]
     M = args.M or wl.workload_widths(args.workload)[0]
     outliers = args.workload == "2b_sweep_outlier"
+    widths_of = lambda v: [int(w) for w in v.split(",") if w]  # noqa: E731
 
     t_setup = time.perf_counter()
     dev_set = LayerSetOnDevice(twd, torch, ls, ls.layers)
-    log(f"weights ready: {dev_set.bytes_per_sweep / 1e6:.1f} MB packed in "
+    bytes_step = dev_set.bytes_per_sweep
+    log(f"weights ready: {bytes_step / 1e6:.1f} MB packed in "
         f"{time.perf_counter() - t_setup:.1f} s")
 
+    # the headline step: one sweep launch.  Its outputs must equal the
+    # per-projection launches' bit for bit, and every graph replay the eager
+    # launch's.
     step = Step(twd, torch, dev_set, args.workload, M, kernel, outliers)
-    nlaunch = len(step.keys())
-    g_step = capture(torch, step.fused)
-    g_two = capture(torch, step.two_launch)
-
-    # graph replays must equal eager results (every replay is checked), and
-    # the one-launch and two-launch forms must agree bit for bit
-    if args.check:
-        step.two_launch()
-        torch.cuda.synchronize()
-        eager = {k: v.clone() for k, v in step.y.items()}
-        for g in (g_step, g_step, g_two):
-            for v in step.y.values():
-                v.zero_()
-            g.replay()
-            torch.cuda.synchronize()
-            for k in step.keys():
-                if not torch.equal(step.y[k], eager[k]):
-                    raise SystemExit(f"graph replay differs from eager at {k}")
-
-    # the step without graph capture, timed before the graph replays so that
-    # the timed replays stay the last dispatches of the fused kernels (the
-    # kernel-trace summary relies on that)
-    reps = max(10, args.steps // 2)
     step.fused()
-    eager_wall = time_eager(torch, step.fused, reps)
+    torch.cuda.synchronize()
+    ref = step.snapshot()
+    step.clear()
+    step.sweep()
+    torch.cuda.synchronize()
+    if not step.equals(ref):
+        raise SystemExit("the sweep differs from the per-projection launches")
+    g_sweep = capture(torch, step.sweep)
+    for _ in range(2):
+        step.clear()
+        g_sweep.replay()
+        torch.cuda.synchronize()
+        if not step.equals(ref):
+            raise SystemExit("a graph replay of the sweep differs from the eager launch")
+    log(f"headline: sweep of {len(step.keys())} projections, M={M}, "
+        f"{step.plan.nwg} workgroups, checked against the per-projection launches")
 
+    # The step is a single launch, so it is timed as launched directly on the
+    # stream: back to back, each launch starts as the last one ends.  (A
+    # one-kernel graph adds a fixed cost per replay; it is timed beside.)
+    reps = max(10, args.steps // 2)
+    g_sec = None
+    for _ in range(3):  # settle the clocks: about 1.5 s of replays, untimed
+        g_sweep.replay()
+    torch.cuda.synchronize()
+    t_end = time.perf_counter() + 1.5
+    while time.perf_counter() < t_end:
+        for _ in range(200):
+            g_sweep.replay()
+        torch.cuda.synchronize()
+    _, g_sec = time_replays(torch, g_sweep, reps)
+    g_sec /= reps
     for _ in range(args.warmup):
-        g_step.replay()
-    wall, ev_sec = time_replays(torch, g_step, args.steps)
-    bytes_step = dev_set.bytes_per_sweep
+        step.sweep()
+    wall, ev_sec = time_launches(torch, step.sweep, args.steps)
     value = bytes_step * args.steps / wall / 1e9
-    lin_dur = ev_sec / (args.steps * nlaunch)
-    lin_gbs = bytes_step * args.steps / ev_sec / 1e9
-
-    g_two.replay()
-    two_wall, _ = time_replays(torch, g_two, reps)
-
-    ref_gbs, ref_dur = stream_read_reference(twd, torch, dev_set, reps)
-    traffic = counter_traffic(args.workload, M, bytes_step / nlaunch)
-    kname = kernel_map(twd, ls, M, kernel)
-    del g_two
-
-    widths = {}
-    if args.widths:
-        for Mw in [int(v) for v in args.widths.split(",") if v]:
-            if Mw == M:
-                widths[str(Mw)] = {"gbs": round(lin_gbs, 1), "frac": round(lin_gbs / HBM_PEAK_GBS, 4),
-                                   "traffic": traffic,
-                                   "us_per_launch": round(lin_dur * 1e6, 3),
-                                   "two_launch_gbs": round(bytes_step * reps / two_wall / 1e9, 1),
-                                   "kernels": kname,
-                                   "two_launch_kernels": kernel_map(twd, ls, M, kernel, False)}
-                continue
-            st = Step(twd, torch, dev_set, args.workload, Mw, kernel, outliers)
-            g = capture(torch, st.fused)
-            g.replay()
-            _, sec = time_replays(torch, g, reps)
-            gbs = bytes_step * reps / sec / 1e9
-            del g
-            g2 = capture(torch, st.two_launch)
-            g2.replay()
-            _, sec2 = time_replays(torch, g2, reps)
-            widths[str(Mw)] = {"gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
-                               "traffic": counter_traffic(args.workload, Mw, bytes_step / nlaunch),
-                               "us_per_launch": round(sec / (reps * nlaunch) * 1e6, 3),
-                               "two_launch_gbs": round(bytes_step * reps / sec2 / 1e9, 1),
-                               "kernels": kernel_map(twd, ls, Mw, kernel),
-                               "two_launch_kernels": kernel_map(twd, ls, Mw, kernel, False)}
-            del st, g2
-            torch.cuda.empty_cache()
-
-    proj_table = per_projection(twd, torch, ls, M, kernel, reps) if args.per_proj else None
-    kvc = kv_commit_bench(twd, torch, ls, reps) if args.kv_commit else None
-    atlas = atlas_bench(twd, torch, dev_set, kernel, reps) if args.atlas else None
-    head = None
-    if args.projection_widths:
-        head = output_projection_bench(
-            twd, torch, [int(v) for v in args.projection_widths.split(",") if v], reps)
-    if args.cpu_seconds > 0:
-        if head is not None:
-            head["cpu_baseline"] = cpu_projection_baseline(args.cpu_seconds / 5)
-        if kvc is not None:
-            kvc["cpu_baseline"] = cpu_kv_baseline(args.cpu_seconds / 10)
-    calib = copy_calibration(twd, torch) if args.copy_calibration else None
-
-    cpu = cpu1 = None
-    if args.cpu_seconds > 0:
-        cpu = cpu_baseline(ls, args.workload, M, outliers, args.cpu_seconds)
-        cpu1 = cpu_baseline(ls, args.workload, M, outliers, args.cpu_seconds / 3, threads=1)
+    launch_s = ev_sec / args.steps
+    achieved = bytes_step / launch_s / 1e9
+    rec = sweep_record(args.workload, M)
+    roofline = {
+        "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": rec["hbm_bytes_per_launch"] if rec else None,
+        "kernel": f"sweep_kernel (M={M}; one launch per step over the {len(step.keys())} "
+                  f"projections)",
+        "algorithmic_bytes_per_launch": bytes_step,
+        "avg_launch_us": round(launch_s * 1e6, 2), "launches_timed": args.steps,
+    }
+    if rec:
+        roofline["trace"] = {"avg_us": rec["kernel_trace_avg_us"],
+                             "frac": round(bytes_step / (rec["kernel_trace_avg_us"] * 1e3)
+                                           / HBM_PEAK_GBS, 4),
+                             "summary": rec["summary"]}
+    log(f"headline: {value:.1f} GB/s ({launch_s * 1e6:.1f} us per launch)")
 
     out = {
         "metric": METRIC,
@@ -1130,46 +1399,102 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int8",
-        "data": "synthetic (seeded N(0,0.02) weights, absmean-ternarized; N(0,1) bf16 activations)",
+        "data": "synthetic (seeded N(0,0.02) weights, absmean-ternarized; N(0,1) bf16 "
+                "activations)",
         "config": {
             "workload": args.workload,
             "layer_set": f"{ls.name.upper()}-class, hidden {ls.hidden}, {ls.layers} layers",
             "M": M,
             "packed_weight_bytes_per_step": bytes_step,
-            "launches_per_step": nlaunch,
-            "hip_graph": True,
-            "kernels": kname,
+            "form": "one multi-projection sweep launch per step (twd_ternary_sweep over the "
+                    f"{len(step.keys())} independent projections), tiled weights",
+            "launches_per_step": 1,
+            "hip_graph": False,
+            "sweep_workgroups": step.plan.nwg,
+            "sweep_lds_bytes": step.plan.lds_bytes,
         },
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(lin_gbs, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(lin_gbs / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
-            "kernel": "ternary linear with fused activation quantization (every launch of the step)",
-            "avg_launch_us": round(lin_dur * 1e6, 3),
-            "launches_timed": args.steps * nlaunch,
-        },
-        "stream_read_ref": {"gbs": round(ref_gbs, 1), "avg_launch_us": round(ref_dur * 1e6, 3),
-                            "linear_over_ref": round(lin_gbs / ref_gbs, 4)},
-        "two_launch_step_gbs": round(bytes_step * reps / two_wall / 1e9, 1),
-        "eager_step": {"gbs": round(bytes_step * reps / eager_wall / 1e9, 1),
-                       "us_per_launch": round(eager_wall / (reps * nlaunch) * 1e6, 3),
-                       "note": "the same step without graph capture: each call goes through "
-                               "the Python binding and is launched on the stream directly"},
-        "widths": widths,
-        "per_projection_cold": proj_table,
-        "output_projection": head,
-        "kv_commit": kvc,
-        "graph_atlas": atlas,
-        "cpu_baseline": cpu,
-        "cpu_single_thread": cpu1,
+        "roofline": roofline,
+        "graph_step": {"us": round(g_sec * 1e6, 2),
+                       "gbs": round(bytes_step / g_sec / 1e9, 1),
+                       "note": "the same step captured into a HIP graph and replayed back to "
+                               "back (the timed steps above are direct launches)"},
         "kernel_source_hash": kernel_source_hash(),
+        "sweep_source_hash": kernel_source_hash(SWEEP_SOURCES),
         "projection_source_hash": kernel_source_hash(PROJECTION_SOURCES),
     }
-    if calib:
-        out["copy_calibration_bytes"] = calib
+    del g_sweep
+
+    if not args.headline_only:
+        # the same step as one launch per projection (a decode chain's form)
+        pl = width_entry(twd, torch, dev_set, args.workload, M, kernel, reps, outliers,
+                         forms=("fused", "two_launch"))
+        one, per = stream_read_reference(twd, torch, dev_set, reps)
+        pl["per_launch"]["traffic"] = counter_traffic(args.workload, M, bytes_step / len(step.keys()))
+        out["per_launch_step"] = {**pl["per_launch"], "two_launch_gbs": pl["two_launch"]["gbs"],
+                                  "note": "one launch per projection, 120 per step, graph-replayed"}
+        out["stream_read_ref"] = {
+            "one_launch": one, "per_projection_launches": per,
+            "sweep_over_one_launch": round(achieved / one["gbs"], 4),
+            "per_launch_over_per_projection_launches": round(
+                pl["per_launch"]["gbs"] / per["gbs"], 4)}
+        widths = {}
+        for Mw in widths_of(args.widths):
+            log(f"width {Mw}")
+            widths[str(Mw)] = width_entry(twd, torch, dev_set, args.workload if Mw == 1
+                                          else ("2b_verify" if set_name == "2b" else args.workload),
+                                          Mw, kernel, reps, outliers)
+        out["widths"] = widths
+        if set_name == "2b" and args.outlier_widths:
+            curve = {}
+            for Mw in widths_of(args.outlier_widths):
+                log(f"outlier workload, width {Mw}")
+                e = width_entry(twd, torch, dev_set, "2b_sweep_outlier", Mw, kernel,
+                                max(10, reps // 2), True, forms=("sweep", "fused"), graphs=False)
+                curve[str(Mw)] = {"sweep_gbs": e["sweep"]["gbs"], "sweep_frac": e["sweep"]["frac"],
+                                  "per_launch_gbs": e["per_launch"]["gbs"]}
+            out["outlier_sweep_2b"] = {
+                "workload": "2b_sweep_outlier: the 2B set, 1% of channels x20, every width",
+                "widths": curve}
+        if args.per_proj:
+            out["per_projection_cold"] = per_projection(twd, torch, ls, M, kernel, reps)
+        if args.kv_commit:
+            out["kv_commit"] = kv_commit_bench(twd, torch, ls, reps)
+        if args.atlas and set_name == "2b":
+            log("graph atlas")
+            out["graph_atlas"] = atlas_bench(twd, torch, dev_set, max(5, reps // 4))
+        if args.projection_widths:
+            out["output_projection"] = output_projection_bench(
+                twd, torch, widths_of(args.projection_widths), reps)
+        del step
+        if set_name == "2b" and args.set4b_widths:
+            log("4B-class stack")
+            del dev_set
+            torch.cuda.empty_cache()
+            ds4 = LayerSetOnDevice(twd, torch, wl.SET_4B, wl.SET_4B.layers)
+            tab = {}
+            for Mw in widths_of(args.set4b_widths):
+                e = width_entry(twd, torch, ds4, "4b_stack", Mw, kernel, reps,
+                                forms=("sweep", "fused"), graphs=False)
+                tab[str(Mw)] = {"sweep_gbs": e["sweep"]["gbs"], "sweep_frac": e["sweep"]["frac"],
+                                "sweep_us": e["sweep"]["us"],
+                                "per_launch_gbs": e["per_launch"]["gbs"],
+                                "per_launch_kernels": e["per_launch"]["kernels"]}
+            out["set_4b"] = {"layer_set": "4B-class, hidden 3072, 36 layers",
+                             "packed_weight_bytes_per_step": ds4.bytes_per_sweep,
+                             "widths": tab}
+            del ds4
+            torch.cuda.empty_cache()
+        if args.cpu_seconds > 0:
+            if "output_projection" in out:
+                out["output_projection"]["cpu_baseline"] = cpu_projection_baseline(
+                    args.cpu_seconds / 5)
+            if "kv_commit" in out:
+                out["kv_commit"]["cpu_baseline"] = cpu_kv_baseline(args.cpu_seconds / 10)
+            out["cpu_baseline"] = cpu_baseline(ls, args.workload, M, outliers, args.cpu_seconds)
+            out["cpu_single_thread"] = cpu_baseline(ls, args.workload, M, outliers,
+                                                    args.cpu_seconds / 3, threads=1)
+    if args.copy_calibration:
+        out["copy_calibration_bytes"] = copy_calibration(twd, torch)
     print(json.dumps(out), flush=True)
 
 

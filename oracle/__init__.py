@@ -44,6 +44,30 @@ def build(force: bool = True) -> str:
     return _LIB_PATH
 
 
+NATIVE_FLAGS = ["-O3", "-march=native"]
+
+
+def build_native(path=None) -> str:
+    """Compile ``oracle.c`` with ``-O3 -march=native`` (plain loops, still no
+    fast-math or contraction) into a separate library for timing the oracle
+    on the machine it runs on; the tests keep the portable ``-O2`` build."""
+    import tempfile
+    path = path or os.path.join(tempfile.gettempdir(), f"liboracle_native_{os.getpid()}.so")
+    cmd = ["gcc", "-std=c11", *NATIVE_FLAGS, "-fPIC", "-shared", "-fopenmp",
+           "-ffp-contract=off", "-fno-fast-math", "-o", path, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    return path
+
+
+def select(path) -> None:
+    """Use the oracle library at ``path`` (e.g. from build_native) for the
+    calls that follow in this process."""
+    global _lib, _LIB_PATH
+    _LIB_PATH = path
+    _lib = None
+    _load()
+
+
 def _load():
     global _lib
     if _lib is not None:

@@ -382,12 +382,19 @@ def kv_commit(segments, c0: int, layers: int, row_bytes: int, block, W: int, n_m
     segments: device tensors, segment s holding [layers][2][c0 2^s][row_bytes]
     bytes; n_mat, n_new: device int32 (one element used); state_in /
     state_out: device int32[4], distinct."""
+    torch = _torch()
     nseg = len(segments)
+    seg_ptrs = []
     for s, t in enumerate(segments):
+        seg_ptrs.append(_dev_ptr(t, f"segment {s}").value)
         _need(_nbytes(t) >= layers * 2 * (c0 << s) * row_bytes,
               f"segment {s} smaller than layers * 2 * c0 * 2^s * row_bytes")
     _need(_nbytes(block) >= layers * 2 * W * row_bytes, "block smaller than its rows")
-    ptrs = (ctypes.c_void_p * max(nseg, 1))(*[t.data_ptr() for t in segments])
+    for name, t, n in (("n_mat", n_mat, 1), ("n_new", n_new, 1), ("state_in", state_in, 4),
+                       ("state_out", state_out, 4)):
+        _dev_ptr(t, name, (torch.int32,))
+        _need(t.numel() >= n, f"{name} must hold at least {n} int32 value(s)")
+    ptrs = (ctypes.c_void_p * max(nseg, 1))(*seg_ptrs)
     _check(_lib_kv_commit(ptrs, nseg, int(c0), int(layers), int(row_bytes),
                           _dev_ptr(block, "block"), int(W), _dev_ptr(n_mat, "n_mat"),
                           _dev_ptr(n_new, "n_new"), _dev_ptr(state_in, "state_in"),

@@ -1,8 +1,9 @@
 // Measurement references.  stream_read: the achievable-bandwidth reference,
 // a plain streaming read with the linear kernels' cache policy (16-byte
 // non-temporal loads) that fills the chip: at least one 256-thread workgroup
-// per compute unit (four per unit for large buffers), each lane keeping up to
-// eight loads in flight over a grid-stride loop.  It reduces what it reads
+// per compute unit (four per unit for large buffers), each lane keeping
+// eight loads in flight, each workgroup reading contiguous 32 KiB chunks in
+// turn.  It reduces what it reads
 // to one word and stores it only when it equals a guard value, so the loads
 // cannot be removed.  stream_copy: a plain copy of known size, the
 // calibration for the HBM byte counters (bytes read = bytes written = size).
@@ -21,14 +22,16 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(kThreads) void stream_read_kernel(
     const uint4 *__restrict__ p, int64_t n16, uint32_t *__restrict__ sink) {
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+    // workgroup g reads chunks g, g + G, ... of kThreads * kReadLoads words,
+    // each chunk contiguous: load u of a lane is word u * kThreads + lane
+    constexpr int64_t kChunk = int64_t(kThreads) * kReadLoads;
     uint32_t h = 0;
-    for (int64_t base = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; base < n16;
-         base += stride * kReadLoads) {
+    for (int64_t c = blockIdx.x; c * kChunk < n16; c += gridDim.x) {
+        const int64_t base = c * kChunk + threadIdx.x;
         v4u v[kReadLoads];
 #pragma unroll
         for (int u = 0; u < kReadLoads; ++u) {
-            const int64_t i = base + u * stride;
+            const int64_t i = base + int64_t(u) * kThreads;
             v[u] = i < n16 ? __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p + i))
                            : v4u{0u, 0u, 0u, 0u};
         }
@@ -74,7 +77,7 @@ hipError_t launch_stream_read(const void *buf, int64_t bytes, uint32_t *sink,
                               hipStream_t stream) {
     const int64_t n16 = bytes / 16;
     // one workgroup per compute unit at least; more (up to four per unit)
-    // while each lane still gets all eight of its loads
+    // while each gets a whole chunk
     int64_t grid = (n16 + int64_t(kThreads) * kReadLoads - 1) / (int64_t(kThreads) * kReadLoads);
     grid = grid < kCUs ? kCUs : grid > kMaxReadGroups ? kMaxReadGroups : grid;
     hipLaunchKernelGGL(stream_read_kernel, dim3(static_cast<uint32_t>(grid)),

@@ -282,21 +282,23 @@ def test_extreme_values(env):
     ("2b", "2b_verify", 19, 3),
     ("2b", "2b_verify", 7, 4),
     ("2b", "2b_verify", 7, 8),
-    ("2b", "2b_sweep_outlier", 3, 13),
+    ("2b", "2b_verify", 23, 16),
     ("4b", "4b_stack", 35, 1),
     ("4b", "4b_stack", 17, 4),
     ("4b", "4b_stack", 0, 16),
-])
+] + [("2b", "2b_sweep_outlier", (5 * M + 3) % 30, M) for M in range(1, 17)])
 def test_full_size_layer(env, set_name, workload, layer, M):
     """Every projection of one full-size layer, in the dispatch the benchmark
-    times, compared element by element."""
+    times (one launch per projection, AUTO), in both forms, compared element
+    by element; the outlier workload at every width 1..16."""
     torch, twd, orc = env
     ls = wl.LAYER_SETS[set_name]
+    threads = orc.max_threads()
     for pi, proj in enumerate(ls.projs):
         W = wl.layer_weights(ls, layer, pi)
         x = wl.layer_activations(workload, proj.K, M, layer, pi,
                                  outliers=workload == "2b_sweep_outlier")
-        ref = orc.forward(W, proj.segs, x)
+        ref = orc.forward(W, proj.segs, x, threads=threads)
         run_case(env, W, proj.segs, x, twd.KERNEL_AUTO, (set_name, layer, pi), ref=ref)
         run_case(env, W, proj.segs, x, twd.KERNEL_AUTO, (set_name, layer, pi), ref=ref,
                  fused=True)
@@ -304,12 +306,13 @@ def test_full_size_layer(env, set_name, workload, layer, M):
 
 # ------------------------------------------------------------ graph replay
 
-def test_linear_graph_replays_match_eager(env):
+def test_linear_graph_replays_match_oracle(env):
     """Every linear kernel family, in the one-launch bf16 form and in the
     two-launch form (quantize_act, then the int8 linear), captured into one
     graph: three replays, with eager work and synchronization between them,
-    each bit-identical to the eager results (quantized activations and
-    scales included)."""
+    each checked against the oracle (quantized activations and scales
+    bit-exact, acc bit-exact, y within 1e-6) and bit-identical to the eager
+    results."""
     torch, twd, orc = env
     cases = [("dot", 1, 2560, (96,)), ("dot", 3, 768, (40, 24)),
              ("mfma", 2, 2560, (64, 32, 32)), ("mfma", 9, 6912, (33,)),
@@ -320,6 +323,7 @@ def test_linear_graph_replays_match_eager(env):
         packed, gammas = twd.prepare_weights(W, segs)
         N = int(sum(segs))
         runs.append(dict(
+            ref=orc.forward(W, segs, x),
             fam=family(twd, fam), segs=segs, gammas=gammas,
             wp=torch.from_numpy(packed).cuda(), x=to_dev_bf16(torch, x),
             acc_f=torch.empty((M, N), dtype=torch.int32, device="cuda"),
@@ -362,6 +366,13 @@ def test_linear_graph_replays_match_eager(env):
                 if a.dtype == torch.float32:
                     a, b = a.view(torch.int32), b.view(torch.int32)
                 assert torch.equal(a, b), f"replay {rep}, case {cases[i]}, {k}"
+            o = r["ref"]
+            np.testing.assert_array_equal(r["xq"].cpu().numpy(), o["q"])
+            np.testing.assert_array_equal(r["xs"].cpu().numpy().view(np.uint32),
+                                          o["scale"].view(np.uint32))
+            for acc_k, y_k in (("acc_f", "y_f"), ("acc_i", "y_i")):
+                np.testing.assert_array_equal(r[acc_k].cpu().numpy(), o["acc"])
+                check_y(r[y_k].cpu().numpy(), o["y"])
         _ = sum(float(r["y_f"].sum()) for r in runs)  # eager work between replays
 
 

@@ -176,12 +176,15 @@ def test_full_output_projection_sampled(env, M):
     check_bound(yc.cpu().numpy()[:, rows], dot, absdot, K, f"critical full M={M}")
 
 
-def test_graph_replays_match_eager(env):
+def test_graph_replays_match_oracle(env):
     """Both roles captured into one graph: three replays, with eager work and
-    synchronization between them, each bit-identical to the eager results."""
+    synchronization between them, each within the fp32 summation bound of the
+    oracle and bit-identical to the eager results."""
     torch, twd, orc = env
     M, K, N = 5, 2560, 1000
     W, _, x = wl.random_case(11, M, K, (N,), w_sigma=0.02)
+    r8 = orc.fast_projection(W, x)
+    d16, a16 = orc.bf16_linear(x, wl.f32_to_bf16_bits(W))
     wq, ws = orc.quantize_fp8_rows(W)
     wq_d, ws_d = torch.from_numpy(wq).cuda(), torch.from_numpy(ws).cuda()
     wb = dev_bf16(torch, wl.f32_to_bf16_bits(W))
@@ -209,4 +212,6 @@ def test_graph_replays_match_eager(env):
         torch.cuda.synchronize()
         assert torch.equal(y8.view(torch.int32), ref8.view(torch.int32)), f"fast replay {rep}"
         assert torch.equal(y16.view(torch.int32), ref16.view(torch.int32)), f"critical replay {rep}"
+        check_bound(y8.cpu().numpy(), r8["y"], r8["yabs"], K, f"fast replay {rep}")
+        check_bound(y16.cpu().numpy(), d16, a16, K, f"critical replay {rep}")
         _ = (y8.sum() + y16.sum()).item()  # eager work between replays

@@ -256,3 +256,50 @@ def test_sweep_errors(env):
         x3 = torch.zeros((3, 256), dtype=torch.bfloat16, device="cuda")
         twd.Sweep([c.entry(), (c.wt, segs, c.gammas, x3, None, None)])
     del bad
+
+
+def test_sweep_width_atlas_replays_match_oracle(env):
+    """A width-keyed atlas: one captured graph per width, all held at once
+    over the same weights (each width with its own activation and output
+    buffers), replayed in an interleaved order, every replay checked against
+    the oracle."""
+    torch, twd, orc = env
+    shapes = [(2560, (96, 40, 40)), (6912, (48,)), (1024, (130,))]
+    base = []
+    for i, (K, segs) in enumerate(shapes):
+        W, segs, _ = wl.random_case(seed=300 + i, M=1, K=K, seg_rows=segs)
+        packed, gammas = twd.prepare_weights(W, segs)
+        N = int(sum(segs))
+        base.append((W, segs, gammas, torch.from_numpy(twd.tile_for_sweep(packed, N, K)).cuda()))
+    atlas = {}
+    for M in (1, 2, 5, 9, 16):
+        cases, entries = [], []
+        for i, (W, segs, gammas, wt) in enumerate(base):
+            _, _, x = wl.random_case(seed=400 + 17 * M + i, M=M, K=W.shape[1], seg_rows=segs)
+            N = int(sum(segs))
+            acc = torch.empty((M, N), dtype=torch.int32, device="cuda")
+            y = torch.empty((M, N), device="cuda")
+            entries.append((wt, segs, gammas, dev_bf16(torch, x), acc, y))
+            cases.append((W, segs, x, acc, y, orc.forward(W, segs, x)))
+        sw = twd.Sweep(entries)
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            sw.run()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                sw.run()
+        atlas[M] = (g, sw, cases)
+    log(f"atlas of {len(atlas)} graphs held")
+    for rep, M in enumerate((16, 1, 9, 2, 5, 1, 16, 9)):
+        g, _, cases = atlas[M]
+        for (_, _, _, acc, y, _) in cases:
+            acc.fill_(-3)
+            y.fill_(-3.0)
+        g.replay()
+        torch.cuda.synchronize()
+        for (W, segs, x, acc, y, ref) in cases:
+            np.testing.assert_array_equal(acc.cpu().numpy(), ref["acc"])
+            check_y(y.cpu().numpy(), ref["y"], f"atlas M={M} replay {rep}")
+        _ = float(cases[0][4].sum())  # eager work between replays

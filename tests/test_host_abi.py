@@ -289,6 +289,52 @@ def test_kv_commit_rejects_before_launch(twd):
     assert twd._lib_last_error()
 
 
+class _FakeDev:
+    """Stands in for a device tensor in binding checks that must fail before
+    any library call (no GPU here)."""
+
+    def __init__(self, n, dtype="int32", contiguous=True, cuda=True, esize=4):
+        import torch
+        self.n, self.dtype = n, getattr(torch, dtype)
+        self._contig, self.is_cuda, self.esize = contiguous, cuda, esize
+
+    def is_contiguous(self):
+        return self._contig
+
+    def data_ptr(self):
+        return 0x100000
+
+    def numel(self):
+        return self.n
+
+    def element_size(self):
+        return self.esize
+
+
+def test_kv_commit_binding_checks_tensors(twd):
+    """The binding refuses host, non-contiguous or short tensors for the
+    segments, counts and state words before calling the library."""
+    pytest.importorskip("torch")
+    c0, layers, row = 2, 2, 16
+    segs = [_FakeDev(layers * 2 * (c0 << s) * row, "uint8", esize=1) for s in range(2)]
+    block = _FakeDev(layers * 2 * 4 * row, "uint8", esize=1)
+    good = dict(n_mat=_FakeDev(1), n_new=_FakeDev(1), state_in=_FakeDev(4),
+                state_out=_FakeDev(4))
+
+    def call(segments=segs, **kw):
+        a = dict(good, **kw)
+        twd.kv_commit(segments, c0, layers, row, block, 4, a["n_mat"], a["n_new"],
+                      a["state_in"], a["state_out"])
+
+    for bad in (dict(segments=[segs[0], _FakeDev(10 ** 6, "uint8", cuda=False, esize=1)]),
+                dict(segments=[segs[0], _FakeDev(10 ** 6, "uint8", contiguous=False, esize=1)]),
+                dict(n_mat=_FakeDev(0)), dict(n_new=_FakeDev(1, cuda=False)),
+                dict(state_in=_FakeDev(3)), dict(state_out=_FakeDev(4, contiguous=False)),
+                dict(state_in=_FakeDev(4, "float32"))):
+        with pytest.raises(ValueError):
+            call(**bad)
+
+
 def test_profile_summary_refuses_runs_of_other_sources(tmp_path):
     """A counter record is stamped with the kernel-source hash of the run it
     summarizes: a run that printed another hash is refused, so stale counters
@@ -298,9 +344,10 @@ def test_profile_summary_refuses_runs_of_other_sources(tmp_path):
     import sys
     run = tmp_path / "run.json"
     run.write_text(json.dumps({"kernel_source_hash": "0" * 16,
-                               "projection_source_hash": "0" * 16}) + "\n")
+                               "projection_source_hash": "0" * 16,
+                               "sweep_source_hash": "0" * 16}) + "\n")
     d = str(tmp_path)
-    for flag in ("--summarize-profile", "--summarize-projection"):
+    for flag in ("--summarize-profile", "--summarize-projection", "--summarize-sweep"):
         r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), flag, d, d, d,
                             "--profile-run-json", str(run), "--profile-out", d],
                            capture_output=True, text=True, cwd=ROOT)
