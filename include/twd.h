@@ -123,7 +123,15 @@ twd_status twd_quantize_act(const uint16_t *x_bf16, int64_t M, int64_t K,
                             int8_t *xq, float *xscale, void *stream);
 
 /* W2A8 ternary linear: acc[m][n] = sum_k xq[m][k] * t[n][k] in int32
- * (exact), y[m][n] = acc[m][n] * xscale[m] * gamma in fp32.
+ * (exact), y[m][n] = acc[m][n] * xscale[m] * gamma in fp32.  The packed
+ * low-bit operator that M1 selects by replay width and input/output
+ * dimensions (page "BitMTP: When Multi-Token Prediction Meets Low-Bit Large
+ * Language Models", ai.info AI summary, "Methodology in Plain English", last
+ * paragraph), in the W2A8 setting ("Main Findings", first bullet): ternary
+ * weights with one absmean scale, int8 activations with one scale per token
+ * (BitNet b1.58, named in "What This Paper Is About").  The pages give no
+ * rounding order for the dequantization; the two fp32 products are taken in
+ * the order written.
  * wpacked: device packed weights [N][K/4] (format above); xq, xscale: the
  * outputs of twd_quantize_act; acc (int32 [M][N]) and y (fp32 [M][N]) are
  * device outputs, either may be NULL (not both).
@@ -136,7 +144,11 @@ twd_status twd_ternary_linear(const uint8_t *wpacked, float gamma,
                               int32_t *acc, float *y, void *stream);
 
 /* Fused projections (Q/K/V, gate/up): one launch over the concatenated
- * output rows.  seg_rows / seg_gamma are HOST arrays of nseg (1..4) entries:
+ * output rows.  The operator of twd_ternary_linear (same page and passages)
+ * applied to projections that read the same activations; each keeps its own
+ * absmean scale, as BitNet b1.58 ternarizes each weight tensor on its own.
+ * The pages do not describe the fusion; it is a launch-count choice of this
+ * library and changes no result.  seg_rows / seg_gamma are HOST arrays of nseg (1..4) entries:
  * segment s covers the next seg_rows[s] rows and is dequantized with
  * seg_gamma[s].  They are copied into the kernel arguments, so a captured
  * graph keeps them.  N = sum of seg_rows; other arguments as above. */
