@@ -162,25 +162,43 @@ struct SpanOut {
     int N;
     int qs;     // row sum of q for token r
     float sc;   // scale of token r
+    bool vec;   // 16-byte stores: N % 4 == 0 and both outputs 16-byte aligned
 };
 
-// After a tile's last pass: lane (token r, group g) holds rows 4g .. 4g+3.
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// After a tile's last pass: lane (token r, group g) holds rows 4g .. 4g+3,
+// four consecutive outputs of token r, written with one 16-byte store each
+// for acc and y where the row layout allows it.
 template <int M>
 __device__ __forceinline__ void epilogue(const SpanOut &so, int t, int r, int g, const v4i &c0,
                                          const v4i &c3, const v4i &c4, const v4i &c16) {
     const v4i cc = c0 + c3 + (c4 >> 2) + (c16 >> 4);
     const int n0 = 16 * t + 4 * g;
+    v4i tot;
+    v4f yv;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int n = n0 + i;
-        const int total = cc[i] - so.qs;
-        const float yv = static_cast<float>(total) * so.sc * row_gamma(so.segs, n);
-        if (r < M && n < so.N) {
-            const int64_t o = static_cast<int64_t>(r) * so.N + n;
+        tot[i] = cc[i] - so.qs;
+        yv[i] = static_cast<float>(tot[i]) * so.sc * row_gamma(so.segs, n0 + i);
+    }
+    if (r < M && n0 < so.N) {
+        const int64_t o = static_cast<int64_t>(r) * so.N + n0;
+        if (so.vec) {
+            // N % 4 == 0, so n0 < N means all four rows are in range
             if (so.acc)
-                so.acc[o] = total;
+                *reinterpret_cast<v4i *>(so.acc + o) = tot;
             if (so.y)
-                so.y[o] = yv;
+                *reinterpret_cast<v4f *>(so.y + o) = yv;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (n0 + i < so.N) {
+                    if (so.acc)
+                        so.acc[o + i] = tot[i];
+                    if (so.y)
+                        so.y[o + i] = yv[i];
+                }
         }
     }
 }
@@ -191,9 +209,6 @@ template <int M, int NW, int kS, int SW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(SW)))
 void sweep_kernel(const SweepHeader *header_g, const SweepProj *projs_g,
                   const SweepWork *work_g, uint32_t check) {
-    constexpr int T = 64 * NW;
-    // chunks of 8 activations per thread and token row: K <= 8192
-    constexpr int kRounds = (TWD_MAX_K / 8 + T - 1) / T;
     extern __shared__ __align__(16) uint8_t smem[];
     uint8_t *zero = smem;  // 64 zero bytes
     uint32_t *st_max = reinterpret_cast<uint32_t *>(smem + 64);  // [span][16]
@@ -214,114 +229,94 @@ void sweep_kernel(const SweepHeader *header_g, const SweepProj *projs_g,
     const cptr<SweepWork> wk = (cptr<SweepWork>)work_g + blockIdx.x;
     const int nspan = wk->nspan;
 
-    // 1. stage the activations of every span: absmax per token row, then
-    //    the int8 rows in the permuted B layout and their row sums
+    // 1. stage the activations of every span.  Token row m is quantized by
+    //    kWpr waves (a whole wave per row once M >= NW; waves past the last
+    //    row idle): their lanes take the row's chunks of 8 activations in
+    //    turn, all loaded in one round trip and kept in registers from the
+    //    absmax to the rounding.  With one wave per row the absmax and the row
+    //    sum are wave reductions and need no barrier.
+    constexpr int kWpr = M >= NW ? 1 : NW / M;
+    constexpr int kLanes = 64 * kWpr;
+    // chunk rounds per lane: K <= 8192
+    constexpr int kRounds = (TWD_MAX_K / 8 + kLanes - 1) / kLanes;
+    const int m = wave / kWpr;               // this wave's token row
+    const int cl = 64 * (wave % kWpr) + lane;  // its first chunk of the row
     if (tid < 16 + 2 * kSweepMaxSpans * 16)
         reinterpret_cast<uint32_t *>(smem)[tid] = 0u;
     __syncthreads();
-    for (int s = 0; s < nspan; ++s) {
-        const cptr<SweepProj> P = projs + wk->span[s].q;
-        const int K = P->K;
-        const int C = K >> 3;
-        const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t *>(P->x), 0, M * K * 2, kRawBufferFlags);
-        // token rows in groups whose loads are all issued before any is used
-        constexpr int G = M < 4 ? M : 4;
-        for (int m0 = 0; m0 < M; m0 += G) {
-            uint4 v[G][kRounds];
-#pragma unroll
-            for (int gm = 0; gm < G; ++gm)
-#pragma unroll
-                for (int i = 0; i < kRounds; ++i) {
-                    const int ch = tid + T * i;
-                    const int m = m0 + gm;
-                    const uint32_t off = ch < C && m < M
-                                             ? static_cast<uint32_t>((m * K + 8 * ch) * 2)
-                                             : kOutOfRange;
-                    const auto x = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
-                    v[gm][i] = make_uint4(x[0], x[1], x[2], x[3]);
-                }
-            __builtin_amdgcn_sched_barrier(0);
-            uint32_t mv[G];
-#pragma unroll
-            for (int gm = 0; gm < G; ++gm) {
-                u16x2 am = {0, 0};
-#pragma unroll
-                for (int i = 0; i < kRounds; ++i) {
-                    am = absmax_pair(am, v[gm][i].x);
-                    am = absmax_pair(am, v[gm][i].y);
-                    am = absmax_pair(am, v[gm][i].z);
-                    am = absmax_pair(am, v[gm][i].w);
-                }
-                mv[gm] = absmax_bits(am);
-            }
-            row_max16<G>(mv);
-            if ((lane & 15) == 15) {
-#pragma unroll
-                for (int gm = 0; gm < G; ++gm)
-                    if (m0 + gm < M)
-                        __hip_atomic_fetch_max(&st_max[s * 16 + m0 + gm], mv[gm],
-                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-            }
-        }
-    }
-    __syncthreads();  // absmax of every token row
     for (int s = 0; s < nspan; ++s) {
         const SweepSpan sp = span_at(wk, s);
         const cptr<SweepProj> P = projs + sp.q;
         const int K = P->K;
         const int C = K >> 3;
-        const int stride = P->stride;
+        // Every round is loaded and every load feeds the absmax, on every
+        // path: rounds past the row end, and waves without a row (an empty
+        // descriptor), load zeros without memory traffic.  Loads or uses
+        // behind a branch would leave the compiler unsure which loads are
+        // still in flight at the next span, and it would then wait for all of
+        // them before each new load.
+        const bool has_row = m < M;
         const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t *>(P->x), 0, M * K * 2, kRawBufferFlags);
-        constexpr int G = M < 4 ? M : 4;
-        for (int m0 = 0; m0 < M; m0 += G) {
-            uint4 v[G][kRounds];
+            const_cast<uint16_t *>(P->x) + (has_row ? static_cast<int64_t>(m) * K : 0), 0,
+            has_row ? K * 2 : 0, kRawBufferFlags);
+        uint4 v[kRounds];
 #pragma unroll
-            for (int gm = 0; gm < G; ++gm)
+        for (int i = 0; i < kRounds; ++i) {
+            const int ch = cl + kLanes * i;
+            const uint32_t off = ch < C ? static_cast<uint32_t>(16 * ch) : kOutOfRange;
+            const auto x = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
+            v[i] = make_uint4(x[0], x[1], x[2], x[3]);
+        }
+        u16x2 am = {0, 0};
 #pragma unroll
-                for (int i = 0; i < kRounds; ++i) {
-                    const int ch = tid + T * i;
-                    const int m = m0 + gm;
-                    const uint32_t off = ch < C && m < M
-                                             ? static_cast<uint32_t>((m * K + 8 * ch) * 2)
-                                             : kOutOfRange;
-                    const auto x = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
-                    v[gm][i] = make_uint4(x[0], x[1], x[2], x[3]);
-                }
-            __builtin_amdgcn_sched_barrier(0);
-            int sq[G];
+        for (int i = 0; i < kRounds; ++i) {
+            am = absmax_pair(am, v[i].x);
+            am = absmax_pair(am, v[i].y);
+            am = absmax_pair(am, v[i].z);
+            am = absmax_pair(am, v[i].w);
+        }
+        uint32_t amax = wave_umax(absmax_bits(am));
+        // the rounding skips rounds that hold no chunk below C (uniformly
+        // over the wave)
+        const int first = cl - lane;
+        if constexpr (kWpr > 1) {
+            if (m < M && lane == 0)
+                __hip_atomic_fetch_max(&st_max[s * 16 + m], amax, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+            __syncthreads();  // absmax of every token row of this span
+            if (m < M)
+                amax = st_max[s * 16 + m];
+        }
+        if (m < M) {
+            const float a_m = __uint_as_float(amax);
+            // correctly rounded fp32 divisions (build flag), as in the
+            // stand-alone quantizer; an all-zero row quantizes to zeros
+            const float inv = a_m > 0.0f ? 127.0f / a_m : 0.0f;
+            if (cl == 0)
+                st_scale[s * 16 + m] = a_m / 127.0f;
+            uint8_t *row = xbase + sp.xoff + m * P->stride;
+            int sq = 0;
 #pragma unroll
-            for (int gm = 0; gm < G; ++gm) {
-                const int m = m0 + gm;
-                const float a_m = __uint_as_float(st_max[s * 16 + (m < M ? m : 0)]);
-                // correctly rounded fp32 divisions (build flag), as in the
-                // stand-alone quantizer; an all-zero row quantizes to zeros
-                const float inv = a_m > 0.0f ? 127.0f / a_m : 0.0f;
-                if (tid == 0 && m < M)
-                    st_scale[s * 16 + m] = a_m / 127.0f;
-                uint8_t *row = xbase + sp.xoff + m * stride;
-                sq[gm] = 0;
-#pragma unroll
-                for (int i = 0; i < kRounds; ++i) {
-                    const int ch = tid + T * i;
-                    const uint32_t q0 = quant4(v[gm][i].x, v[gm][i].y, inv);
-                    const uint32_t q1 = quant4(v[gm][i].z, v[gm][i].w, inv);
-                    if (ch < C && m < M) {
+            for (int i = 0; i < kRounds; ++i) {
+                if (first + kLanes * i < C) {
+                    const int ch = cl + kLanes * i;
+                    const uint32_t q0 = quant4(v[i].x, v[i].y, inv);
+                    const uint32_t q1 = quant4(v[i].z, v[i].w, inv);
+                    if (ch < C) {
                         *reinterpret_cast<uint32_t *>(row + 4 * permuted_word(2 * ch)) = q0;
                         *reinterpret_cast<uint32_t *>(row + 4 * permuted_word(2 * ch + 1)) = q1;
                     }
-                    sq[gm] = sdot4(q0, kOnes, sq[gm]);
-                    sq[gm] = sdot4(q1, kOnes, sq[gm]);
+                    sq = sdot4(q0, kOnes, sq);
+                    sq = sdot4(q1, kOnes, sq);
                 }
             }
-            row_sum16<G>(sq);
-            if ((lane & 15) == 15) {
-#pragma unroll
-                for (int gm = 0; gm < G; ++gm)
-                    if (m0 + gm < M)
-                        __hip_atomic_fetch_add(&st_sum[s * 16 + m0 + gm], sq[gm],
-                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            sq = wave_sum(sq);
+            if (lane == 0) {
+                if constexpr (kWpr == 1)
+                    st_sum[s * 16 + m] = sq;
+                else
+                    __hip_atomic_fetch_add(&st_sum[s * 16 + m], sq, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_WORKGROUP);
             }
         }
     }
@@ -350,6 +345,9 @@ void sweep_kernel(const SweepHeader *header_g, const SweepProj *projs_g,
         so.N = P->N;
         so.qs = st_sum[s * 16 + r];
         so.sc = st_scale[s * 16 + r];
+        so.vec = (so.N & 3) == 0 &&
+                 ((reinterpret_cast<uintptr_t>(so.acc) | reinterpret_cast<uintptr_t>(so.y)) &
+                  15) == 0;
         const uint8_t *bsrc = r < M ? xbase + sp.xoff + r * P->stride + 64 * g : zero;
         const int ustep = r < M ? 256 : 0;
 
