@@ -34,6 +34,8 @@
 // activation block (token columns at or past M read a zero block).  After a
 // tile's last pass, lane (token r, group g) holds rows 4g..4g+3 for token r:
 // sum q t = sum q c - sum q, then the dequant epilogue.
+#include <type_traits>
+
 #include "kernel_common.h"
 
 namespace twd {
@@ -203,6 +205,62 @@ __device__ __forceinline__ void epilogue(const SpanOut &so, int t, int r, int g,
     }
 }
 
+// A wave's walk over its passes, across the spans of its workgroup: tiles
+// t0 + first, t0 + first + NW, ... of each span in turn (first from the turn
+// carried over from the spans before), each tile's passes in order.  Past
+// the last span the cursor stays on an empty span (t1 = 0), whose loads
+// return zeros without memory traffic.
+struct Cursor {
+    SpanW w;     // weights of the current span
+    PassPos c;   // tile and pass
+    int passes;  // passes per tile in the current span
+    int t0;      // first tile of the current span
+    int s;       // current span
+    int turn;    // tiles of the spans before s, modulo NW
+};
+
+// Enter span s, or the first span after it in which this wave has a tile.
+template <int NW>
+__device__ __forceinline__ void enter(Cursor &cu, int s, int nspan, int wave,
+                                      cptr<SweepWork> wk, cptr<SweepProj> projs) {
+    for (; s < nspan; ++s) {
+        const SweepSpan sp = span_at(wk, s);
+        const int first = (wave - cu.turn + NW) % NW;
+        if (sp.t0 + first < sp.t1) {
+            const cptr<SweepProj> P = projs + sp.q;
+            cu.w.w = P->w;
+            cu.w.tile_bytes = 1024 * P->slices;
+            cu.w.t1 = sp.t1;
+            cu.passes = P->passes;
+            cu.t0 = sp.t0;
+            cu.c = PassPos{sp.t0 + first, 0};
+            cu.s = s;
+            return;
+        }
+        cu.turn = (cu.turn + sp.t1 - sp.t0) % NW;
+    }
+    cu.w.t1 = 0;
+    cu.passes = 1;
+    cu.t0 = 0;
+    cu.c = PassPos{0, 0};
+    cu.s = nspan;
+}
+
+// Next pass; true when the cursor moved to another span.
+template <int NW>
+__device__ __forceinline__ bool advance(Cursor &cu, int nspan, int wave, cptr<SweepWork> wk,
+                                        cptr<SweepProj> projs) {
+    if (++cu.c.p < cu.passes)
+        return false;
+    cu.c.p = 0;
+    cu.c.t += NW;
+    if (cu.c.t < cu.w.t1 || cu.s >= nspan)
+        return false;
+    cu.turn = (cu.turn + cu.w.t1 - cu.t0) % NW;
+    enter<NW>(cu, cu.s + 1, nspan, wave, wk, projs);
+    return true;
+}
+
 // Built for SW resident waves per SIMD (512 / SW registers per lane) with a
 // register ring of kS passes.
 template <int M, int NW, int kS, int SW>
@@ -229,6 +287,26 @@ void sweep_kernel(const SweepHeader *header_g, const SweepProj *projs_g,
     const cptr<SweepWork> wk = (cptr<SweepWork>)work_g + blockIdx.x;
     const int nspan = wk->nspan;
 
+    // The issue cursor f runs kS - 1 passes ahead of the compute cursor c,
+    // from span to span, so the ring never drains at a span boundary.  Its
+    // first kS - 1 passes go out before the staging at M <= 2 (after the
+    // first span's activation loads), so the first weights arrive while the
+    // activations are quantized; at larger M the staging holds too many
+    // registers for the ring to be live across it.
+    constexpr bool kEarly = M <= 2;
+    Cursor f;
+    f.turn = 0;
+    enter<NW>(f, 0, nspan, wave, wk, projs);
+    const Cursor c0s = f;
+    uint4 ring[kS][kSweepLP];
+    auto prologue = [&]() {
+#pragma unroll
+        for (int k = 0; k < kS - 1; ++k) {
+            issue(f.w, f.c, lane, ring[k]);
+            advance<NW>(f, nspan, wave, wk, projs);
+        }
+    };
+
     // 1. stage the activations of every span.  Token row m is quantized by
     //    kWpr waves (a whole wave per row once M >= NW; waves past the last
     //    row idle): their lanes take the row's chunks of 8 activations in
@@ -244,7 +322,7 @@ void sweep_kernel(const SweepHeader *header_g, const SweepProj *projs_g,
     if (tid < 16 + 2 * kSweepMaxSpans * 16)
         reinterpret_cast<uint32_t *>(smem)[tid] = 0u;
     __syncthreads();
-    for (int s = 0; s < nspan; ++s) {
+    auto stage = [&](int s, auto early) {
         const SweepSpan sp = span_at(wk, s);
         const cptr<SweepProj> P = projs + sp.q;
         const int K = P->K;
@@ -267,6 +345,8 @@ void sweep_kernel(const SweepHeader *header_g, const SweepProj *projs_g,
             const auto x = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
             v[i] = make_uint4(x[0], x[1], x[2], x[3]);
         }
+        if constexpr (decltype(early)::value)
+            prologue();
         u16x2 am = {0, 0};
 #pragma unroll
         for (int i = 0; i < kRounds; ++i) {
@@ -319,26 +399,42 @@ void sweep_kernel(const SweepHeader *header_g, const SweepProj *projs_g,
                                            __HIP_MEMORY_SCOPE_WORKGROUP);
             }
         }
-    }
+    };
+    if (nspan > 0)
+        stage(0, std::integral_constant<bool, kEarly>{});
+    else if constexpr (kEarly)
+        prologue();  // the same loads on both paths (all past the end here)
+    for (int s = 1; s < nspan; ++s)
+        stage(s, std::false_type{});
     __syncthreads();  // staged rows, row sums and scales
+    if constexpr (!kEarly)
+        prologue();
 
-    // 2. stream each span's tiles: compute the pass in one ring slot while
-    //    the next kS - 1 passes' loads are in flight
-    uint4 ring[kS][kSweepLP];
-    v4i c0 = {0, 0, 0, 0}, c3 = c0, c4 = c0, c16 = c0;
-    int turn = 0;  // tiles of the spans before, modulo NW
-    for (int s = 0; s < nspan; ++s) {
+    // 2. stream: compute the pass in one ring slot while the next kS - 1
+    //    passes' loads are in flight, the loads running ahead across spans.
+    //    Passes of this wave: sum over spans of its tiles times the passes
+    //    per tile.
+    int left = 0;
+    {
+        int turn = 0;
+        for (int s = 0; s < nspan; ++s) {
+            const SweepSpan sp = span_at(wk, s);
+            const int first = (wave - turn + NW) % NW;
+            turn = (turn + sp.t1 - sp.t0) % NW;
+            if (sp.t0 + first < sp.t1)
+                left += (sp.t1 - sp.t0 - first + NW - 1) / NW * projs[sp.q].passes;
+        }
+    }
+    Cursor c = c0s;
+    SpanOut so;
+    const uint8_t *bsrc;
+    int ustep, slices;
+    // the compute side of the span c is in
+    auto load_span = [&]() {
+        const int s = c.s < nspan ? c.s : 0;
         const SweepSpan sp = span_at(wk, s);
         const cptr<SweepProj> P = projs + sp.q;
-        const int first = (wave - turn + NW) % NW;  // this wave's first tile
-        turn = (turn + sp.t1 - sp.t0) % NW;
-        SpanW sw;
-        sw.w = P->w;
-        sw.tile_bytes = 1024 * P->slices;
-        sw.t1 = sp.t1;
-        const int passes = P->passes;
-        const int slices = P->slices;
-        SpanOut so;
+        slices = P->slices;
         so.acc = P->acc;
         so.y = P->y;
         so.segs = segs_of(P);
@@ -348,43 +444,34 @@ void sweep_kernel(const SweepHeader *header_g, const SweepProj *projs_g,
         so.vec = (so.N & 3) == 0 &&
                  ((reinterpret_cast<uintptr_t>(so.acc) | reinterpret_cast<uintptr_t>(so.y)) &
                   15) == 0;
-        const uint8_t *bsrc = r < M ? xbase + sp.xoff + r * P->stride + 64 * g : zero;
-        const int ustep = r < M ? 256 : 0;
-
-        // passes of this wave in the span: tiles t0 + first, + NW, ...
-        const int tiles =
-            sp.t0 + first < sp.t1 ? (sp.t1 - sp.t0 - first + NW - 1) / NW : 0;
-        int left = tiles * passes;
-        PassPos c{sp.t0 + first, 0};
-        PassPos f = c;
-#pragma unroll
-        for (int k = 0; k < kS - 1; ++k) {
-            issue(sw, f, lane, ring[k]);
-            step<NW>(f, passes);
-        }
-        // one step: issue the pass kS - 1 ahead into the slot freed by the
-        // last step, then compute the pass in slot CUR
+        bsrc = r < M ? xbase + sp.xoff + r * P->stride + 64 * g : zero;
+        ustep = r < M ? 256 : 0;
+    };
+    load_span();
+    v4i c0 = {0, 0, 0, 0}, c3 = c0, c4 = c0, c16 = c0;
+    // one step: issue the pass kS - 1 ahead into the slot freed by the last
+    // step, then compute the pass in slot CUR
 #define TWD_SWEEP_STEP(CUR)                                                    \
-    issue(sw, f, lane, ring[((CUR) + kS - 1) % kS]);                           \
-    step<NW>(f, passes);                                                       \
-    compute(c.p, slices, bsrc, ustep, zero, ring[CUR], c0, c3, c4, c16);       \
-    if (c.p == passes - 1)                                                     \
-        epilogue<M>(so, c.t, r, g, c0, c3, c4, c16);                           \
-    step<NW>(c, passes);
-        for (; left >= kS; left -= kS) {
+    issue(f.w, f.c, lane, ring[((CUR) + kS - 1) % kS]);                        \
+    advance<NW>(f, nspan, wave, wk, projs);                                    \
+    compute(c.c.p, slices, bsrc, ustep, zero, ring[CUR], c0, c3, c4, c16);     \
+    if (c.c.p == c.passes - 1)                                                 \
+        epilogue<M>(so, c.c.t, r, g, c0, c3, c4, c16);                         \
+    if (advance<NW>(c, nspan, wave, wk, projs))                                \
+        load_span();
+    for (; left >= kS; left -= kS) {
 #pragma unroll
-            for (int k = 0; k < kS; ++k) {
-                TWD_SWEEP_STEP(k)
-            }
+        for (int k = 0; k < kS; ++k) {
+            TWD_SWEEP_STEP(k)
         }
-#pragma unroll
-        for (int k = 0; k < kS - 1; ++k) {
-            if (left > k) {
-                TWD_SWEEP_STEP(k)
-            }
-        }
-#undef TWD_SWEEP_STEP
     }
+#pragma unroll
+    for (int k = 0; k < kS - 1; ++k) {
+        if (left > k) {
+            TWD_SWEEP_STEP(k)
+        }
+    }
+#undef TWD_SWEEP_STEP
 }
 
 using Fn = void (*)(const SweepHeader *, const SweepProj *, const SweepWork *, uint32_t);
