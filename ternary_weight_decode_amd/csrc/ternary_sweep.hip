@@ -239,6 +239,8 @@ __device__ __forceinline__ void enter(Cursor &cu, int s, int nspan, int wave,
         }
         cu.turn = (cu.turn + sp.t1 - sp.t0) % NW;
     }
+    cu.w.w = nullptr;  // an empty descriptor: every load is out of range
+    cu.w.tile_bytes = 0;
     cu.w.t1 = 0;
     cu.passes = 1;
     cu.t0 = 0;

@@ -108,6 +108,27 @@ def test_sweep_random_lists(env, M):
         c.check(orc)
 
 
+@pytest.mark.parametrize("M", [1, 2, 5, 9, 16])
+def test_sweep_tiny_projections_cross_spans(env, M):
+    """Many projections of one or two 16-row tiles (ragged N): each workgroup
+    holds four spans and most of its waves own no tile in most of them, so
+    the loads that run ahead skip from span to span."""
+    torch, twd, orc = env
+    rng = np.random.default_rng([17, M])
+    cases = []
+    for i in range(40):
+        K = 64 * int(rng.integers(1, 41))
+        N = int(rng.integers(1, 33))
+        W, segs, x = wl.random_case(seed=4000 + 50 * M + i, M=M, K=K, seg_rows=(N,))
+        cases.append(Case(env, W, segs, x, want_acc=i % 3 != 1, want_y=i % 3 != 2))
+    sw = twd.Sweep([c.entry() for c in cases])
+    log(f"sweep tiny projections M={M}: {len(cases)} projections, {sw.plan.nwg} workgroups")
+    sw.run()
+    torch.cuda.synchronize()
+    for c in cases:
+        c.check(orc)
+
+
 @pytest.mark.parametrize("M", [1, 3, 16])
 def test_sweep_zero_rows_and_empty_projections(env, M):
     """All-zero token rows (scale 0, outputs 0) and projections with N = 0."""
@@ -123,6 +144,11 @@ def test_sweep_zero_rows_and_empty_projections(env, M):
     torch.cuda.synchronize()
     cases[1].check(orc)
     assert not cases[1].acc[0].any() and not cases[1].y[0].any()
+    # a list of empty projections only: one workgroup that stages nothing
+    empty = twd.Sweep([cases[0].entry(), cases[2].entry()])
+    assert empty.plan.nwg == 1 and empty.weight_bytes == 0
+    empty.run()
+    torch.cuda.synchronize()
 
 
 @pytest.mark.parametrize("M", list(range(1, 17)))
