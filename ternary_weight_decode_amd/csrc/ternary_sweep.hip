@@ -20,9 +20,12 @@
 // across tile and projection boundaries, with no barrier and no kernel
 // boundary until the list ends.
 //
-// Work split.  The waves of a workgroup take its tiles in turn (the turn
-// carries over from one projection to the next).  A tile (16 weight rows,
-// all of K) is read in passes of four 256-wide K slices.  The weights come in
+// Work split.  One workgroup of 16 waves per compute unit; its waves take
+// the tiles of each of its projections one at a time from an LDS counter, so
+// they run out of work together (a fixed share per wave left the compute
+// unit with fewer and fewer loads in flight as its faster waves finished).
+// A tile (16 weight rows, all of K) is read in passes of four 256-wide K
+// slices.  The weights come in
 // the sweep's tiled layout (twd_sweep_tile_weights): tile t is a contiguous
 // run of ceil(K / 256) blocks of 1 KiB, block u holding, at lane l = 16 g +
 // r, the 16 packed bytes of tile row r at K offset 256 u + 64 g -- so each
@@ -205,63 +208,59 @@ __device__ __forceinline__ void epilogue(const SpanOut &so, int t, int r, int g,
     }
 }
 
-// A wave's walk over its passes, across the spans of its workgroup: tiles
-// t0 + first, t0 + first + NW, ... of each span in turn (first from the turn
-// carried over from the spans before), each tile's passes in order.  Past
-// the last span the cursor stays on an empty span (t1 = 0), whose loads
-// return zeros without memory traffic.
-struct Cursor {
-    SpanW w;     // weights of the current span
-    PassPos c;   // tile and pass
-    int passes;  // passes per tile in the current span
-    int t0;      // first tile of the current span
-    int s;       // current span
-    int turn;    // tiles of the spans before s, modulo NW
-};
+// The next tile of span s from the workgroup's LDS counter: one lane takes
+// it, the whole wave gets it as a uniform value.
+__device__ __forceinline__ int fetch_tile(int *ctr, int s, int lane) {
+    int t = 0;
+    if (lane == 0)
+        t = __hip_atomic_fetch_add(&ctr[s], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return __builtin_amdgcn_readfirstlane(t);
+}
 
-// Enter span s, or the first span after it in which this wave has a tile.
-template <int NW>
-__device__ __forceinline__ void enter(Cursor &cu, int s, int nspan, int wave,
-                                      cptr<SweepWork> wk, cptr<SweepProj> projs) {
-    for (; s < nspan; ++s) {
-        const SweepSpan sp = span_at(wk, s);
-        const int first = (wave - cu.turn + NW) % NW;
-        if (sp.t0 + first < sp.t1) {
-            const cptr<SweepProj> P = projs + sp.q;
-            cu.w.w = P->w;
-            cu.w.tile_bytes = 1024 * P->slices;
-            cu.w.t1 = sp.t1;
-            cu.passes = P->passes;
-            cu.t0 = sp.t0;
-            cu.c = PassPos{sp.t0 + first, 0};
-            cu.s = s;
-            return;
+// The issue side's position: span s, tile t, pass p.  A wave takes the tiles
+// of span s one at a time from the span's counter; when the span runs out it
+// moves on to the next span.  Past the last span the position holds an empty
+// descriptor (loads return zeros without memory traffic) and s = nspan.
+struct DynCursor {
+    SpanW w;
+    int t, p, passes, s;
+
+    __device__ __forceinline__ void begin(int s0, int nspan, cptr<SweepWork> wk,
+                                          cptr<SweepProj> projs, int *ctr, int lane) {
+        for (s = s0; s < nspan; ++s) {
+            const SweepSpan sp = span_at(wk, s);
+            t = fetch_tile(ctr, s, lane);
+            if (t < sp.t1) {
+                const cptr<SweepProj> P = projs + sp.q;
+                w.w = P->w;
+                w.tile_bytes = 1024 * P->slices;
+                w.t1 = sp.t1;
+                passes = P->passes;
+                p = 0;
+                return;
+            }
         }
-        cu.turn = (cu.turn + sp.t1 - sp.t0) % NW;
+        w.w = nullptr;
+        w.tile_bytes = 0;
+        w.t1 = 0;
+        t = 0;
+        p = 0;
+        passes = 1;
     }
-    cu.w.w = nullptr;  // an empty descriptor: every load is out of range
-    cu.w.tile_bytes = 0;
-    cu.w.t1 = 0;
-    cu.passes = 1;
-    cu.t0 = 0;
-    cu.c = PassPos{0, 0};
-    cu.s = nspan;
-}
 
-// Next pass; true when the cursor moved to another span.
-template <int NW>
-__device__ __forceinline__ bool advance(Cursor &cu, int nspan, int wave, cptr<SweepWork> wk,
-                                        cptr<SweepProj> projs) {
-    if (++cu.c.p < cu.passes)
-        return false;
-    cu.c.p = 0;
-    cu.c.t += NW;
-    if (cu.c.t < cu.w.t1 || cu.s >= nspan)
-        return false;
-    cu.turn = (cu.turn + cu.w.t1 - cu.t0) % NW;
-    enter<NW>(cu, cu.s + 1, nspan, wave, wk, projs);
-    return true;
-}
+    __device__ __forceinline__ void advance(int nspan, cptr<SweepWork> wk, cptr<SweepProj> projs,
+                                            int *ctr, int lane) {
+        if (s >= nspan)
+            return;
+        if (++p < passes)
+            return;
+        p = 0;
+        t = fetch_tile(ctr, s, lane);
+        if (t < w.t1)
+            return;
+        begin(s + 1, nspan, wk, projs, ctr, lane);
+    }
+};
 
 // Built for SW resident waves per SIMD (512 / SW registers per lane) with a
 // register ring of kS passes.
@@ -289,23 +288,27 @@ void sweep_kernel(const SweepHeader *header_g, const SweepProj *projs_g,
     const cptr<SweepWork> wk = (cptr<SweepWork>)work_g + blockIdx.x;
     const int nspan = wk->nspan;
 
-    // The issue cursor f runs kS - 1 passes ahead of the compute cursor c,
-    // from span to span, so the ring never drains at a span boundary.  Its
-    // first kS - 1 passes go out before the staging at M <= 2 (after the
-    // first span's activation loads), so the first weights arrive while the
-    // activations are quantized; at larger M the staging holds too many
-    // registers for the ring to be live across it.
+    // The issue side f runs kS - 1 passes ahead of the compute side, from
+    // span to span, so the ring never drains at a span boundary; each ring
+    // slot carries the span, tile and pass it holds.  The first kS - 1
+    // passes go out before the staging at M <= 2 (after the first span's
+    // activation loads), so the first weights arrive while the activations
+    // are quantized; at larger M the staging holds too many registers for the
+    // ring to be live across it.  The counters hold each span's next tile.
     constexpr bool kEarly = M <= 2;
-    Cursor f;
-    f.turn = 0;
-    enter<NW>(f, 0, nspan, wave, wk, projs);
-    const Cursor c0s = f;
+    int *ctr = reinterpret_cast<int *>(st_scale + kSweepMaxSpans * 16);
+    DynCursor f;
     uint4 ring[kS][kSweepLP];
+    int tag_s[kS], tag_t[kS], tag_p[kS];
     auto prologue = [&]() {
+        f.begin(0, nspan, wk, projs, ctr, lane);
 #pragma unroll
         for (int k = 0; k < kS - 1; ++k) {
-            issue(f.w, f.c, lane, ring[k]);
-            advance<NW>(f, nspan, wave, wk, projs);
+            issue(f.w, PassPos{f.t, f.p}, lane, ring[k]);
+            tag_s[k] = f.s;
+            tag_t[k] = f.t;
+            tag_p[k] = f.p;
+            f.advance(nspan, wk, projs, ctr, lane);
         }
     };
 
@@ -323,6 +326,14 @@ void sweep_kernel(const SweepHeader *header_g, const SweepProj *projs_g,
     const int cl = 64 * (wave % kWpr) + lane;  // its first chunk of the row
     if (tid < 16 + 2 * kSweepMaxSpans * 16)
         reinterpret_cast<uint32_t *>(smem)[tid] = 0u;
+    if (tid < kSweepMaxSpans) {
+        int t0 = 0;
+#pragma unroll
+        for (int k = 0; k < kSweepMaxSpans; ++k)
+            if (k == tid && k < nspan)
+                t0 = wk->span[k].t0;
+        ctr[tid] = t0;
+    }
     __syncthreads();
     auto stage = [&](int s, auto early) {
         const SweepSpan sp = span_at(wk, s);
@@ -409,34 +420,21 @@ void sweep_kernel(const SweepHeader *header_g, const SweepProj *projs_g,
     for (int s = 1; s < nspan; ++s)
         stage(s, std::false_type{});
     __syncthreads();  // staged rows, row sums and scales
-    if constexpr (!kEarly)
-        prologue();
 
-    // 2. stream: compute the pass in one ring slot while the next kS - 1
-    //    passes' loads are in flight, the loads running ahead across spans.
-    //    Passes of this wave: sum over spans of its tiles times the passes
-    //    per tile.
-    int left = 0;
-    {
-        int turn = 0;
-        for (int s = 0; s < nspan; ++s) {
-            const SweepSpan sp = span_at(wk, s);
-            const int first = (wave - turn + NW) % NW;
-            turn = (turn + sp.t1 - sp.t0) % NW;
-            if (sp.t0 + first < sp.t1)
-                left += (sp.t1 - sp.t0 - first + NW - 1) / NW * projs[sp.q].passes;
-        }
-    }
-    Cursor c = c0s;
+    // 2. stream: the waves of the workgroup take the tiles of each span from
+    //    its LDS counter, one tile at a time, span after span, so they all run
+    //    out of work within about a tile of each other.  Each ring slot
+    //    carries the span, tile and pass it holds; the compute side reads
+    //    them back.  The loads run kS - 1 passes ahead, across spans.
+    int cs = 0;  // span whose outputs the compute side holds
     SpanOut so;
-    const uint8_t *bsrc;
-    int ustep, slices;
-    // the compute side of the span c is in
-    auto load_span = [&]() {
-        const int s = c.s < nspan ? c.s : 0;
+    const uint8_t *bsrc = zero;
+    int ustep = 0, slices = 1, cpasses = 1;
+    auto load_span = [&](int s) {
         const SweepSpan sp = span_at(wk, s);
         const cptr<SweepProj> P = projs + sp.q;
         slices = P->slices;
+        cpasses = P->passes;
         so.acc = P->acc;
         so.y = P->y;
         so.segs = segs_of(P);
@@ -449,31 +447,39 @@ void sweep_kernel(const SweepHeader *header_g, const SweepProj *projs_g,
         bsrc = r < M ? xbase + sp.xoff + r * P->stride + 64 * g : zero;
         ustep = r < M ? 256 : 0;
     };
-    load_span();
+    load_span(0);  // (with no span: the table's zeroed entry, never used)
     v4i c0 = {0, 0, 0, 0}, c3 = c0, c4 = c0, c16 = c0;
-    // one step: issue the pass kS - 1 ahead into the slot freed by the last
-    // step, then compute the pass in slot CUR
+#define TWD_SWEEP_ISSUE(SLOT)                                                  \
+    issue(f.w, PassPos{f.t, f.p}, lane, ring[SLOT]);                           \
+    tag_s[SLOT] = f.s;                                                         \
+    tag_t[SLOT] = f.t;                                                         \
+    tag_p[SLOT] = f.p;                                                         \
+    f.advance(nspan, wk, projs, ctr, lane);
 #define TWD_SWEEP_STEP(CUR)                                                    \
-    issue(f.w, f.c, lane, ring[((CUR) + kS - 1) % kS]);                        \
-    advance<NW>(f, nspan, wave, wk, projs);                                    \
-    compute(c.c.p, slices, bsrc, ustep, zero, ring[CUR], c0, c3, c4, c16);     \
-    if (c.c.p == c.passes - 1)                                                 \
-        epilogue<M>(so, c.c.t, r, g, c0, c3, c4, c16);                         \
-    if (advance<NW>(c, nspan, wave, wk, projs))                                \
-        load_span();
-    for (; left >= kS; left -= kS) {
+    TWD_SWEEP_ISSUE(((CUR) + kS - 1) % kS)                                     \
+    if (tag_s[CUR] != cs && tag_s[CUR] < nspan) {                              \
+        cs = tag_s[CUR];                                                       \
+        load_span(cs);                                                         \
+    }                                                                          \
+    compute(tag_p[CUR], slices, bsrc, ustep, zero, ring[CUR], c0, c3, c4, c16); \
+    if (tag_s[CUR] < nspan && tag_p[CUR] == cpasses - 1)                       \
+        epilogue<M>(so, tag_t[CUR], r, g, c0, c3, c4, c16);
+    if constexpr (!kEarly)
+        prologue();
+    for (;;) {
 #pragma unroll
         for (int k = 0; k < kS; ++k) {
             TWD_SWEEP_STEP(k)
         }
-    }
+        bool pending = f.s < nspan;
 #pragma unroll
-    for (int k = 0; k < kS - 1; ++k) {
-        if (left > k) {
-            TWD_SWEEP_STEP(k)
-        }
+        for (int k = 0; k < kS - 1; ++k)
+            pending = pending || tag_s[k] < nspan;
+        if (!pending)
+            break;
     }
 #undef TWD_SWEEP_STEP
+#undef TWD_SWEEP_ISSUE
 }
 
 using Fn = void (*)(const SweepHeader *, const SweepProj *, const SweepWork *, uint32_t);

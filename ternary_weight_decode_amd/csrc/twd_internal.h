@@ -107,20 +107,20 @@ constexpr int kSweepMaxSpans = 4;      // projections one workgroup stages
 constexpr int kSweepLP = 4;            // 256-wide K slices per pass
 // Per width: waves per workgroup, resident waves per SIMD the kernel is
 // built for (its register budget: 512 / that many registers per lane), and
-// the passes of its register ring (one computed, the rest in flight).  A
-// workgroup's waves share its staged activations (M x K bytes per
-// projection in LDS), so wider calls take bigger workgroups; the planner
-// aims for 4 x sweep_simd_waves(M) resident waves on each of kSweepCUs
+// the passes of its register ring (one computed, the rest in flight).  One
+// workgroup fills a compute unit (16 waves, four per SIMD), so all the
+// compute unit's waves share one tile counter; the planner aims for
+// 4 x sweep_simd_waves(M) / sweep_waves(M) workgroups on each of kSweepCUs
 // compute units.
 constexpr int kSweepCUs = 256;
-constexpr int sweep_waves(int M) { return M <= 4 ? 4 : M <= 8 ? 8 : 16; }
-constexpr int sweep_simd_waves(int M) { return M <= 4 ? 4 : 4; }
-constexpr int sweep_ring(int M) { return M <= 4 ? 3 : 3; }
+constexpr int sweep_waves(int) { return 16; }
+constexpr int sweep_simd_waves(int) { return 4; }
+constexpr int sweep_ring(int) { return 3; }
 constexpr int kSweepHeaderBytes = 64;  // table header
 constexpr uint32_t kSweepMagic = 0x53445754u;  // "TWDS"
 // LDS: zero block (64 B), then per-span absmax, row-sum and scale words
-// (kSweepMaxSpans x 16 each), the workgroup's tile counter (16 B), then the
-// staged activation rows.
+// (kSweepMaxSpans x 16 each), the next-tile counter of each span (16 B),
+// then the staged activation rows.
 constexpr int kSweepLdsHeader = 64 + 3 * kSweepMaxSpans * 16 * 4 + 16;
 
 struct SweepProj {       // 96 bytes
