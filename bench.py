@@ -211,19 +211,21 @@ def time_eager(torch, fn, reps):
 def stream_read_reference(twd, torch, dev_set, reps):
     """The plain streaming-read kernel (every compute unit busy, eight loads
     in flight per lane): once over one contiguous buffer of the step's bytes
-    (the sweep's reference: one launch), and over each projection's weight
-    buffer in turn (the per-projection launches' reference).  Returns
+    (the sweep's reference: one launch, timed as direct launches like the
+    sweep), and over each projection's weight buffer in turn (the
+    per-projection launches' reference, graph-replayed like them).  Returns
     ({gbs, us}, {gbs, avg_launch_us})."""
     sink = torch.zeros(256, dtype=torch.int32, device="cuda")
     keys = [(l, p) for l in range(dev_set.layers) for p in range(len(dev_set.ls.projs))]
     nbytes = dev_set.bytes_per_sweep
     big = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     big.fill_(1)
-    g = capture(torch, lambda: twd.stream_read(big, nbytes, sink))
-    g.replay()
-    _, sec = time_replays(torch, g, reps)
+    # direct launches, as the sweep step is timed
+    for _ in range(5):
+        twd.stream_read(big, nbytes, sink)
+    _, sec = time_launches(torch, lambda: twd.stream_read(big, nbytes, sink), reps)
     one = {"gbs": round(nbytes * reps / sec / 1e9, 1), "us": round(sec / reps * 1e6, 2)}
-    del g, big
+    del big
 
     def sweep():
         for k in keys:

@@ -115,7 +115,7 @@ constexpr int kSweepLP = 4;            // 256-wide K slices per pass
 constexpr int kSweepCUs = 256;
 constexpr int sweep_waves(int) { return 16; }
 constexpr int sweep_simd_waves(int) { return 4; }
-constexpr int sweep_ring(int) { return 3; }
+constexpr int sweep_ring(int) { return 2; }
 constexpr int kSweepHeaderBytes = 64;  // table header
 constexpr uint32_t kSweepMagic = 0x53445754u;  // "TWDS"
 // LDS: zero block (64 B), then per-span absmax, row-sum and scale words
