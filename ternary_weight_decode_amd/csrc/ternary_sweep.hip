@@ -291,11 +291,12 @@ void sweep_kernel(const SweepHeader *header_g, const SweepProj *projs_g,
     // The issue side f runs kS - 1 passes ahead of the compute side, from
     // span to span, so the ring never drains at a span boundary; each ring
     // slot carries the span, tile and pass it holds.  The first kS - 1
-    // passes go out before the staging at M <= 2 (after the first span's
+    // passes go out before the staging at M <= 8 (after the first span's
     // activation loads), so the first weights arrive while the activations
-    // are quantized; at larger M the staging holds too many registers for the
-    // ring to be live across it.  The counters hold each span's next tile.
-    constexpr bool kEarly = M <= 2;
+    // are quantized; at larger M the staging holds too many registers (a
+    // wave per token row, 16 rounds of loads) for the ring to be live across
+    // it.  The counters hold each span's next tile.
+    constexpr bool kEarly = M <= 8;
     int *ctr = reinterpret_cast<int *>(st_scale + kSweepMaxSpans * 16);
     DynCursor f;
     uint4 ring[kS][kSweepLP];
