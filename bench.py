@@ -297,6 +297,13 @@ def width_entry(twd, torch, dev_set, workload, M, kernel, reps, outliers=False,
         out["two_launch"] = {"gbs": round(nbytes / sec / 1e9, 1),
                              "kernels": kernel_map(twd, dev_set.ls, M, kernel, False)}
         del g
+    if "per_launch" in out and "two_launch" in out:
+        # the faster per-projection form at this width (the one-launch entry
+        # point cannot pick the two-launch form: it would need a workspace
+        # for the quantized rows)
+        best = max(("one_launch", out["per_launch"]["gbs"]), ("two_launch", out["two_launch"]["gbs"]),
+                   key=lambda kv: kv[1])
+        out["per_projection_best"] = {"form": best[0], "gbs": best[1]}
     del st
     torch.cuda.empty_cache()
     return out
@@ -911,13 +918,15 @@ def summarize_profiles(args):
                              f"gap in back-to-back replay")
             else:
                 lines.append(f"- the unprofiled default run: **{bench_live:.3f} us** per launch, "
-                             f"{-gap:.3f} us below the kernels' own duration under kernel tracing: "
-                             f"back to back, each launch finds the code, kernel arguments and "
-                             f"activations that the previous launches left in the caches (the "
-                             f"weight loads are non-temporal to keep them there), and the traced "
-                             f"dispatches do not show that gain; it is the profiler's handling of "
-                             f"each dispatch rather than the spacing, since spacing unprofiled "
-                             f"launches apart with idle kernels costs only about 0.1 us per launch")
+                             f"{-gap:.3f} us below the kernels' own duration under kernel tracing, "
+                             f"so this trace does not back the live per-launch figure: traced "
+                             f"dispatches run slower than the same launches back to back (a likely "
+                             f"cause, not measured: each back-to-back launch finds the code, "
+                             f"kernel arguments and activations the previous ones left in the "
+                             f"caches; spacing unprofiled launches apart with idle kernels costs "
+                             f"only about 0.1 us per launch). The live figure is backed instead by "
+                             f"the HBM counters (traffic per launch, in the counter summary) and "
+                             f"by the one-launch sweep, whose trace agrees with its live figure")
         lines.append("")
     trace_path = os.path.join(out_dir, f"ternary_linear_{tag}_kernel_trace.md")
     with open(trace_path, "w") as f:
