@@ -5,10 +5,11 @@ Bar, as for the one-launch linear: int32 accumulators bit-exact, fp32 outputs
 within 1e-6 relative of the oracle's double-precision value.  Cases: random
 projection lists at every width M = 1..16 (ragged K and N, 1..4 segments,
 empty projections, K = 64 and K = 8192), one full-size 2B-class layer at
-every width on the outlier workload, the whole 30-layer 2B set at M = 1 in
-the benchmark's launch (sampled rows against the oracle, every row against
-the per-projection launches), graph replays checked against the oracle, and
-a table that does not match its plan (nothing written).
+every width on the outlier workload, whole layer sets in the benchmark's
+launch (the 2B set at M = 1, 2, 4, 8 and on the outlier workload at M = 16,
+the 4B stack at M = 1, 4, 16; sampled rows against the oracle, every row
+against the per-projection launches), graph replays checked against the
+oracle, and a table that does not match its plan (nothing written).
 """
 import sys
 
@@ -172,47 +173,98 @@ def test_sweep_full_size_layer_every_width(env, M):
         c.check(orc, orc.forward(c.W, c.segs, c.x, threads=threads))
 
 
-def test_sweep_whole_2b_set_m1(env):
-    """The benchmark's M = 1 launch: all 120 projections of the 30-layer 2B
-    set in one sweep.  Every output equals the per-projection launch; sampled
-    rows of every projection equal the oracle (ternarized over the whole
-    segment, contracted on the sampled rows)."""
+SAMPLED_ROWS = 24
+
+
+def _threads():
+    import os
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+@pytest.fixture(scope="module")
+def whole_sets(env):
+    """Each layer set once: tiled and row-major packed weights on the device,
+    and for a fixed sample of rows per projection the oracle's ternary codes
+    and per-row gamma (ternarized over the whole segment)."""
+    from concurrent.futures import ThreadPoolExecutor
     torch, twd, orc = env
-    ls = wl.SET_2B
-    M = 1
-    rng = np.random.default_rng(123)
-    entries, refs, rowmajor = [], [], []
-    for layer in range(ls.layers):
-        for pi, proj in enumerate(ls.projs):
+    cache = {}
+
+    def get(name):
+        if name in cache:
+            return cache[name]
+        ls = wl.LAYER_SETS[name]
+        keys = [(layer, pi) for layer in range(ls.layers) for pi in range(len(ls.projs))]
+
+        def prep(key):
+            layer, pi = key
+            proj = ls.projs[pi]
             W = wl.layer_weights(ls, layer, pi)
-            x = wl.layer_activations("2b_decode", proj.K, M, layer, pi)
             packed, gammas = twd.prepare_weights(W, proj.segs)
-            # the oracle on sampled rows (gamma over the whole segment)
             t, gam, grow = orc.ternarize_segments(W, proj.segs)
             assert gam == list(gammas)
-            rows = np.sort(rng.choice(proj.N, 24, replace=False))
-            q, s = orc.quantize_act(x)
-            ra = orc.linear(q, t[rows])
-            refs.append((layer, pi, rows, ra, orc.dequant(ra, s, grow[rows])))
-            del W, t
-            entries.append((torch.from_numpy(twd.tile_for_sweep(packed, proj.N, proj.K)).cuda(),
-                            proj.segs, gammas, dev_bf16(torch, x),
-                            torch.full((M, proj.N), -7, dtype=torch.int32, device="cuda"),
-                            torch.full((M, proj.N), -7.0, device="cuda")))
-            rowmajor.append(torch.from_numpy(packed).cuda())
-    log("sweep whole 2B set M=1: planned")
+            rows = np.sort(np.random.default_rng([123, layer, pi]).choice(
+                proj.N, SAMPLED_ROWS, replace=False))
+            tiled = twd.tile_for_sweep(packed, proj.N, proj.K)
+            return key, packed, tiled, gammas, t[rows].copy(), grow[rows].copy(), rows
+
+        out = {}
+        with ThreadPoolExecutor(max_workers=_threads()) as ex:
+            for key, packed, tiled, gammas, trows, grows, rows in ex.map(prep, keys):
+                out[key] = (torch.from_numpy(tiled).cuda(), torch.from_numpy(packed).cuda(),
+                            gammas, trows, grows, rows)
+        torch.cuda.synchronize()
+        cache.clear()  # hold one set on the device at a time
+        cache[name] = (ls, keys, out)
+        log(f"whole-set fixture {name}: {len(keys)} projections prepared")
+        return cache[name]
+
+    return get
+
+
+WHOLE_SET_CASES = [("2b", "2b_decode", 1), ("2b", "2b_verify", 2), ("2b", "2b_verify", 4),
+                   ("2b", "2b_verify", 8), ("2b", "2b_sweep_outlier", 16),
+                   ("4b", "4b_stack", 1), ("4b", "4b_stack", 4), ("4b", "4b_stack", 16)]
+
+
+@pytest.mark.parametrize("set_name,workload,M", WHOLE_SET_CASES)
+def test_sweep_whole_layer_set(env, whole_sets, set_name, workload, M):
+    """The benchmark's launch at full size: every projection of a layer set
+    (the 30-layer 2B set, the 36-layer 4B stack) in one sweep at width M.
+    Every output equals the per-projection launch; sampled rows of every
+    projection equal the oracle."""
+    torch, twd, orc = env
+    ls, keys, dev = whole_sets(set_name)
+    log(f"sweep whole set {set_name} {workload} M={M}")
+    outliers = workload == "2b_sweep_outlier"
+    entries, checks = [], []
+    for key in keys:
+        layer, pi = key
+        proj = ls.projs[pi]
+        wt, wp, gammas, trows, grows, rows = dev[key]
+        x = wl.layer_activations(workload, proj.K, M, layer, pi, outliers=outliers)
+        q, s = orc.quantize_act(x)
+        ra = orc.linear(q, trows)
+        xd = dev_bf16(torch, x)
+        entries.append((wt, proj.segs, gammas, xd,
+                        torch.full((M, proj.N), -7, dtype=torch.int32, device="cuda"),
+                        torch.full((M, proj.N), -7.0, device="cuda")))
+        checks.append((key, wp, rows, ra, orc.dequant(ra, s, grows)))
     sw = twd.Sweep(entries)
     assert sw.weight_bytes == ls.packed_bytes
     sw.run()
     torch.cuda.synchronize()
-    for (wt, segs, gammas, xd, acc, y), wp, (layer, pi, rows, ra, ry) in zip(entries, rowmajor,
-                                                                            refs):
+    for (wt, segs, gammas, xd, acc, y), (key, wp, rows, ra, ry) in zip(entries, checks):
         a2, y2 = twd.ternary_linear_bf16(wp, segs, gammas, xd)
         torch.cuda.synchronize()
-        assert torch.equal(acc, a2), (layer, pi)
-        assert torch.equal(y, y2), (layer, pi)
+        assert torch.equal(acc, a2), key
+        assert torch.equal(y, y2), key
         np.testing.assert_array_equal(acc.cpu().numpy()[:, rows], ra)
-        check_y(y.cpu().numpy()[:, rows], ry, f"{layer},{pi}")
+        check_y(y.cpu().numpy()[:, rows], ry, f"{key}")
 
 
 def test_sweep_graph_replays_match_oracle(env):
