@@ -28,6 +28,34 @@ int stride_bytes(int K) { return ((K + 255) / 256) * 256 + 16; }
 constexpr int64_t kMinTilesPerWave = 2;
 constexpr int kLdsHardCap = 160 * 1024;
 
+// Outputs gathered in LDS and written after the stream.  A workgroup's tiles
+// of one projection are consecutive, so for each token row its outputs form
+// one run of 16 (t1 - t0) values: written at the end, each run goes out as
+// whole lines in one pass, instead of 64-byte pieces of 16 token rows
+// interleaved with the weight stream.  A workgroup defers when its staged
+// activations and the outputs of all its spans fit in LDS together.
+// Deferring only some spans was slower than deferring none: the workgroup
+// then pays both for the stores in the stream and for the write-out at the
+// end.
+int lay_out_deferred(SweepWork &w, const std::vector<SweepProj> &P, int m, int staged_end) {
+    int off = (staged_end + 15) & ~15;
+    for (int s = 0; s < w.nspan; ++s) {
+        SweepSpan &sp = w.span[s];
+        const SweepProj &d = P[sp.q];
+        const int bytes = 4 * m * 16 * (sp.t1 - sp.t0);
+        sp.yoff = d.y ? off : -1;
+        off += d.y ? bytes : 0;
+        sp.aoff = d.acc ? off : -1;
+        off += d.acc ? bytes : 0;
+    }
+    w.defer = off <= kLdsHardCap ? 1 : 0;
+    if (w.defer)
+        return off;
+    for (int s = 0; s < w.nspan; ++s)
+        w.span[s].yoff = w.span[s].aoff = -1;
+    return staged_end;
+}
+
 uint32_t fnv1a(const uint8_t *p, size_t n) {
     uint32_t h = 2166136261u;
     for (size_t i = 0; i < n; ++i) {
@@ -133,9 +161,10 @@ twd_status sweep_plan(const twd_sweep_proj *projs, int nproj, int64_t M, const v
     int64_t cum = 0;
     auto close = [&]() {
         if (cur.nspan > 0) {
+            const int end = lay_out_deferred(cur, P, m, cur_lds);
             work.push_back(cur);
-            if (cur_lds > lds_max)
-                lds_max = cur_lds;
+            if (end > lds_max)
+                lds_max = end;
         }
         std::memset(&cur, 0, sizeof cur);
         cur_lds = kSweepLdsHeader;

@@ -37,6 +37,12 @@
 // activation block (token columns at or past M read a zero block).  After a
 // tile's last pass, lane (token r, group g) holds rows 4g..4g+3 for token r:
 // sum q t = sum q c - sum q, then the dequant epilogue.
+//
+// Outputs.  Stores issued inside the weight stream, 64 bytes for each of up
+// to 16 token rows per tile, slow the stream far more than their bytes
+// would suggest.  Where the workgroup's outputs fit in LDS beside its staged
+// activations (the planner decides), the epilogue writes them to LDS and the
+// workgroup writes each token row's run of consecutive outputs at the end.
 #include <type_traits>
 
 #include "kernel_common.h"
@@ -62,6 +68,8 @@ __device__ __forceinline__ SweepSpan span_at(cptr<SweepWork> wk, int s) {
     sp.t0 = wk->span[s].t0;
     sp.t1 = wk->span[s].t1;
     sp.xoff = wk->span[s].xoff;
+    sp.yoff = wk->span[s].yoff;
+    sp.aoff = wk->span[s].aoff;
     return sp;
 }
 
@@ -168,13 +176,18 @@ struct SpanOut {
     int qs;     // row sum of q for token r
     float sc;   // scale of token r
     bool vec;   // 16-byte stores: N % 4 == 0 and both outputs 16-byte aligned
+    bool def;   // outputs gathered in LDS (ydef / adef: [M][rows], null if absent)
+    uint8_t *ydef;
+    uint8_t *adef;
+    int t0, rows;  // the span's first tile and 16 x its tile count
 };
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 // After a tile's last pass: lane (token r, group g) holds rows 4g .. 4g+3,
 // four consecutive outputs of token r, written with one 16-byte store each
-// for acc and y where the row layout allows it.
+// for acc and y where the row layout allows it -- into the span's LDS rows
+// when the workgroup defers its outputs (rows past N are never written out).
 template <int M>
 __device__ __forceinline__ void epilogue(const SpanOut &so, int t, int r, int g, const v4i &c0,
                                          const v4i &c3, const v4i &c4, const v4i &c16) {
@@ -187,7 +200,13 @@ __device__ __forceinline__ void epilogue(const SpanOut &so, int t, int r, int g,
         tot[i] = cc[i] - so.qs;
         yv[i] = static_cast<float>(tot[i]) * so.sc * row_gamma(so.segs, n0 + i);
     }
-    if (r < M && n0 < so.N) {
+    if (r < M && n0 < so.N && so.def) {
+        const int e = 4 * (r * so.rows + 16 * (t - so.t0) + 4 * g);
+        if (so.adef)
+            *reinterpret_cast<v4i *>(so.adef + e) = tot;
+        if (so.ydef)
+            *reinterpret_cast<v4f *>(so.ydef + e) = yv;
+    } else if (r < M && n0 < so.N) {
         const int64_t o = static_cast<int64_t>(r) * so.N + n0;
         if (so.vec) {
             // N % 4 == 0, so n0 < N means all four rows are in range
@@ -204,6 +223,47 @@ __device__ __forceinline__ void epilogue(const SpanOut &so, int t, int r, int g,
                     if (so.y)
                         so.y[o + i] = yv[i];
                 }
+        }
+    }
+}
+
+// Write a deferred span's LDS rows ([M][rows], rows = 16 (t1 - t0), from
+// output row 16 t0) to acc and y: 16-byte stores where N % 4 == 0 and both
+// outputs are 16-byte aligned, else 4-byte stores; rows at or past N stay in
+// LDS.
+template <int M>
+__device__ __forceinline__ void write_deferred(const uint8_t *smem, const SweepSpan &sp,
+                                               cptr<SweepProj> P, int tid, int nthreads) {
+    if (sp.yoff < 0 && sp.aoff < 0)
+        return;
+    const int N = P->N;
+    const int rows = 16 * (sp.t1 - sp.t0);
+    const int n0 = 16 * sp.t0;
+    const int valid = N - n0 < rows ? N - n0 : rows;
+    int32_t *acc = P->acc;
+    float *y = P->y;
+    const bool vec = (N & 3) == 0 &&
+                     ((reinterpret_cast<uintptr_t>(acc) | reinterpret_cast<uintptr_t>(y)) & 15) ==
+                         0;
+    for (int r = 0; r < M; ++r) {
+        const int64_t o = static_cast<int64_t>(r) * N + n0;
+        const int e = 4 * r * rows;
+        if (vec) {
+            for (int j = 4 * tid; j < valid; j += 4 * nthreads) {
+                if (sp.aoff >= 0)
+                    *reinterpret_cast<v4i *>(acc + o + j) =
+                        *reinterpret_cast<const v4i *>(smem + sp.aoff + e + 4 * j);
+                if (sp.yoff >= 0)
+                    *reinterpret_cast<v4f *>(y + o + j) =
+                        *reinterpret_cast<const v4f *>(smem + sp.yoff + e + 4 * j);
+            }
+        } else {
+            for (int j = tid; j < valid; j += nthreads) {
+                if (sp.aoff >= 0)
+                    acc[o + j] = *reinterpret_cast<const int32_t *>(smem + sp.aoff + e + 4 * j);
+                if (sp.yoff >= 0)
+                    y[o + j] = *reinterpret_cast<const float *>(smem + sp.yoff + e + 4 * j);
+            }
         }
     }
 }
@@ -447,6 +507,11 @@ void sweep_kernel(const SweepHeader *header_g, const SweepProj *projs_g,
                   15) == 0;
         bsrc = r < M ? xbase + sp.xoff + r * P->stride + 64 * g : zero;
         ustep = r < M ? 256 : 0;
+        so.def = sp.yoff >= 0 || sp.aoff >= 0;
+        so.ydef = sp.yoff >= 0 ? smem + sp.yoff : nullptr;
+        so.adef = sp.aoff >= 0 ? smem + sp.aoff : nullptr;
+        so.t0 = sp.t0;
+        so.rows = 16 * (sp.t1 - sp.t0);
     };
     load_span(0);  // (with no span: the table's zeroed entry, never used)
     v4i c0 = {0, 0, 0, 0}, c3 = c0, c4 = c0, c16 = c0;
@@ -481,6 +546,14 @@ void sweep_kernel(const SweepHeader *header_g, const SweepProj *projs_g,
     }
 #undef TWD_SWEEP_STEP
 #undef TWD_SWEEP_ISSUE
+
+    // 3. deferred outputs: once every wave is done, each token row's run of
+    //    each span goes out in one pass over consecutive addresses.
+    if (wk->defer) {
+        __syncthreads();
+        for (int s = 0; s < nspan; ++s)
+            write_deferred<M>(smem, span_at(wk, s), projs + wk->span[s].q, tid, 64 * NW);
+    }
 }
 
 using Fn = void (*)(const SweepHeader *, const SweepProj *, const SweepWork *, uint32_t);

@@ -120,7 +120,8 @@ constexpr int kSweepHeaderBytes = 64;  // table header
 constexpr uint32_t kSweepMagic = 0x53445754u;  // "TWDS"
 // LDS: zero block (64 B), then per-span absmax, row-sum and scale words
 // (kSweepMaxSpans x 16 each), the next-tile counter of each span (16 B),
-// then the staged activation rows.
+// then the staged activation rows, then (where they fit) the deferred
+// outputs: per span, [M][16 (t1 - t0)] values of y and of acc.
 constexpr int kSweepLdsHeader = 64 + 3 * kSweepMaxSpans * 16 * 4 + 16;
 
 struct SweepProj {       // 96 bytes
@@ -140,14 +141,17 @@ static_assert(sizeof(SweepProj) == 96, "SweepProj layout");
 
 struct SweepSpan {       // tiles [t0, t1) of projection q, activations at xoff
     int q, t0, t1, xoff;
+    int yoff, aoff;      // LDS byte offsets of the deferred y / acc rows, or -1
+    int pad[2];
 };
 
-struct SweepWork {       // 80 bytes: one workgroup's spans, in order
+struct SweepWork {       // 144 bytes: one workgroup's spans, in order
     int nspan;
-    int pad[3];
+    int defer;           // 1: the spans' outputs are gathered in LDS, written at the end
+    int pad[2];
     SweepSpan span[kSweepMaxSpans];
 };
-static_assert(sizeof(SweepWork) == 80, "SweepWork layout");
+static_assert(sizeof(SweepWork) == 144, "SweepWork layout");
 
 struct SweepHeader {     // 64 bytes
     uint32_t magic, check;

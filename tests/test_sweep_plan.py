@@ -1,8 +1,9 @@
 """Host logic of the multi-projection sweep (no GPU): the planner's table
 image, decoded field by field, must cover every 16-row tile of every
 projection exactly once, in order, with at most four projections per
-workgroup, consistent LDS offsets and a check value bound to the table's
-device address; bad arguments must be rejected before anything is written.
+workgroup, consistent LDS offsets (staged activations, then the deferred
+outputs where they fit) and a check value bound to the table's device
+address; bad arguments must be rejected before anything is written.
 """
 import ctypes
 
@@ -17,31 +18,33 @@ HEADER = np.dtype([("magic", "<u4"), ("check", "<u4"), ("nproj", "<i4"), ("nwg",
 PROJ = np.dtype([("w", "<u8"), ("x", "<u8"), ("acc", "<u8"), ("y", "<u8"), ("K", "<i4"),
                  ("N", "<i4"), ("passes", "<i4"), ("slices", "<i4"), ("stride", "<i4"),
                  ("nseg", "<i4"), ("bound", "<i4", 4), ("gamma", "<f4", 4), ("pad", "<i4", 2)])
-WORK = np.dtype([("nspan", "<i4"), ("pad", "<i4", 3), ("span", "<i4", (4, 4))])
+WORK = np.dtype([("nspan", "<i4"), ("defer", "<i4"), ("pad", "<i4", 2),
+                 ("span", "<i4", (4, 8))])  # q, t0, t1, xoff, yoff, aoff, pad, pad
 LDS_HEADER = 64 + 3 * 4 * 16 * 4 + 16
 MAX_SPANS = 4
 
 
-def fake_list(shapes, base=1 << 32):
+def fake_list(shapes, base=1 << 32, outputs=lambda i: (True, True)):
     """(K, seg_rows) list -> descriptors with distinct aligned fake pointers
-    (the planner never dereferences them)."""
+    (the planner never dereferences them); outputs(i) -> (acc?, y?)."""
     rows = []
     for i, (K, segs) in enumerate(shapes):
         p = base + (i << 24)
-        rows.append((p, p + (1 << 20), p + (2 << 20), p + (3 << 20), K, segs,
-                     [0.5 + i] * len(segs)))
+        a, y = outputs(i)
+        rows.append((p, p + (1 << 20), p + (2 << 20) if a else None, p + (3 << 20) if y else None,
+                     K, segs, [0.5 + i] * len(segs)))
     return rows
 
 
 def decode(img):
     h = np.frombuffer(img[:64].tobytes(), HEADER)[0]
     projs = np.frombuffer(img[h["proj_off"]:h["proj_off"] + 96 * h["nproj"]].tobytes(), PROJ)
-    work = np.frombuffer(img[h["work_off"]:h["work_off"] + 80 * h["nwg"]].tobytes(), WORK)
+    work = np.frombuffer(img[h["work_off"]:h["work_off"] + 144 * h["nwg"]].tobytes(), WORK)
     return h, projs, work
 
 
-def plan(shapes, M, table_dev=0x7F0000000000):
-    descs = twd.sweep_descs(fake_list(shapes), M)
+def plan(shapes, M, table_dev=0x7F0000000000, outputs=lambda i: (True, True)):
+    descs = twd.sweep_descs(fake_list(shapes, outputs=outputs), M)
     img, p = twd.sweep_encode(descs, M, table_dev)
     return img, p
 
@@ -58,11 +61,16 @@ SHAPE_LISTS = [
 ]
 
 
+OUTPUTS = {"both": lambda i: (True, True), "y": lambda i: (False, True),
+           "mixed": lambda i: (i % 3 != 1, i % 3 != 2)}
+
+
+@pytest.mark.parametrize("outs", sorted(OUTPUTS))
 @pytest.mark.parametrize("M", [1, 4, 16])
 @pytest.mark.parametrize("li", range(len(SHAPE_LISTS)))
-def test_plan_covers_every_tile_once(li, M):
+def test_plan_covers_every_tile_once(li, M, outs):
     shapes = SHAPE_LISTS[li]
-    img, p = plan(shapes, M)
+    img, p = plan(shapes, M, outputs=OUTPUTS[outs])
     h, projs, work = decode(img)
     assert h["magic"] == 0x53445754 and h["nproj"] == len(shapes) and h["M"] == M
     assert p.nwg == h["nwg"] == len(work) and p.lds_bytes == h["lds"]
@@ -81,12 +89,32 @@ def test_plan_covers_every_tile_once(li, M):
         assert 1 <= n <= MAX_SPANS or (n == 0 and total == 0)
         lds = LDS_HEADER
         for s in range(n):
-            q, t0, t1, xoff = (int(v) for v in w["span"][s])
+            q, t0, t1, xoff = (int(v) for v in w["span"][s][:4])
             assert xoff == lds - LDS_HEADER
             lds += M * stride(shapes[q][0])
             assert t0 < t1
             seen.extend((q, t) for t in range(t0, t1))
         assert lds <= h["lds"] <= 160 * 1024
+        # deferred outputs: per span, y then acc rows [M][16 (t1 - t0)] fp32 /
+        # int32, from the first 16-byte boundary past the staged rows, when
+        # the rows of all its spans fit in 160 KiB
+        off = (lds + 15) & ~15
+        expect = []
+        for s in range(n):
+            q, t0, t1 = (int(v) for v in w["span"][s][:3])
+            a, y = OUTPUTS[outs](q)
+            b = 4 * M * 16 * (t1 - t0)
+            ey = off if y else -1
+            off += b if y else 0
+            ea = off if a else -1
+            off += b if a else 0
+            expect.append((ey, ea))
+        got = [(int(w["span"][s][4]), int(w["span"][s][5])) for s in range(n)]
+        if n and off <= 160 * 1024:
+            assert w["defer"] == 1 and got == expect
+            assert off <= h["lds"]
+        else:
+            assert w["defer"] == 0 and all(g == (-1, -1) for g in got)
     expect = [(q, t) for q, (K, s) in enumerate(shapes) for t in range(-(-sum(s) // 16))]
     assert seen == expect
 
@@ -100,7 +128,7 @@ def test_plan_balances_bytes():
     for w in work:
         b = 0
         for s in range(int(w["nspan"])):
-            q, t0, t1, _ = (int(v) for v in w["span"][s])
+            q, t0, t1, _ = (int(v) for v in w["span"][s][:4])
             b += (t1 - t0) * 16 * ls[q][0] // 4
         sizes.append(b)
     sizes = np.array(sizes)
@@ -111,6 +139,25 @@ def test_plan_balances_bytes():
     # the cuts fall on tile boundaries: no workgroup exceeds the mean share
     # by more than a tile
     assert sizes.max() <= h["weight_bytes"] / 256 + 16 * 6912 // 4
+
+
+@pytest.mark.parametrize("M,acc,deferring", [(1, False, 256), (4, False, 256), (1, True, 256),
+                                             (8, False, None), (16, False, 0),
+                                             (16, True, 0)])
+def test_plan_defers_where_outputs_fit(M, acc, deferring):
+    """The 2B-class layer set: at small M every workgroup gathers its outputs
+    in LDS (y alone, or acc and y); at M = 16 the staged activations leave no
+    room for every span's outputs in most workgroups, which then write in the
+    stream; a workgroup defers all its spans or none."""
+    ls = [(2560, (2560, 640, 640)), (2560, (2560,)), (2560, (6912, 6912)), (6912, (2560,))] * 30
+    img, p = plan(ls, M, outputs=lambda i: (acc, True))
+    h, projs, work = decode(img)
+    n = int(sum(int(w["defer"]) for w in work))
+    if deferring is None:
+        assert 0 < n < len(work)
+    else:
+        assert n == min(deferring, len(work))
+    assert h["lds"] <= 160 * 1024
 
 
 def test_check_binds_device_address():
