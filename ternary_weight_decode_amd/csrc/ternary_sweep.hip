@@ -20,10 +20,11 @@
 // across tile and projection boundaries, with no barrier and no kernel
 // boundary until the list ends.
 //
-// Work split.  One workgroup of 16 waves per compute unit; its waves take
-// the tiles of each of its projections one at a time from an LDS counter, so
-// they run out of work together (a fixed share per wave left the compute
-// unit with fewer and fewer loads in flight as its faster waves finished).
+// Work split.  One workgroup of 12 or 16 waves per compute unit; its waves
+// take the tiles of each of its projections one at a time from an LDS
+// counter, so they run out of work together (a fixed share per wave left the
+// compute unit with fewer and fewer loads in flight as its faster waves
+// finished).
 // A tile (16 weight rows, all of K) is read in passes of four 256-wide K
 // slices.  The weights come in
 // the sweep's tiled layout (twd_sweep_tile_weights): tile t is a contiguous
@@ -351,12 +352,12 @@ void sweep_kernel(const SweepHeader *header_g, const SweepProj *projs_g,
     // The issue side f runs kS - 1 passes ahead of the compute side, from
     // span to span, so the ring never drains at a span boundary; each ring
     // slot carries the span, tile and pass it holds.  The first kS - 1
-    // passes go out before the staging at M <= 8 (after the first span's
+    // passes go out before the staging at M <= 12 (after the first span's
     // activation loads), so the first weights arrive while the activations
-    // are quantized; at larger M the staging holds too many registers (a
+    // are quantized; above, in 128 registers, the staging holds too many (a
     // wave per token row, 16 rounds of loads) for the ring to be live across
     // it.  The counters hold each span's next tile.
-    constexpr bool kEarly = M <= 8;
+    constexpr bool kEarly = M <= 12;
     int *ctr = reinterpret_cast<int *>(st_scale + kSweepMaxSpans * 16);
     DynCursor f;
     uint4 ring[kS][kSweepLP];

@@ -108,13 +108,14 @@ constexpr int kSweepLP = 4;            // 256-wide K slices per pass
 // Per width: waves per workgroup, resident waves per SIMD the kernel is
 // built for (its register budget: 512 / that many registers per lane), and
 // the passes of its register ring (one computed, the rest in flight).  One
-// workgroup fills a compute unit (16 waves, four per SIMD), so all the
-// compute unit's waves share one tile counter; the planner aims for
-// 4 x sweep_simd_waves(M) / sweep_waves(M) workgroups on each of kSweepCUs
-// compute units.
+// workgroup fills a compute unit, so all the compute unit's waves share one
+// tile counter: 12 waves (three per SIMD, up to 168 registers) while the
+// staging has a wave for every token row, M <= 12; 16 waves (four per SIMD,
+// 128 registers) above.  The planner aims for 4 x sweep_simd_waves(M) /
+// sweep_waves(M) workgroups on each of kSweepCUs compute units.
 constexpr int kSweepCUs = 256;
-constexpr int sweep_waves(int) { return 16; }
-constexpr int sweep_simd_waves(int) { return 4; }
+constexpr int sweep_waves(int m) { return m <= 12 ? 12 : 16; }
+constexpr int sweep_simd_waves(int m) { return m <= 12 ? 3 : 4; }
 constexpr int sweep_ring(int) { return 2; }
 constexpr int kSweepHeaderBytes = 64;  // table header
 constexpr uint32_t kSweepMagic = 0x53445754u;  // "TWDS"
