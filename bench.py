@@ -1154,9 +1154,10 @@ def summarize_projection(args):
     lines = ["# output projection 2560 -> 128256, M=1: rocprofv3 kernel trace and HBM counters",
              "", "Commands (from the repository root):", "", "    " + cmds[0], "",
              "    " + cmds[1], "", "    " + cmds[2], "",
-             "bench.py times each role over two distinct weight copies per graph replay "
-             "(every launch reads cold weights); the trace covers all of that run's "
-             "dispatches of the kernel, eager warm-up included.", "",
+             "bench.py times each role with direct launches alternating two distinct "
+             "weight copies (every launch reads cold weights), and the same launches "
+             "replayed from a graph beside them; the trace covers all of that run's "
+             "dispatches of the kernel, warm-up included.", "",
              "| role | kernel | dispatches | average us | min us | algorithmic bytes | GB/s (avg) |"
              " % of 8 TB/s |", "|---|---|---|---|---|---|---|---|"]
     avg = {}
@@ -1170,15 +1171,6 @@ def summarize_projection(args):
         shown = ", ".join(f"`{n}`" for n in sorted(names))
         lines.append(f"| {role} | {shown} | {len(d)} | {a / 1e3:.2f} | {min(d) / 1e3:.2f} | "
                      f"{nbytes:,} | {nbytes / a:.1f} | {100 * nbytes / a / HBM_PEAK_GBS:.1f} |")
-    # the streaming reads over the projection's weight copies (the largest
-    # grids of that kernel in the run; the layer sweep's are far smaller)
-    sr = [r for r in trace if _short(_col(r, "Kernel_Name")) == "stream_read_kernel"]
-    big = max((grid(r) for r in sr), default=0)
-    reads = {}
-    for r in sr:
-        if grid(r) * 4 >= big:  # fp8-size and bf16-size reads
-            reads.setdefault(grid(r), []).append(
-                int(_col(r, "End_Timestamp")) - int(_col(r, "Start_Timestamp")))
 
     def per_kernel(d, counter):
         agg = {}
@@ -1215,11 +1207,20 @@ def summarize_projection(args):
     os.makedirs(args.profile_out, exist_ok=True)
     with open(os.path.join(args.profile_out, "output_projection_counters_2b_m1.json"), "w") as f:
         json.dump(rec, f, indent=1)
-    for g, d in sorted(reads.items()):
-        nbytes = g * 16 * 4  # 256 threads x 4 loads x 16 bytes per workgroup
-        a = sum(d) / len(d)
-        lines += ["", f"Streaming-read reference over {nbytes:,} bytes in the same run: "
-                  f"average {a / 1e3:.2f} us over {len(d)} dispatches ({nbytes / a:.1f} GB/s)."]
+    # the streaming read of the same bytes, as the profiled run timed it
+    # (large reads stride over one workgroup per compute unit, so the trace's
+    # grid sizes no longer tell the buffers apart)
+    run = None
+    if args.profile_run_json and os.path.exists(args.profile_run_json):
+        with open(args.profile_run_json) as f:
+            for line in f:
+                if line.startswith("{"):
+                    run = json.loads(line).get("output_projection")
+    if run:
+        f8, b16 = run["stream_read_fp8_bytes"], run["stream_read_bf16_bytes"]
+        lines += ["", "Streaming read of the same bytes in the profiled run (HIP events, direct "
+                  f"launches): {f8['us']:.2f} us over the E4M3 weights ({f8['gbs']:.0f} GB/s), "
+                  f"{b16['us']:.2f} us over the bf16 weights ({b16['gbs']:.0f} GB/s)."]
     lines.append("")
     path = os.path.join(args.profile_out, "output_projection_2b_m1_trace_and_counters.md")
     with open(path, "w") as f:

@@ -159,7 +159,12 @@ __device__ __forceinline__ v4f compute_chunk(uint4 (&buf)[LD], v4f acc, const ui
     return acc;
 }
 
-template <bool FP8, int NWV, int LD>
+// DEFER: the workgroup gathers its outputs in LDS after the staged rows
+// ([M][its rows] floats) and writes each token row's run once every wave is
+// done, instead of storing tile pairs inside the weight stream (stores in
+// the stream slow it far more than their bytes; the launcher picks DEFER
+// where the rows fit).
+template <bool FP8, int NWV, int LD, bool DEFER>
 __global__ __launch_bounds__(64 * NWV) void projection_kernel(
     const uint8_t *__restrict__ W, const float *__restrict__ wscale,
     const uint16_t *__restrict__ x, int M, int K, int N, int Kp, float *__restrict__ y, int ldy,
@@ -189,6 +194,9 @@ __global__ __launch_bounds__(64 * NWV) void projection_kernel(
     const int ntiles = max(0, min(tpw, tiles - first));
     const int tile_end = first + ntiles;
     const int total = ntiles * C;
+    float *ybuf = reinterpret_cast<float *>(smem + stage_bytes(M, Kp, NWV));
+    const int wg_rows = NWV * tpw * 16;
+    const int wg_n0 = blockIdx.x * wg_rows;
 
     // 1. Loads, oldest first, so that waiting for the activations never
     //    waits for weights: (fast role) one weight scale per thread -- row
@@ -222,10 +230,10 @@ __global__ __launch_bounds__(64 * NWV) void projection_kernel(
         }
     }
     __builtin_amdgcn_sched_barrier(0);
-    // Every step issues LD loads and then 8 stores (out of range, and so
-    // dropped, unless a tile pair has just finished): the body is
-    // straight-line and the load counter waits stay exact, one chunk always
-    // in flight.
+    // Every step issues LD loads and, unless the outputs are deferred, then
+    // 8 stores (out of range, and so dropped, unless a tile pair has just
+    // finished): the body is straight-line and the load counter waits stay
+    // exact, one chunk always in flight.
     const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
         y, 0, M * ldy * 4, kRawBufferFlags);
     uint4 bA[LD], bB[LD];
@@ -256,9 +264,11 @@ __global__ __launch_bounds__(64 * NWV) void projection_kernel(
     };
     const v4f zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
     next_load(bA);
-    put(zero4, zero4, 0, 0, 0);
+    if constexpr (!DEFER)
+        put(zero4, zero4, 0, 0, 0);
     next_load(bB);
-    put(zero4, zero4, 0, 0, 0);
+    if constexpr (!DEFER)
+        put(zero4, zero4, 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
 
     // 2. stage the activations as bf16 (wave w owns token rows w, w + NWV)
@@ -351,16 +361,27 @@ __global__ __launch_bounds__(64 * NWV) void projection_kernel(
             for (int i = 0; i < 4; ++i)
                 v[i] = acc[i] * sx[i] * ws;
         }
-        // a finished tile with an odd ordinal completes a pair: write both;
-        // an even one waits in `held`, unless it is the wave's last
         const bool fin = c_cp == C - 1;
-        const bool odd = (ord & 1) != 0;
-        const int lim_h = fin && odd ? N : 0;
-        const int lim_c = fin && (odd || ord == ntiles - 1) ? N : 0;
-        const int n = (t_cp - (odd ? 1 : 0)) * 16 + r;
-        put(held, v, n - (odd ? 0 : 16), lim_h, lim_c);
-        if (fin && !odd)
-            held = v;
+        if constexpr (DEFER) {
+            // rows past N are never written out
+            if (fin) {
+                const int row = t_cp * 16 + r - wg_n0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (4 * g + i < M)
+                        ybuf[(4 * g + i) * wg_rows + row] = v[i];
+            }
+        } else {
+            // a finished tile with an odd ordinal completes a pair: write
+            // both; an even one waits in `held`, unless it is the wave's last
+            const bool odd = (ord & 1) != 0;
+            const int lim_h = fin && odd ? N : 0;
+            const int lim_c = fin && (odd || ord == ntiles - 1) ? N : 0;
+            const int n = (t_cp - (odd ? 1 : 0)) * 16 + r;
+            put(held, v, n - (odd ? 0 : 16), lim_h, lim_c);
+            if (fin && !odd)
+                held = v;
+        }
         if (++c_cp == C) {
             c_cp = 0;
             ++t_cp;
@@ -373,6 +394,26 @@ __global__ __launch_bounds__(64 * NWV) void projection_kernel(
         if (it + 1 >= total)
             break;
         step(bB);
+    }
+
+    // 4. deferred outputs: each token row's run of this workgroup's rows, in
+    //    16-byte words where N and ldy are multiples of 4 and y is 16-byte
+    //    aligned, else in 4-byte words
+    if constexpr (DEFER) {
+        __syncthreads();
+        const int valid = min(wg_rows, N - wg_n0);
+        const bool vec = ((N | ldy) & 3) == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0;
+        for (int m = 0; m < M; ++m) {
+            float *dst = y + static_cast<int64_t>(m) * ldy + wg_n0;
+            const float *src = ybuf + m * wg_rows;
+            if (vec) {
+                for (int j = 4 * tid; j < valid; j += 4 * 64 * NWV)
+                    *reinterpret_cast<v4f *>(dst + j) = *reinterpret_cast<const v4f *>(src + j);
+            } else {
+                for (int j = tid; j < valid; j += 64 * NWV)
+                    dst[j] = src[j];
+            }
+        }
     }
 }
 
@@ -409,17 +450,24 @@ int projection_lds_bytes(bool fp8, int M, int K) {
     return stage_bytes(M, projection_padded_k(fp8, K), kShapeWaves);
 }
 
+namespace {
+
+// Tiles per wave as the kernel computes them for a launch of `grid`
+// workgroups over `tiles` tiles.
+int tiles_per_wave(int tiles, int grid) {
+    const int nwaves = grid * kShapeWaves;
+    return 2 * ((tiles + 2 * nwaves - 1) / (2 * nwaves));
+}
+
+}  // namespace
+
 hipError_t launch_projection(bool fp8, const uint8_t *w, const float *wscale,
                              const uint16_t *x, int M, int K, int N, float *y,
                              uint8_t *xq_out, float *xs_out, hipStream_t stream) {
     constexpr int NWV = kShapeWaves;
     const int Kp = projection_padded_k(fp8, K);
-    const int lds = stage_bytes(M, Kp, NWV);
-    const ProjFn fn = fp8 ? &projection_kernel<true, NWV, kShapeLoads>
-                          : &projection_kernel<false, NWV, kShapeLoads>;
-    hipError_t e = ensure_lds_limit(reinterpret_cast<const void *>(fn), lds);
-    if (e != hipSuccess)
-        return e;
+    const int lds_stage = stage_bytes(M, Kp, NWV);
+    hipError_t e = hipSuccess;
     const int cus = compute_units();
     if (cus <= 0)
         return hipErrorInvalidDevice;
@@ -432,6 +480,17 @@ hipError_t launch_projection(bool fp8, const uint8_t *w, const float *wscale,
         const int tiles = (rows + 15) / 16;
         const int want = (tiles + NWV - 1) / NWV;
         const int grid = want < cus ? want : cus;
+        // deferred outputs where the workgroup's rows fit beside the staging
+        const int lds_defer = lds_stage + M * NWV * tiles_per_wave(tiles, grid) * 16 * 4;
+        const bool defer = lds_defer <= 160 * 1024;
+        const int lds = defer ? lds_defer : lds_stage;
+        const ProjFn fn = fp8 ? (defer ? &projection_kernel<true, NWV, kShapeLoads, true>
+                                       : &projection_kernel<true, NWV, kShapeLoads, false>)
+                              : (defer ? &projection_kernel<false, NWV, kShapeLoads, true>
+                                       : &projection_kernel<false, NWV, kShapeLoads, false>);
+        e = ensure_lds_limit(reinterpret_cast<const void *>(fn), lds);
+        if (e != hipSuccess)
+            return e;
         hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * NWV), lds, stream, w + n0 * row_bytes,
                            wscale ? wscale + n0 : nullptr, x, M, K, rows, Kp, y + n0, N,
                            n0 == 0 ? xq_out : nullptr, n0 == 0 ? xs_out : nullptr);
