@@ -154,50 +154,126 @@ twd_status sweep_plan(const twd_sweep_proj *projs, int nproj, int64_t M, const v
     groups = groups < 1 ? 1 : groups > target ? target : groups;
     std::vector<SweepWork> work;
     int lds_max = kSweepLdsHeader;
-    SweepWork cur;
-    std::memset(&cur, 0, sizeof cur);
-    int cur_lds = kSweepLdsHeader;
-    int64_t cur_target = -1;
-    int64_t cum = 0;
-    auto close = [&]() {
-        if (cur.nspan > 0) {
-            const int end = lay_out_deferred(cur, P, m, cur_lds);
-            work.push_back(cur);
-            if (end > lds_max)
-                lds_max = end;
-        }
-        std::memset(&cur, 0, sizeof cur);
-        cur_lds = kSweepLdsHeader;
-    };
-    for (int q = 0; q < nproj; ++q) {
-        const SweepProj &d = P[q];
-        const int tiles = (d.N + 15) / 16;
-        for (int t = 0; t < tiles; ++t) {
-            const int64_t range = total > 0 ? cum * groups / total : 0;
-            if (range != cur_target) {
-                close();
-                cur_target = range;
+    // Where two neighbouring projections cannot be staged by one workgroup
+    // (their rows exceed the LDS share together), a range must end between
+    // them.  Such boundaries cut the list into segments, and each segment
+    // gets a whole number of ranges in proportion to its bytes: ranges are
+    // handed out one at a time to the segment with the most bytes per range.
+    std::vector<int> seg_of(nproj);
+    std::vector<int64_t> seg_bytes;
+    {
+        int prev = -1;
+        for (int q = 0; q < nproj; ++q) {
+            const int64_t b = static_cast<int64_t>(P[q].N) * P[q].K / 4;
+            if (b == 0) {
+                seg_of[q] = seg_bytes.empty() ? 0 : static_cast<int>(seg_bytes.size()) - 1;
+                continue;
             }
-            SweepSpan *last = cur.nspan ? &cur.span[cur.nspan - 1] : nullptr;
-            if (!last || last->q != q) {
-                const int need = m * d.stride;
-                if (cur.nspan == kSweepMaxSpans ||
-                    (cur.nspan > 0 && cur_lds + need > lds_soft))
-                    close();
-                SweepSpan &sp = cur.span[cur.nspan++];
-                sp.q = q;
-                sp.t0 = t;
-                sp.t1 = t;
-                sp.xoff = cur_lds - kSweepLdsHeader;
-                cur_lds += need;
-                last = &sp;
-            }
-            last->t1 = t + 1;
-            const int rows = d.N - 16 * t < 16 ? d.N - 16 * t : 16;
-            cum += static_cast<int64_t>(rows) * d.K / 4;
+            const bool forced = prev < 0 || kSweepLdsHeader + m * P[prev].stride +
+                                                    m * P[q].stride > lds_soft;
+            if (forced)
+                seg_bytes.push_back(0);
+            seg_of[q] = static_cast<int>(seg_bytes.size()) - 1;
+            seg_bytes.back() += b;
+            prev = q;
         }
+        if (seg_bytes.empty())
+            seg_bytes.push_back(0);
     }
-    close();
+    const int nsegs = static_cast<int>(seg_bytes.size());
+    std::vector<int64_t> seg_ranges(nsegs), seg_base(nsegs);
+    auto apportion = [&](int64_t g) {
+        for (int i = 0; i < nsegs; ++i)
+            seg_ranges[i] = 1;
+        for (int64_t left = g - nsegs; left > 0; --left) {
+            int best = 0;
+            for (int i = 1; i < nsegs; ++i)  // bytes / ranges, compared exactly
+                if (seg_bytes[i] * seg_ranges[best] > seg_bytes[best] * seg_ranges[i])
+                    best = i;
+            ++seg_ranges[best];
+        }
+        int64_t base = 0;
+        for (int i = 0; i < nsegs; ++i) {
+            seg_base[i] = base;
+            base += seg_ranges[i];
+        }
+    };
+    // Cut the tiles into about `g` ranges (per segment, of about equal
+    // bytes); a range also closes early at the span or LDS limit, which adds
+    // workgroups.
+    auto cut = [&](int64_t g) {
+        apportion(g);
+        work.clear();
+        lds_max = kSweepLdsHeader;
+        SweepWork cur;
+        std::memset(&cur, 0, sizeof cur);
+        int cur_lds = kSweepLdsHeader;
+        int64_t cur_target = -1;
+        int64_t cum = 0;  // bytes before this tile in its segment
+        int seg = -1;
+        auto close = [&]() {
+            if (cur.nspan > 0) {
+                const int end = lay_out_deferred(cur, P, m, cur_lds);
+                work.push_back(cur);
+                if (end > lds_max)
+                    lds_max = end;
+            }
+            std::memset(&cur, 0, sizeof cur);
+            cur_lds = kSweepLdsHeader;
+        };
+        for (int q = 0; q < nproj; ++q) {
+            const SweepProj &d = P[q];
+            const int tiles = (d.N + 15) / 16;
+            if (tiles > 0 && seg_of[q] != seg) {
+                seg = seg_of[q];
+                cum = 0;
+            }
+            for (int t = 0; t < tiles; ++t) {
+                const int64_t sb = seg_bytes[seg];
+                const int64_t range =
+                    seg_base[seg] + (sb > 0 ? cum * seg_ranges[seg] / sb : 0);
+                if (range != cur_target) {
+                    close();
+                    cur_target = range;
+                }
+                SweepSpan *last = cur.nspan ? &cur.span[cur.nspan - 1] : nullptr;
+                if (!last || last->q != q) {
+                    const int need = m * d.stride;
+                    if (cur.nspan == kSweepMaxSpans ||
+                        (cur.nspan > 0 && cur_lds + need > lds_soft))
+                        close();
+                    SweepSpan &sp = cur.span[cur.nspan++];
+                    sp.q = q;
+                    sp.t0 = t;
+                    sp.t1 = t;
+                    sp.xoff = cur_lds - kSweepLdsHeader;
+                    cur_lds += need;
+                    last = &sp;
+                }
+                last->t1 = t + 1;
+                const int rows = d.N - 16 * t < 16 ? d.N - 16 * t : 16;
+                cum += static_cast<int64_t>(rows) * d.K / 4;
+            }
+        }
+        close();
+    };
+    // Workgroups past the resident count would run as a second round after
+    // the first ones finish, so where the early closes push the count past
+    // it, take the largest number of byte ranges that keeps it resident
+    // (the count grows with g, so a bisection finds it).
+    cut(groups);
+    if (static_cast<int64_t>(work.size()) > target && groups > 1) {
+        int64_t lo = 1, hi = groups - 1;
+        while (lo < hi) {
+            const int64_t mid = (lo + hi + 1) / 2;
+            cut(mid);
+            if (static_cast<int64_t>(work.size()) <= target)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        cut(lo);
+    }
     if (work.empty()) {
         // every projection is empty: one workgroup that stages nothing
         SweepWork w;

@@ -55,6 +55,7 @@ def stride(K):
 
 SHAPE_LISTS = [
     [(2560, (2560, 640, 640)), (2560, (2560,)), (2560, (6912, 6912)), (6912, (2560,))] * 3,
+    [(3072, (3072, 1024, 1024)), (3072, (3072,)), (3072, (8192, 8192)), (8192, (3072,))] * 3,
     [(64, (1,)), (8192, (33, 7)), (320, (0,)), (1536, (64, 33, 33, 5)), (256, (700,))],
     [(256, (16,))] * 40,           # many small projections: span limit
     [(8192, (5000,)), (64, (3,))],
@@ -158,6 +159,29 @@ def test_plan_defers_where_outputs_fit(M, acc, deferring):
     else:
         assert n == min(deferring, len(work))
     assert h["lds"] <= 160 * 1024
+
+
+@pytest.mark.parametrize("M", [1, 8, 12, 14, 15, 16])
+def test_plan_stays_resident(M):
+    """The 4B-class stack: where the staged rows of a K = 8192 projection
+    leave no room for a neighbour (M >= 15), the ranges must end at those
+    boundaries; the plan still fits one workgroup per compute unit (no second
+    round) and no workgroup carries more than a range's share of its
+    segment: at most 10% above the mean here."""
+    ls = [(3072, (3072, 1024, 1024)), (3072, (3072,)), (3072, (8192, 8192)), (8192, (3072,))] * 36
+    img, p = plan(ls, M, outputs=lambda i: (False, True))
+    h, projs, work = decode(img)
+    assert len(work) <= 256
+    sizes = []
+    for w in work:
+        b = 0
+        for s in range(int(w["nspan"])):
+            q, t0, t1 = (int(v) for v in w["span"][s][:3])
+            b += (t1 - t0) * 16 * ls[q][0] // 4
+        sizes.append(b)
+    sizes = np.array(sizes)
+    assert sizes.sum() == h["weight_bytes"]
+    assert sizes.max() <= 1.1 * sizes.mean()
 
 
 def test_check_binds_device_address():
