@@ -24,14 +24,13 @@
 // take the tiles of each of its projections one at a time from an LDS
 // counter, so they run out of work together (a fixed share per wave left the
 // compute unit with fewer and fewer loads in flight as its faster waves
-// finished).
-// A tile (16 weight rows, all of K) is read in passes of four 256-wide K
-// slices.  The weights come in
-// the sweep's tiled layout (twd_sweep_tile_weights): tile t is a contiguous
-// run of ceil(K / 256) blocks of 1 KiB, block u holding, at lane l = 16 g +
-// r, the 16 packed bytes of tile row r at K offset 256 u + 64 g -- so each
-// pass is four whole-line loads of 1 KiB each, and each load is the
-// matrix-core A operand as it stands.  A register ring holds the pass being
+// finished).  A tile (16 weight rows, all of K) is read in passes of four
+// 256-wide K slices.  The weights come in the sweep's tiled layout
+// (twd_sweep_tile_weights): tile t is a contiguous run of ceil(K / 256)
+// blocks of 1 KiB, block u holding, at lane l = 16 g + r, the 16 packed
+// bytes of tile row r at K offset 256 u + 64 g -- so each pass is four
+// whole-line loads of 1 KiB each, and each load is the matrix-core A operand
+// as it stands.  A register ring holds the pass being
 // computed and the next passes' loads.  Each slice is decoded into four byte
 // planes (codes c = t + 1 scaled 1, 4, 16, 1), the A operands of four
 // v_mfma_i32_16x16x64_i8 with their own accumulators; B is the staged int8
