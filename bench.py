@@ -131,6 +131,20 @@ class Step:
             self.twd.ternary_linear_bf16(self.ds.w[k], p.segs, self.ds.gammas[k], self.x[k],
                                          y=self.y[k], want_acc=False, kernel=self.kernel)
 
+    def workspace_form(self):
+        """One call per projection of the bf16 linear that runs two launches
+        through a workspace where they are faster (one workspace shared by
+        the calls, which run in order on one stream)."""
+        if getattr(self, "_ws", None) is None:
+            K = max(p.K for p in self.ds.ls.projs)
+            self._ws = self.torch.empty(self.twd.linear_bf16_workspace_bytes(self.M, K),
+                                        dtype=self.torch.uint8, device="cuda")
+        for k in self.keys():
+            p = self.ds.ls.projs[k[1]]
+            self.twd.ternary_linear_bf16_ws(self.ds.w[k], p.segs, self.ds.gammas[k], self.x[k],
+                                            workspace=self._ws, y=self.y[k], want_acc=False,
+                                            kernel=self.kernel)
+
     def two_launch(self):
         """Stand-alone quantizer, then the pre-quantized linear."""
         for k in self.keys():
@@ -251,7 +265,7 @@ def time_graph(torch, fn, reps):
 
 
 def width_entry(twd, torch, dev_set, workload, M, kernel, reps, outliers=False,
-                forms=("sweep", "fused", "two_launch"), graphs=True):
+                forms=("sweep", "fused", "two_launch", "workspace"), graphs=True):
     """One width.  The sweep (one launch per step) is timed as launched
     directly, back to back, and (graphs) also captured into a graph and
     replayed; the per-projection forms are captured and replayed (graph) and,
@@ -297,10 +311,22 @@ def width_entry(twd, torch, dev_set, workload, M, kernel, reps, outliers=False,
         out["two_launch"] = {"gbs": round(nbytes / sec / 1e9, 1),
                              "kernels": kernel_map(twd, dev_set.ls, M, kernel, False)}
         del g
+    if "workspace" in forms:
+        # the entry point that picks the form per shape (two launches through
+        # a workspace where they are faster); its outputs equal the
+        # one-launch form's
+        if "fused" in forms:
+            st.clear()
+            st.workspace_form()
+            torch.cuda.synchronize()
+            if not st.equals(ref):
+                raise SystemExit(f"workspace form differs from the one-launch form at M={M}")
+        g, sec = time_graph(torch, st.workspace_form, reps)
+        out["workspace_form"] = {"gbs": round(nbytes / sec / 1e9, 1),
+                                 "us_per_projection": round(sec / n * 1e6, 3)}
+        del g
     if "per_launch" in out and "two_launch" in out:
-        # the faster per-projection form at this width (the one-launch entry
-        # point cannot pick the two-launch form: it would need a workspace
-        # for the quantized rows)
+        # the faster of the two fixed per-projection forms at this width
         best = max(("one_launch", out["per_launch"]["gbs"]), ("two_launch", out["two_launch"]["gbs"]),
                    key=lambda kv: kv[1])
         out["per_projection_best"] = {"form": best[0], "gbs": best[1]}

@@ -185,6 +185,32 @@ twd_status twd_ternary_linear_bf16(const uint8_t *wpacked, int nseg,
                                    int64_t K, int32_t *acc, float *y,
                                    int kernel, void *stream);
 
+/* Bytes of the workspace twd_ternary_linear_bf16_ws uses for (M, K): the
+ * int8 rows [M][K], then (at the next 16-byte boundary) the fp32 scales
+ * [M].  -1 for M outside 0..TWD_MAX_M or K outside the linear's limits. */
+int64_t twd_linear_bf16_workspace_bytes(int64_t M, int64_t K);
+
+/* twd_ternary_linear_bf16 with the form picked by width and shape (M1 picks
+ * the operator by replay width and by the layer's dimensions: BitMTP page,
+ * "Methodology in Plain English", paragraph 3).  Where every workgroup of
+ * the fused launch would quantize a wide M x K block -- M >= 14, or M >= 7
+ * with K >= 4096 -- and kernel is TWD_KERNEL_AUTO, it runs two launches
+ * instead: twd_quantize_act into the workspace, then the pre-quantized
+ * linear (twd_ternary_linear_fused) from it.  Results are identical either
+ * way (acc bit for bit, y the same fp32 evaluation).  workspace: device,
+ * 16-byte aligned, at least twd_linear_bf16_workspace_bytes(M, K) bytes,
+ * owned by the caller; calls that share a workspace must not overlap.
+ * workspace = NULL always runs the one-launch form.  Other arguments and
+ * errors as twd_ternary_linear_bf16, plus INVALID_ARG for a misaligned or
+ * short workspace. */
+twd_status twd_ternary_linear_bf16_ws(const uint8_t *wpacked, int nseg,
+                                      const int64_t *seg_rows,
+                                      const float *seg_gamma,
+                                      const uint16_t *x_bf16, int64_t M,
+                                      int64_t K, int32_t *acc, float *y,
+                                      int kernel, void *workspace,
+                                      int64_t workspace_bytes, void *stream);
+
 /* The kernel family the width dispatch picks for (M, K, N), without
  * launching anything: for twd_ternary_linear_bf16 if bf16_input != 0, else
  * for the int8 entry points (the choice can differ where the quantization

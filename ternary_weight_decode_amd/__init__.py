@@ -66,6 +66,8 @@ _lib_fused_kernel = _sig("twd_ternary_linear_fused_kernel",
                          [_p, _int, _p, _p, _p, _p, _i64, _i64, _p, _p, _int, _p])
 _lib_bf16 = _sig("twd_ternary_linear_bf16",
                  [_p, _int, _p, _p, _p, _i64, _i64, _p, _p, _int, _p])
+_lib_bf16_ws = _sig("twd_ternary_linear_bf16_ws",
+                    [_p, _int, _p, _p, _p, _i64, _i64, _p, _p, _int, _p, _i64, _p])
 _lib_select = _sig("twd_select_kernel", [_i64, _i64, _i64, _int])
 _lib_quantize_fp8_rows = _sig("twd_quantize_fp8_rows", [_p, _i64, _i64, _p, _p])
 _lib_proj_fp8 = _sig("twd_projection_fp8", [_p, _p, _p, _i64, _i64, _i64, _p, _p, _p, _p])
@@ -91,6 +93,7 @@ class SweepPlan(ctypes.Structure):
 
 
 _lib_tiled_bytes = _sig("twd_sweep_tiled_bytes", [_i64, _i64], _i64)
+_lib_ws_bytes = _sig("twd_linear_bf16_workspace_bytes", [_i64, _i64], _i64)
 _lib_tile = _sig("twd_sweep_tile_weights", [_p, _i64, _i64, _p])
 _lib_sweep_bytes = _sig("twd_sweep_table_bytes", [_p, _int, _i64, _p])
 _lib_sweep_encode = _sig("twd_sweep_encode", [_p, _int, _i64, _p, _p, _i64, _p])
@@ -101,6 +104,7 @@ EXPORTS = ("twd_version", "twd_last_error", "twd_ternarize_absmean",
            "twd_pack_ternary", "twd_unpack_ternary", "twd_quantize_act",
            "twd_ternary_linear", "twd_ternary_linear_fused",
            "twd_ternary_linear_fused_kernel", "twd_ternary_linear_bf16",
+           "twd_linear_bf16_workspace_bytes", "twd_ternary_linear_bf16_ws",
            "twd_select_kernel", "twd_quantize_fp8_rows", "twd_projection_fp8",
            "twd_projection_bf16", "twd_kv_commit", "twd_stream_read", "twd_stream_copy",
            "twd_sweep_tiled_bytes", "twd_sweep_tile_weights",
@@ -306,6 +310,37 @@ def ternary_linear_bf16(wpacked, seg_rows, seg_gamma, x, acc=None, y=None,
                      _dev_ptr(x, "x", (torch.bfloat16, torch.int16)), M, K,
                      _dev_ptr(acc, "acc", (torch.int32,)), _dev_ptr(y, "y", (torch.float32,)),
                      int(kernel), _stream(stream)))
+    return acc, y
+
+
+def linear_bf16_workspace_bytes(M: int, K: int) -> int:
+    """Workspace bytes ternary_linear_bf16_ws needs for (M, K); -1 if invalid."""
+    return int(_lib_ws_bytes(int(M), int(K)))
+
+
+def ternary_linear_bf16_ws(wpacked, seg_rows, seg_gamma, x, workspace=None, acc=None, y=None,
+                           want_acc=True, want_y=True, kernel=KERNEL_AUTO, stream=None):
+    """ternary_linear_bf16 with the form picked by width and shape: two
+    launches (quantizer into `workspace`, a device uint8 tensor of at least
+    linear_bf16_workspace_bytes(M, K) bytes, then the int8 linear) where they
+    are faster, else one.  workspace=None: always one launch."""
+    torch = _torch()
+    _need(x.dim() == 2, "x must be [M, K]")
+    M, K = x.shape
+    seg_rows = [int(r) for r in seg_rows]
+    nseg = len(seg_rows)
+    _need(len(seg_gamma) == nseg, "one gamma per segment")
+    N = int(sum(seg_rows))
+    _need(_nbytes(wpacked) >= N * K // 4, "wpacked holds fewer than N*K/4 bytes")
+    rows = (ctypes.c_int64 * max(nseg, 1))(*seg_rows)
+    gam = (ctypes.c_float * max(nseg, 1))(*[float(g) for g in seg_gamma])
+    acc, y = _outputs(M, N, x.device, acc, y, want_acc, want_y)
+    ws = _dev_ptr(workspace, "workspace", (torch.uint8,)) if workspace is not None else None
+    _check(_lib_bf16_ws(_dev_ptr(wpacked, "wpacked", (torch.uint8,)), nseg, rows, gam,
+                        _dev_ptr(x, "x", (torch.bfloat16, torch.int16)), M, K,
+                        _dev_ptr(acc, "acc", (torch.int32,)), _dev_ptr(y, "y", (torch.float32,)),
+                        int(kernel), ws, _nbytes(workspace) if workspace is not None else 0,
+                        _stream(stream)))
     return acc, y
 
 

@@ -165,6 +165,68 @@ extern "C" twd_status twd_ternary_linear_bf16(
                       M, K, acc, y, kernel, stream);
 }
 
+namespace {
+
+// Where every workgroup of the fused launch would quantize a wide M x K
+// block, the stand-alone quantizer followed by the pre-quantized linear is
+// faster: from M = 14 on every 2B-class shape, and from M = 7 where
+// K >= 4096 (the down projection, K = 6912: 6.8 against 7.6 us at M = 7,
+// 8.3 against 10.6 us at M = 16, per launch, graph-replayed; at M = 6 one
+// launch is still ahead, 6.2 against 6.6 us).
+bool two_launch_pays(int64_t M, int64_t K) { return M >= 14 || (K >= 4096 && M >= 7); }
+
+// Workspace of the two-launch form: the int8 rows [M][K], then (16-byte
+// aligned) the fp32 scales [M].
+int64_t quantized_offset(int64_t M, int64_t K) { return (M * K + 15) / 16 * 16; }
+
+}  // namespace
+
+extern "C" int64_t twd_linear_bf16_workspace_bytes(int64_t M, int64_t K) {
+    if (M < 0 || M > TWD_MAX_M || K < 64 || K > TWD_MAX_K || K % 64 != 0)
+        return -1;
+    return quantized_offset(M, K) + 4 * M;
+}
+
+extern "C" twd_status twd_ternary_linear_bf16_ws(
+    const uint8_t *wpacked, int nseg, const int64_t *seg_rows,
+    const float *seg_gamma, const uint16_t *x_bf16, int64_t M, int64_t K,
+    int32_t *acc, float *y, int kernel, void *workspace, int64_t workspace_bytes,
+    void *stream) {
+    Segments segs;
+    int64_t N = 0;
+    twd_status st = check_linear(wpacked, nseg, seg_rows, seg_gamma, x_bf16, true, nullptr,
+                                 M, K, acc, y, kernel, &segs, &N);
+    if (st != TWD_OK)
+        return st;
+    if (workspace) {
+        if (!aligned(workspace, 16))
+            return set_error(TWD_ERR_INVALID_ARG, "linear_bf16_ws: workspace not 16-byte aligned");
+        if (workspace_bytes < twd_linear_bf16_workspace_bytes(M, K))
+            return set_error(TWD_ERR_INVALID_ARG,
+                             "linear_bf16_ws: workspace of %lld bytes, %lld needed",
+                             (long long)workspace_bytes,
+                             (long long)twd_linear_bf16_workspace_bytes(M, K));
+    }
+    if (M == 0 || N == 0)
+        return TWD_OK;
+    if (!workspace || kernel != TWD_KERNEL_AUTO || !two_launch_pays(M, K))
+        return run_linear(wpacked, nseg, seg_rows, seg_gamma, x_bf16, true, nullptr, M, K,
+                          acc, y, kernel, stream);
+    int8_t *xq = static_cast<int8_t *>(workspace);
+    float *xs = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) +
+                                          quantized_offset(M, K));
+    hipError_t e = launch_quantize_act(x_bf16, static_cast<int>(M), static_cast<int>(K), xq,
+                                       xs, as_stream(stream));
+    if (e != hipSuccess)
+        return hip_status(e, "quantize_act launch");
+    const LinearPlan plan = plan_linear(static_cast<int>(M), static_cast<int>(K),
+                                        static_cast<int>(N), false, TWD_KERNEL_AUTO);
+    return hip_status(launch_linear(plan, wpacked, xq, false, xs, static_cast<int>(M),
+                                    static_cast<int>(K), static_cast<int>(N), segs, acc, y,
+                                    as_stream(stream)),
+                      "linear launch");
+}
+
 extern "C" twd_status twd_ternary_linear_fused(
     const uint8_t *wpacked, int nseg, const int64_t *seg_rows,
     const float *seg_gamma, const int8_t *xq, const float *xscale, int64_t M,

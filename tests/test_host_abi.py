@@ -263,6 +263,35 @@ def test_projection_rejects_before_launch(twd):
     assert twd._lib_last_error()
 
 
+def test_linear_bf16_workspace_bytes(twd):
+    """The two-launch form's workspace: int8 rows [M][K], then the fp32
+    scales [M] at the next 16-byte boundary."""
+    assert twd.linear_bf16_workspace_bytes(16, 6912) == 16 * 6912 + 64
+    assert twd.linear_bf16_workspace_bytes(1, 64) == 64 + 4
+    assert twd.linear_bf16_workspace_bytes(3, 64) == 192 + 12
+    assert twd.linear_bf16_workspace_bytes(0, 64) == 0
+    for M, K in ((17, 64), (-1, 64), (1, 100), (1, 0), (1, 16384)):
+        assert twd.linear_bf16_workspace_bytes(M, K) == -1
+
+
+def test_linear_bf16_ws_rejects_before_launch(twd):
+    """A misaligned or short workspace is refused before anything launches;
+    the linear's own checks apply as for twd_ternary_linear_bf16."""
+    f = twd._lib_bf16_ws
+    rows = (ctypes.c_int64 * 1)(16)
+    gam = (ctypes.c_float * 1)(1.0)
+    w, x, y, ws = 0x10000, 0x20000, 0x30000, 0x40000
+    need = twd.linear_bf16_workspace_bytes(16, 6912)
+
+    def call(M=16, K=6912, ws_ptr=ws, ws_bytes=need, kernel=0):
+        return f(w, 1, rows, gam, x, M, K, None, y, kernel, ws_ptr, ws_bytes, None)
+
+    assert call(ws_ptr=ws + 8) == 1
+    assert call(ws_bytes=need - 1) == 1 and b"needed" in twd._lib_last_error()
+    assert call(K=100) == 2 and call(M=17) == 2
+    assert call(M=0) == 0  # nothing to do, nothing launched
+
+
 def test_kv_commit_rejects_before_launch(twd):
     f = twd._lib_kv_commit
     segs = (ctypes.c_void_p * 4)(0x10000, 0x20000, 0x30000, 0x40000)
