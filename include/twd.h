@@ -211,6 +211,29 @@ twd_status twd_ternary_linear_bf16_ws(const uint8_t *wpacked, int nseg,
                                       int kernel, void *workspace,
                                       int64_t workspace_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * twd_ternary_linear_bf16_ws with the library's own workspace, a static
+ * device array of 131136 bytes per device (the workspace of M = TWD_MAX_M,
+ * K = TWD_MAX_K), held until the process ends.  Same arguments, results
+ * and errors as twd_ternary_linear_bf16_ws with a workspace, plus
+ * UNSUPPORTED where twd_linear_bf16_workspace_bytes(M, K) exceeds that
+ * array, and INVALID_ARG if the stream belongs to a device other than the
+ * current one.  The first call on a device that needs the array looks up
+ * its address there (hipGetSymbolAddress; no allocation); make that first
+ * call outside graph capture.  Nothing is allocated, freed or
+ * synchronized.  All calls on one device share its array: calls that
+ * overlap on one device (different streams not ordered against each other,
+ * or host threads launching at once) race on it and give wrong results;
+ * order them on one stream.  Nothing needs clearing between calls (the
+ * quantizer writes every byte the linear then reads). */
+twd_status twd_ternary_linear_bf16_noalloc(const uint8_t *wpacked, int nseg,
+                                           const int64_t *seg_rows,
+                                           const float *seg_gamma,
+                                           const uint16_t *x_bf16, int64_t M,
+                                           int64_t K, int32_t *acc, float *y,
+                                           int kernel, void *stream);
+
 /* The kernel family the width dispatch picks for (M, K, N), without
  * launching anything: for twd_ternary_linear_bf16 if bf16_input != 0, else
  * for the int8 entry points (the choice can differ where the quantization

@@ -68,6 +68,8 @@ _lib_bf16 = _sig("twd_ternary_linear_bf16",
                  [_p, _int, _p, _p, _p, _i64, _i64, _p, _p, _int, _p])
 _lib_bf16_ws = _sig("twd_ternary_linear_bf16_ws",
                     [_p, _int, _p, _p, _p, _i64, _i64, _p, _p, _int, _p, _i64, _p])
+_lib_bf16_noalloc = _sig("twd_ternary_linear_bf16_noalloc",
+                         [_p, _int, _p, _p, _p, _i64, _i64, _p, _p, _int, _p])
 _lib_select = _sig("twd_select_kernel", [_i64, _i64, _i64, _int])
 _lib_quantize_fp8_rows = _sig("twd_quantize_fp8_rows", [_p, _i64, _i64, _p, _p])
 _lib_proj_fp8 = _sig("twd_projection_fp8", [_p, _p, _p, _i64, _i64, _i64, _p, _p, _p, _p])
@@ -105,6 +107,7 @@ EXPORTS = ("twd_version", "twd_last_error", "twd_ternarize_absmean",
            "twd_ternary_linear", "twd_ternary_linear_fused",
            "twd_ternary_linear_fused_kernel", "twd_ternary_linear_bf16",
            "twd_linear_bf16_workspace_bytes", "twd_ternary_linear_bf16_ws",
+           "twd_ternary_linear_bf16_noalloc",
            "twd_select_kernel", "twd_quantize_fp8_rows", "twd_projection_fp8",
            "twd_projection_bf16", "twd_kv_commit", "twd_stream_read", "twd_stream_copy",
            "twd_sweep_tiled_bytes", "twd_sweep_tile_weights",
@@ -341,6 +344,31 @@ def ternary_linear_bf16_ws(wpacked, seg_rows, seg_gamma, x, workspace=None, acc=
                         _dev_ptr(acc, "acc", (torch.int32,)), _dev_ptr(y, "y", (torch.float32,)),
                         int(kernel), ws, _nbytes(workspace) if workspace is not None else 0,
                         _stream(stream)))
+    return acc, y
+
+
+def ternary_linear_bf16_noalloc(wpacked, seg_rows, seg_gamma, x, acc, y, kernel=KERNEL_AUTO,
+                                stream=None):
+    """ternary_linear_bf16_ws with the library's own per-device workspace: the
+    call itself allocates nothing, so acc [M, N] int32 and y [M, N] fp32 are
+    required (either may be None to skip it).  Calls that overlap on one
+    device race on that workspace."""
+    torch = _torch()
+    _need(x.dim() == 2, "x must be [M, K]")
+    M, K = x.shape
+    seg_rows = [int(r) for r in seg_rows]
+    nseg = len(seg_rows)
+    _need(len(seg_gamma) == nseg, "one gamma per segment")
+    N = int(sum(seg_rows))
+    _need(_nbytes(wpacked) >= N * K // 4, "wpacked holds fewer than N*K/4 bytes")
+    for t, name in ((acc, "acc"), (y, "y")):
+        _need(t is None or tuple(t.shape) == (M, N), f"{name} must be [M, N]")
+    rows = (ctypes.c_int64 * max(nseg, 1))(*seg_rows)
+    gam = (ctypes.c_float * max(nseg, 1))(*[float(g) for g in seg_gamma])
+    _check(_lib_bf16_noalloc(_dev_ptr(wpacked, "wpacked", (torch.uint8,)), nseg, rows, gam,
+                             _dev_ptr(x, "x", (torch.bfloat16, torch.int16)), M, K,
+                             _dev_ptr(acc, "acc", (torch.int32,)),
+                             _dev_ptr(y, "y", (torch.float32,)), int(kernel), _stream(stream)))
     return acc, y
 
 

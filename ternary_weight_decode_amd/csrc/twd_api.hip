@@ -187,6 +187,37 @@ extern "C" int64_t twd_linear_bf16_workspace_bytes(int64_t M, int64_t K) {
     return quantized_offset(M, K) + 4 * M;
 }
 
+namespace {
+
+// The body shared by the workspace and the allocation-free forms, after the
+// checks: one launch, or the quantizer into the workspace and then the int8
+// linear from it.
+twd_status linear_bf16_forms(const uint8_t *wpacked, int nseg, const int64_t *seg_rows,
+                             const float *seg_gamma, const uint16_t *x_bf16, int64_t M,
+                             int64_t K, int64_t N, const Segments &segs, int32_t *acc,
+                             float *y, int kernel, void *workspace, void *stream) {
+    if (M == 0 || N == 0)
+        return TWD_OK;
+    if (!workspace || kernel != TWD_KERNEL_AUTO || !two_launch_pays(M, K))
+        return run_linear(wpacked, nseg, seg_rows, seg_gamma, x_bf16, true, nullptr, M, K,
+                          acc, y, kernel, stream);
+    int8_t *xq = static_cast<int8_t *>(workspace);
+    float *xs = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) +
+                                          quantized_offset(M, K));
+    hipError_t e = launch_quantize_act(x_bf16, static_cast<int>(M), static_cast<int>(K), xq,
+                                       xs, as_stream(stream));
+    if (e != hipSuccess)
+        return hip_status(e, "quantize_act launch");
+    const LinearPlan plan = plan_linear(static_cast<int>(M), static_cast<int>(K),
+                                        static_cast<int>(N), false, TWD_KERNEL_AUTO);
+    return hip_status(launch_linear(plan, wpacked, xq, false, xs, static_cast<int>(M),
+                                    static_cast<int>(K), static_cast<int>(N), segs, acc, y,
+                                    as_stream(stream)),
+                      "linear launch");
+}
+
+}  // namespace
+
 extern "C" twd_status twd_ternary_linear_bf16_ws(
     const uint8_t *wpacked, int nseg, const int64_t *seg_rows,
     const float *seg_gamma, const uint16_t *x_bf16, int64_t M, int64_t K,
@@ -207,24 +238,37 @@ extern "C" twd_status twd_ternary_linear_bf16_ws(
                              (long long)workspace_bytes,
                              (long long)twd_linear_bf16_workspace_bytes(M, K));
     }
+    return linear_bf16_forms(wpacked, nseg, seg_rows, seg_gamma, x_bf16, M, K, N, segs, acc, y,
+                             kernel, workspace, stream);
+}
+
+extern "C" twd_status twd_ternary_linear_bf16_noalloc(
+    const uint8_t *wpacked, int nseg, const int64_t *seg_rows,
+    const float *seg_gamma, const uint16_t *x_bf16, int64_t M, int64_t K,
+    int32_t *acc, float *y, int kernel, void *stream) {
+    Segments segs;
+    int64_t N = 0;
+    twd_status st = check_linear(wpacked, nseg, seg_rows, seg_gamma, x_bf16, true, nullptr,
+                                 M, K, acc, y, kernel, &segs, &N);
+    if (st != TWD_OK)
+        return st;
+    const int64_t need = twd_linear_bf16_workspace_bytes(M, K);
+    if (need < 0 || need > kNoAllocScratchBytes)
+        return set_error(TWD_ERR_UNSUPPORTED,
+                         "linear_bf16_noalloc: M=%lld, K=%lld needs %lld scratch bytes, "
+                         "more than the %lld held",
+                         (long long)M, (long long)K, (long long)need,
+                         (long long)kNoAllocScratchBytes);
     if (M == 0 || N == 0)
         return TWD_OK;
-    if (!workspace || kernel != TWD_KERNEL_AUTO || !two_launch_pays(M, K))
-        return run_linear(wpacked, nseg, seg_rows, seg_gamma, x_bf16, true, nullptr, M, K,
-                          acc, y, kernel, stream);
-    int8_t *xq = static_cast<int8_t *>(workspace);
-    float *xs = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) +
-                                          quantized_offset(M, K));
-    hipError_t e = launch_quantize_act(x_bf16, static_cast<int>(M), static_cast<int>(K), xq,
-                                       xs, as_stream(stream));
-    if (e != hipSuccess)
-        return hip_status(e, "quantize_act launch");
-    const LinearPlan plan = plan_linear(static_cast<int>(M), static_cast<int>(K),
-                                        static_cast<int>(N), false, TWD_KERNEL_AUTO);
-    return hip_status(launch_linear(plan, wpacked, xq, false, xs, static_cast<int>(M),
-                                    static_cast<int>(K), static_cast<int>(N), segs, acc, y,
-                                    as_stream(stream)),
-                      "linear launch");
+    void *ws = nullptr;
+    if (kernel == TWD_KERNEL_AUTO && two_launch_pays(M, K)) {
+        st = noalloc_scratch(stream, &ws);
+        if (st != TWD_OK)
+            return st;
+    }
+    return linear_bf16_forms(wpacked, nseg, seg_rows, seg_gamma, x_bf16, M, K, N, segs, acc, y,
+                             kernel, ws, stream);
 }
 
 extern "C" twd_status twd_ternary_linear_fused(

@@ -31,6 +31,12 @@ constexpr bool narrow_fits(int M, int U) { return U >= 1 && U <= 8 && M * U <= 4
 // Thread-local error message; returns `st` for convenient chaining.
 twd_status set_error(twd_status st, const char *fmt, ...);
 
+// The static workspace of twd_ternary_linear_bf16_noalloc: its size, and its
+// address on the device that runs `stream` (which must be the current one),
+// looked up once per device.  Sets the error text on failure.
+constexpr int64_t kNoAllocScratchBytes = int64_t(TWD_MAX_M) * TWD_MAX_K + 4 * TWD_MAX_M;
+twd_status noalloc_scratch(void *stream, void **out);
+
 LinearPlan plan_linear(int M, int K, int N, bool bf16_input, int forced_kernel);
 
 hipError_t launch_quantize_act(const uint16_t *x, int M, int K, int8_t *xq,

@@ -115,6 +115,17 @@ int main() {
     CHECK(twd_ternary_linear_bf16(w, 1, rows, gam, reinterpret_cast<const uint16_t *>(xq), 5,
                                   256, nullptr, y, TWD_KERNEL_DOT, nullptr) ==
           TWD_ERR_UNSUPPORTED);
+    const uint16_t *xb = reinterpret_cast<const uint16_t *>(xq);
+    void *wsp = const_cast<float *>(xs);
+    CHECK(twd_linear_bf16_workspace_bytes(16, 6912) == 16 * 6912 + 64);
+    CHECK(twd_ternary_linear_bf16_ws(w, 1, rows, gam, xb, 16, 6912, nullptr, y, 0, wsp, 64,
+                                     nullptr) == TWD_ERR_INVALID_ARG);
+    CHECK(twd_ternary_linear_bf16_noalloc(w, 1, rows, gam, xb, 17, 256, nullptr, y, 0,
+                                          nullptr) == TWD_ERR_UNSUPPORTED);
+    CHECK(twd_ternary_linear_bf16_noalloc(w, 1, rows, gam, xb, 16, 6912, nullptr, y, 0,
+                                          nullptr) == TWD_ERR_HIP);  // the stub lookup fails
+    CHECK(twd_ternary_linear_bf16_noalloc(w, 1, rows, gam, xb, 4, 256, nullptr, y, 0,
+                                          nullptr) == TWD_ERR_HIP);  // the stub launch fails
     CHECK(twd_select_kernel(1, 2560, 3840, 1) >= 1 && twd_select_kernel(0, 2560, 3840, 1) == -1);
     CHECK(twd_quantize_act(reinterpret_cast<const uint16_t *>(xq), 2, 12, const_cast<int8_t *>(xq),
                            const_cast<float *>(xs), nullptr) == TWD_ERR_UNSUPPORTED);

@@ -50,5 +50,8 @@ hipError_t launch_stream_copy(const void *, void *, int64_t, hipStream_t) {
     return hipErrorInvalidValue;
 }
 hipError_t launch_sweep(const twd_sweep_plan &, hipStream_t) { return hipErrorInvalidValue; }
+twd_status noalloc_scratch(void *, void **) {
+    return set_error(TWD_ERR_HIP, "linear_bf16_noalloc: no device in the host-only build");
+}
 
 }  // namespace twd

@@ -292,6 +292,22 @@ def test_linear_bf16_ws_rejects_before_launch(twd):
     assert call(M=0) == 0  # nothing to do, nothing launched
 
 
+def test_linear_bf16_noalloc_rejects_before_launch(twd):
+    """The allocation-free form applies the linear's checks before it looks up
+    its static workspace or launches anything."""
+    f = twd._lib_bf16_noalloc
+    rows = (ctypes.c_int64 * 1)(16)
+    gam = (ctypes.c_float * 1)(1.0)
+    w, x, y = 0x10000, 0x20000, 0x30000
+
+    def call(M=16, K=6912, kernel=0):
+        return f(w, 1, rows, gam, x, M, K, None, y, kernel, None)
+
+    assert call(K=100) == 2 and call(M=17) == 2 and call(K=8256) == 2
+    assert call(kernel=99) == 1
+    assert call(M=0) == 0  # nothing to do, nothing looked up or launched
+
+
 def test_kv_commit_rejects_before_launch(twd):
     f = twd._lib_kv_commit
     segs = (ctypes.c_void_p * 4)(0x10000, 0x20000, 0x30000, 0x40000)
