@@ -398,3 +398,20 @@ def test_profile_summary_refuses_runs_of_other_sources(tmp_path):
                            capture_output=True, text=True, cwd=ROOT)
         assert r.returncode != 0 and "profile" in r.stderr
         assert not any(p.suffix == ".json" and p.name != "run.json" for p in tmp_path.iterdir())
+
+
+def test_linear_bf16_noalloc_binding_checks_tensors(twd):
+    """The allocation-free binding refuses host tensors and outputs of the
+    wrong shape before calling the library."""
+    torch = pytest.importorskip("torch")
+    M, K, N = 4, 128, 16
+    wp = torch.zeros(N * K // 4, dtype=torch.uint8)
+    x = torch.zeros((M, K), dtype=torch.bfloat16)
+    acc = torch.zeros((M, N), dtype=torch.int32)
+    y = torch.zeros((M, N), dtype=torch.float32)
+    with pytest.raises(ValueError, match="device tensor"):
+        twd.ternary_linear_bf16_noalloc(wp, (N,), (1.0,), x, acc, y)
+    with pytest.raises(ValueError, match=r"acc must be \[M, N\]"):
+        twd.ternary_linear_bf16_noalloc(wp, (N,), (1.0,), x, acc[:, :8], y)
+    with pytest.raises(ValueError, match="one gamma per segment"):
+        twd.ternary_linear_bf16_noalloc(wp, (8, 8), (1.0,), x, acc, y)
