@@ -294,6 +294,9 @@ def width_entry(twd, torch, dev_set, workload, M, kernel, reps, outliers=False,
             g, gsec = time_graph(torch, st.sweep, reps)
             e["graph_us"] = round(gsec * 1e6, 2)
             del g
+        prof = sweep_profile(workload, M, nbytes)
+        if prof:
+            e["trace"] = prof
         out["sweep"] = e
     if "fused" in forms:
         g, sec = time_graph(torch, st.fused, reps)
@@ -710,6 +713,19 @@ def sweep_record(workload, M):
     if rec.get("source_hash") != kernel_source_hash(SWEEP_SOURCES):
         return None
     return rec
+
+
+def sweep_profile(workload, M, nbytes):
+    """The committed rocprofv3 figures of the sweep at this workload and
+    width (kernel-trace average, the fraction of 8 TB/s it gives, HBM bytes
+    per launch, the summary file), or None if none was taken on the current
+    sources."""
+    rec = sweep_record(workload, M)
+    if not rec:
+        return None
+    return {"avg_us": rec["kernel_trace_avg_us"],
+            "frac": round(nbytes / (rec["kernel_trace_avg_us"] * 1e3) / HBM_PEAK_GBS, 4),
+            "traffic": rec["hbm_bytes_per_launch"], "summary": rec["summary"]}
 
 
 def kernel_source_hash(names=LINEAR_SOURCES):
@@ -1542,6 +1558,8 @@ def main():
                                 "sweep_us": e["sweep"]["us"],
                                 "per_launch_gbs": e["per_launch"]["gbs"],
                                 "per_launch_kernels": e["per_launch"]["kernels"]}
+                if "trace" in e["sweep"]:
+                    tab[str(Mw)]["sweep_trace"] = e["sweep"]["trace"]
             out["set_4b"] = {"layer_set": "4B-class, hidden 3072, 36 layers",
                              "packed_weight_bytes_per_step": ds4.bytes_per_sweep,
                              "widths": tab}
