@@ -219,9 +219,9 @@ twd_status twd_ternary_linear_bf16_ws(const uint8_t *wpacked, int nseg,
  * and errors as twd_ternary_linear_bf16_ws with a workspace, plus
  * UNSUPPORTED where twd_linear_bf16_workspace_bytes(M, K) exceeds that
  * array, and INVALID_ARG if the stream belongs to a device other than the
- * current one.  The first call on a device that needs the array looks up
- * its address there (hipGetSymbolAddress; no allocation); make that first
- * call outside graph capture.  Nothing is allocated, freed or
+ * current one.  The first call on a device with M, N > 0, whatever form it
+ * runs, looks up the array's address there (hipGetSymbolAddress; no
+ * allocation); make that first call outside graph capture.  Nothing is allocated, freed or
  * synchronized.  All calls on one device share its array: calls that
  * overlap on one device (different streams not ordered against each other,
  * or host threads launching at once) race on it and give wrong results;

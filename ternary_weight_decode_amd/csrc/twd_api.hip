@@ -261,12 +261,12 @@ extern "C" twd_status twd_ternary_linear_bf16_noalloc(
                          (long long)kNoAllocScratchBytes);
     if (M == 0 || N == 0)
         return TWD_OK;
+    // Every call looks the array up, whichever form it runs, so the first
+    // call on a device (of any shape) sets it up there.
     void *ws = nullptr;
-    if (kernel == TWD_KERNEL_AUTO && two_launch_pays(M, K)) {
-        st = noalloc_scratch(stream, &ws);
-        if (st != TWD_OK)
-            return st;
-    }
+    st = noalloc_scratch(stream, &ws);
+    if (st != TWD_OK)
+        return st;
     return linear_bf16_forms(wpacked, nseg, seg_rows, seg_gamma, x_bf16, M, K, N, segs, acc, y,
                              kernel, ws, stream);
 }

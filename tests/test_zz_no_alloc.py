@@ -81,3 +81,38 @@ def test_noalloc_rejects_before_launch(env):
         twd.ternary_linear_bf16_noalloc(wp, segs, gammas, xd, acc, None, kernel=99)
     torch.cuda.synchronize()
     assert bool((acc == 0).all())
+
+
+def test_noalloc_graph_replays_match_oracle(env):
+    """A caller that cannot allocate under capture: after one eager call has
+    set the device up, the two-launch call is captured into a graph and
+    replayed three times, with eager work between replays; every replay
+    equals the oracle."""
+    torch, twd, orc = env
+    M, K, segs = 16, 6912, (300,)
+    W, segs, x = wl.random_case(seed=995, M=M, K=K, seg_rows=segs)
+    N = int(sum(segs))
+    packed, gammas = twd.prepare_weights(W, segs)
+    wp = torch.from_numpy(packed).cuda()
+    xd = dev_bf16(torch, x)
+    ref = orc.forward(W, segs, x)
+    acc = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    y = torch.empty((M, N), device="cuda")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        twd.ternary_linear_bf16_noalloc(wp, segs, gammas, xd, acc, y)
+    torch.cuda.synchronize()
+    log("noalloc graph: capture")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            twd.ternary_linear_bf16_noalloc(wp, segs, gammas, xd, acc, y)
+    for rep in range(3):
+        acc.fill_(-1)
+        y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(acc.cpu().numpy(), ref["acc"])
+        err = np.abs(y.cpu().numpy().astype(np.float64) - ref["y"])
+        assert not (err > REL_TOL * np.abs(ref["y"])).any(), f"replay {rep}: y outside 1e-6"
+        _ = float(y.sum())  # eager work between replays
