@@ -255,6 +255,19 @@ def stream_read_reference(twd, torch, dev_set, reps):
     return one, per
 
 
+def settle(torch, fn, seconds=0.25):
+    """Untimed direct launches of fn for about `seconds`: the clocks settle
+    before a timed run, as before the headline's."""
+    t_end = time.perf_counter() + seconds
+    i = 0
+    while time.perf_counter() < t_end:
+        fn()
+        i += 1
+        if i % 64 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def time_graph(torch, fn, reps):
     """Capture fn into a graph and time reps replays: (graph, seconds per
     replay)."""
@@ -285,7 +298,7 @@ def width_entry(twd, torch, dev_set, workload, M, kernel, reps, outliers=False,
         torch.cuda.synchronize()
         if "fused" in forms and not st.equals(ref):
             raise SystemExit(f"sweep differs from the per-projection launches at M={M}")
-        st.sweep()
+        settle(torch, st.sweep)
         _, sec = time_launches(torch, st.sweep, reps)
         sec /= reps
         e = {"gbs": round(nbytes / sec / 1e9, 1), "frac": round(nbytes / sec / 1e9 / HBM_PEAK_GBS, 4),
