@@ -33,13 +33,19 @@ constexpr int kLdsHardCap = 160 * 1024;
 // one run of 16 (t1 - t0) values: written at the end, each run goes out as
 // whole lines in one pass, instead of 64-byte pieces of 16 token rows
 // interleaved with the weight stream.  A workgroup defers when its staged
-// activations and the outputs of all its spans fit in LDS together.
+// activations and the outputs of all its spans fit in LDS together: as the
+// fp32 y (and int32 acc) values where they fit, else as each output's
+// accumulator cut to 24 bits (|acc| <= 127 K < 2^20 for K <= 8192), three
+// bytes instead of four for y or eight for acc and y, from which the
+// write-out recomputes y exactly as the epilogue does.  (The packed form
+// costs the write-out about 1 us at M = 4, where the fp32 rows fit.)
 // Deferring only some spans was slower than deferring none: the workgroup
 // then pays both for the stores in the stream and for the write-out at the
 // end.
 int lay_out_deferred(SweepWork &w, const std::vector<SweepProj> &P, int m, int staged_end) {
-    int off = (staged_end + 15) & ~15;
-    for (int s = 0; s < w.nspan; ++s) {
+    const int base = (staged_end + 15) & ~15;
+    int off = base;
+    for (int s = 0; s < w.nspan; ++s) {  // fp32 y and int32 acc rows
         SweepSpan &sp = w.span[s];
         const SweepProj &d = P[sp.q];
         const int bytes = 4 * m * 16 * (sp.t1 - sp.t0);
@@ -48,9 +54,23 @@ int lay_out_deferred(SweepWork &w, const std::vector<SweepProj> &P, int m, int s
         sp.aoff = d.acc ? off : -1;
         off += d.acc ? bytes : 0;
     }
-    w.defer = off <= kLdsHardCap ? 1 : 0;
-    if (w.defer)
+    if (off <= kLdsHardCap) {
+        w.defer = 1;
         return off;
+    }
+    off = base;
+    for (int s = 0; s < w.nspan; ++s) {  // 24-bit accumulators
+        SweepSpan &sp = w.span[s];
+        const SweepProj &d = P[sp.q];
+        sp.aoff = -1;
+        sp.yoff = d.y || d.acc ? off : -1;
+        off += d.y || d.acc ? (3 * m * 16 * (sp.t1 - sp.t0) + 15) & ~15 : 0;
+    }
+    if (off <= kLdsHardCap) {
+        w.defer = 2;
+        return off;
+    }
+    w.defer = 0;
     for (int s = 0; s < w.nspan; ++s)
         w.span[s].yoff = w.span[s].aoff = -1;
     return staged_end;

@@ -41,8 +41,10 @@
 // Outputs.  Stores issued inside the weight stream, 64 bytes for each of up
 // to 16 token rows per tile, slow the stream far more than their bytes
 // would suggest.  Where the workgroup's outputs fit in LDS beside its staged
-// activations (the planner decides), the epilogue writes them to LDS and the
-// workgroup writes each token row's run of consecutive outputs at the end.
+// activations (the planner decides), the epilogue keeps them there -- as the
+// fp32 y and int32 acc values, or, where only that fits, as 24-bit
+// accumulators from which y is recomputed -- and the workgroup writes each
+// token row's run of consecutive outputs at the end.
 #include <type_traits>
 
 #include "kernel_common.h"
@@ -176,7 +178,9 @@ struct SpanOut {
     int qs;     // row sum of q for token r
     float sc;   // scale of token r
     bool vec;   // 16-byte stores: N % 4 == 0 and both outputs 16-byte aligned
-    bool def;   // outputs gathered in LDS (ydef / adef: [M][rows], null if absent)
+    int def;    // outputs gathered in LDS: 1 as fp32 y / int32 acc rows (ydef /
+                // adef: [M][rows], null if absent), 2 as 24-bit accumulators
+                // (ydef: [M][rows] of 3 bytes); 0 stored in the stream
     uint8_t *ydef;
     uint8_t *adef;
     int t0, rows;  // the span's first tile and 16 x its tile count
@@ -187,7 +191,8 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 // After a tile's last pass: lane (token r, group g) holds rows 4g .. 4g+3,
 // four consecutive outputs of token r, written with one 16-byte store each
 // for acc and y where the row layout allows it -- into the span's LDS rows
-// when the workgroup defers its outputs (rows past N are never written out).
+// when the workgroup defers its outputs, as values or as four 24-bit
+// accumulators in three words (rows past N are never written out).
 template <int M>
 __device__ __forceinline__ void epilogue(const SpanOut &so, int t, int r, int g, const v4i &c0,
                                          const v4i &c3, const v4i &c4, const v4i &c16) {
@@ -200,12 +205,23 @@ __device__ __forceinline__ void epilogue(const SpanOut &so, int t, int r, int g,
         tot[i] = cc[i] - so.qs;
         yv[i] = static_cast<float>(tot[i]) * so.sc * row_gamma(so.segs, n0 + i);
     }
-    if (r < M && n0 < so.N && so.def) {
+    if (r < M && n0 < so.N && so.def == 1) {
         const int e = 4 * (r * so.rows + 16 * (t - so.t0) + 4 * g);
         if (so.adef)
             *reinterpret_cast<v4i *>(so.adef + e) = tot;
         if (so.ydef)
             *reinterpret_cast<v4f *>(so.ydef + e) = yv;
+    } else if (r < M && n0 < so.N && so.def == 2 && so.ydef) {
+        // |acc| <= 127 K < 2^23: the low 24 bits keep it
+        uint32_t *d = reinterpret_cast<uint32_t *>(
+            so.ydef + 3 * (r * so.rows + 16 * (t - so.t0) + 4 * g));
+        const uint32_t u0 = static_cast<uint32_t>(tot[0]) & 0xFFFFFFu;
+        const uint32_t u1 = static_cast<uint32_t>(tot[1]) & 0xFFFFFFu;
+        const uint32_t u2 = static_cast<uint32_t>(tot[2]) & 0xFFFFFFu;
+        const uint32_t u3 = static_cast<uint32_t>(tot[3]) & 0xFFFFFFu;
+        d[0] = u0 | (u1 << 24);
+        d[1] = (u1 >> 8) | (u2 << 16);
+        d[2] = (u2 >> 16) | (u3 << 8);
     } else if (r < M && n0 < so.N) {
         const int64_t o = static_cast<int64_t>(r) * so.N + n0;
         if (so.vec) {
@@ -263,6 +279,63 @@ __device__ __forceinline__ void write_deferred(const uint8_t *smem, const SweepS
                     acc[o + j] = *reinterpret_cast<const int32_t *>(smem + sp.aoff + e + 4 * j);
                 if (sp.yoff >= 0)
                     y[o + j] = *reinterpret_cast<const float *>(smem + sp.yoff + e + 4 * j);
+            }
+        }
+    }
+}
+
+// Write a packed deferred span's LDS rows ([M][rows] 24-bit accumulators, rows =
+// 16 (t1 - t0), from output row 16 t0) to acc and y, y recomputed from the
+// accumulator with the epilogue's own fp32 operations (so the same bits):
+// each thread takes four consecutive outputs of a token row, 16-byte stores
+// where N % 4 == 0 and both outputs are 16-byte aligned, else 4-byte stores;
+// rows at or past N stay in LDS.  scale: the span's per-token scales.
+template <int M>
+__device__ __forceinline__ void write_packed(const uint8_t *smem, const SweepSpan &sp,
+                                             cptr<SweepProj> P, const float *scale, int tid,
+                                             int nthreads) {
+    if (sp.yoff < 0)
+        return;
+    const int N = P->N;
+    const int rows = 16 * (sp.t1 - sp.t0);
+    const int n0 = 16 * sp.t0;
+    const int valid = N - n0 < rows ? N - n0 : rows;
+    int32_t *acc = P->acc;
+    float *y = P->y;
+    const Segments segs = segs_of(P);
+    const bool vec = (N & 3) == 0 &&
+                     ((reinterpret_cast<uintptr_t>(acc) | reinterpret_cast<uintptr_t>(y)) & 15) ==
+                         0;
+    for (int r = 0; r < M; ++r) {
+        const int64_t o = static_cast<int64_t>(r) * N + n0;
+        const float sc = scale[r];
+        for (int j = 4 * tid; j < valid; j += 4 * nthreads) {
+            const uint32_t *d =
+                reinterpret_cast<const uint32_t *>(smem + sp.yoff + 3 * (r * rows + j));
+            const uint32_t w0 = d[0], w1 = d[1], w2 = d[2];
+            v4i a;
+            a[0] = static_cast<int32_t>(w0 << 8) >> 8;
+            a[1] = static_cast<int32_t>(((w0 >> 24) | (w1 << 8)) << 8) >> 8;
+            a[2] = static_cast<int32_t>(((w1 >> 16) | (w2 << 16)) << 8) >> 8;
+            a[3] = static_cast<int32_t>(w2) >> 8;
+            v4f yv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                yv[i] = static_cast<float>(a[i]) * sc * row_gamma(segs, n0 + j + i);
+            if (vec) {
+                if (acc)
+                    *reinterpret_cast<v4i *>(acc + o + j) = a;
+                if (y)
+                    *reinterpret_cast<v4f *>(y + o + j) = yv;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (j + i < valid) {
+                        if (acc)
+                            acc[o + j + i] = a[i];
+                        if (y)
+                            y[o + j + i] = yv[i];
+                    }
             }
         }
     }
@@ -507,7 +580,7 @@ void sweep_kernel(const SweepHeader *header_g, const SweepProj *projs_g,
                   15) == 0;
         bsrc = r < M ? xbase + sp.xoff + r * P->stride + 64 * g : zero;
         ustep = r < M ? 256 : 0;
-        so.def = sp.yoff >= 0 || sp.aoff >= 0;
+        so.def = wk->defer;
         so.ydef = sp.yoff >= 0 ? smem + sp.yoff : nullptr;
         so.adef = sp.aoff >= 0 ? smem + sp.aoff : nullptr;
         so.t0 = sp.t0;
@@ -552,7 +625,11 @@ void sweep_kernel(const SweepHeader *header_g, const SweepProj *projs_g,
     if (wk->defer) {
         __syncthreads();
         for (int s = 0; s < nspan; ++s)
-            write_deferred<M>(smem, span_at(wk, s), projs + wk->span[s].q, tid, 64 * NW);
+            if (wk->defer == 2)
+                write_packed<M>(smem, span_at(wk, s), projs + wk->span[s].q, st_scale + s * 16,
+                                tid, 64 * NW);
+            else
+                write_deferred<M>(smem, span_at(wk, s), projs + wk->span[s].q, tid, 64 * NW);
     }
 }
 

@@ -227,7 +227,8 @@ def whole_sets(env):
 
 
 WHOLE_SET_CASES = [("2b", "2b_decode", 1), ("2b", "2b_verify", 2), ("2b", "2b_verify", 4),
-                   ("2b", "2b_verify", 8), ("2b", "2b_sweep_outlier", 16),
+                   ("2b", "2b_verify", 8), ("2b", "2b_verify", 11),
+                   ("2b", "2b_sweep_outlier", 16),
                    ("4b", "4b_stack", 1), ("4b", "4b_stack", 4), ("4b", "4b_stack", 16)]
 
 

@@ -96,9 +96,12 @@ def test_plan_covers_every_tile_once(li, M, outs):
             assert t0 < t1
             seen.extend((q, t) for t in range(t0, t1))
         assert lds <= h["lds"] <= 160 * 1024
-        # deferred outputs: per span, y then acc rows [M][16 (t1 - t0)] fp32 /
-        # int32, from the first 16-byte boundary past the staged rows, when
-        # the rows of all its spans fit in 160 KiB
+        # deferred outputs, from the first 16-byte boundary past the staged
+        # rows, when the rows of all its spans fit in 160 KiB: per span, y
+        # then acc rows [M][16 (t1 - t0)] fp32 / int32 (defer = 1); where
+        # those do not fit, per span with any output, [M][16 (t1 - t0)]
+        # 24-bit accumulators, 3 bytes each, rounded up to 16 bytes, at yoff
+        # (defer = 2)
         off = (lds + 15) & ~15
         expect = []
         for s in range(n):
@@ -110,10 +113,20 @@ def test_plan_covers_every_tile_once(li, M, outs):
             ea = off if a else -1
             off += b if a else 0
             expect.append((ey, ea))
+        packed_off = (lds + 15) & ~15
+        packed = []
+        for s in range(n):
+            q, t0, t1 = (int(v) for v in w["span"][s][:3])
+            a, y = OUTPUTS[outs](q)
+            packed.append((packed_off if a or y else -1, -1))
+            packed_off += (3 * M * 16 * (t1 - t0) + 15) & ~15 if a or y else 0
         got = [(int(w["span"][s][4]), int(w["span"][s][5])) for s in range(n)]
         if n and off <= 160 * 1024:
             assert w["defer"] == 1 and got == expect
             assert off <= h["lds"]
+        elif n and packed_off <= 160 * 1024:
+            assert w["defer"] == 2 and got == packed
+            assert packed_off <= h["lds"]
         else:
             assert w["defer"] == 0 and all(g == (-1, -1) for g in got)
     expect = [(q, t) for q, (K, s) in enumerate(shapes) for t in range(-(-sum(s) // 16))]
@@ -143,21 +156,27 @@ def test_plan_balances_bytes():
 
 
 @pytest.mark.parametrize("M,acc,deferring", [(1, False, 256), (4, False, 256), (1, True, 256),
-                                             (8, False, None), (16, False, 0),
-                                             (16, True, 0)])
+                                             (8, False, 256), (8, True, 256), (12, False, None),
+                                             (16, False, 0), (16, True, 0)])
 def test_plan_defers_where_outputs_fit(M, acc, deferring):
-    """The 2B-class layer set: at small M every workgroup gathers its outputs
-    in LDS (y alone, or acc and y); at M = 16 the staged activations leave no
-    room for every span's outputs in most workgroups, which then write in the
-    stream; a workgroup defers all its spans or none."""
+    """The 2B-class layer set: up to M = 8 every workgroup gathers its outputs
+    in LDS (as values where they fit, else as 24-bit accumulators, with or
+    without acc); at M = 12 some do; at M = 16 the staged activations leave
+    no room for every span's outputs in any workgroup, which then write in
+    the stream; a workgroup defers all its spans or none.  At M = 1 and 4 the
+    values fit everywhere."""
     ls = [(2560, (2560, 640, 640)), (2560, (2560,)), (2560, (6912, 6912)), (6912, (2560,))] * 30
     img, p = plan(ls, M, outputs=lambda i: (acc, True))
     h, projs, work = decode(img)
-    n = int(sum(int(w["defer"]) for w in work))
+    n = int(sum(int(w["defer"]) > 0 for w in work))
     if deferring is None:
         assert 0 < n < len(work)
     else:
         assert n == min(deferring, len(work))
+    if M <= 4:
+        assert all(int(w["defer"]) == 1 for w in work)
+    if M == 12:
+        assert any(int(w["defer"]) == 2 for w in work)
     assert h["lds"] <= 160 * 1024
 
 
