@@ -290,6 +290,8 @@ __device__ __forceinline__ void write_deferred(const uint8_t *smem, const SweepS
 // each thread takes four consecutive outputs of a token row, 16-byte stores
 // where N % 4 == 0 and both outputs are 16-byte aligned, else 4-byte stores;
 // rows at or past N stay in LDS.  scale: the span's per-token scales.
+static_assert(127 * TWD_MAX_K < (1 << 23), "a deferred accumulator fits in 24 bits");
+
 template <int M>
 __device__ __forceinline__ void write_packed(const uint8_t *smem, const SweepSpan &sp,
                                              cptr<SweepProj> P, const float *scale, int tid,
