@@ -70,8 +70,13 @@ OUTPUTS = {"both": lambda i: (True, True), "y": lambda i: (False, True),
 @pytest.mark.parametrize("M", [1, 4, 16])
 @pytest.mark.parametrize("li", range(len(SHAPE_LISTS)))
 def test_plan_covers_every_tile_once(li, M, outs):
-    shapes = SHAPE_LISTS[li]
-    img, p = plan(shapes, M, outputs=OUTPUTS[outs])
+    check_plan(SHAPE_LISTS[li], M, OUTPUTS[outs])
+
+
+def check_plan(shapes, M, outputs):
+    """Decode the plan of (K, seg_rows) list `shapes` at width M and check
+    every field against the planner's rules."""
+    img, p = plan(shapes, M, outputs=outputs)
     h, projs, work = decode(img)
     assert h["magic"] == 0x53445754 and h["nproj"] == len(shapes) and h["M"] == M
     assert p.nwg == h["nwg"] == len(work) and p.lds_bytes == h["lds"]
@@ -106,7 +111,7 @@ def test_plan_covers_every_tile_once(li, M, outs):
         expect = []
         for s in range(n):
             q, t0, t1 = (int(v) for v in w["span"][s][:3])
-            a, y = OUTPUTS[outs](q)
+            a, y = outputs(q)
             b = 4 * M * 16 * (t1 - t0)
             ey = off if y else -1
             off += b if y else 0
@@ -117,7 +122,7 @@ def test_plan_covers_every_tile_once(li, M, outs):
         packed = []
         for s in range(n):
             q, t0, t1 = (int(v) for v in w["span"][s][:3])
-            a, y = OUTPUTS[outs](q)
+            a, y = outputs(q)
             packed.append((packed_off if a or y else -1, -1))
             packed_off += (3 * M * 16 * (t1 - t0) + 15) & ~15 if a or y else 0
         got = [(int(w["span"][s][4]), int(w["span"][s][5])) for s in range(n)]
@@ -131,6 +136,23 @@ def test_plan_covers_every_tile_once(li, M, outs):
             assert w["defer"] == 0 and all(g == (-1, -1) for g in got)
     expect = [(q, t) for q, (K, s) in enumerate(shapes) for t in range(-(-sum(s) // 16))]
     assert seen == expect
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_plan_random_lists(seed):
+    """Seeded random lists (1-24 projections, K from 64 to 8192, up to four
+    segments of 0-3000 rows, acc or y or both) at random widths: every
+    rule of the plan holds, whichever deferral form each workgroup takes."""
+    rng = np.random.default_rng([91, seed])
+    n = int(rng.integers(1, 25))
+    shapes = []
+    for _ in range(n):
+        K = 64 * int(rng.integers(1, 129))
+        segs = tuple(int(v) for v in rng.integers(0, 3001, int(rng.integers(1, 5))))
+        shapes.append((K, segs))
+    M = int(rng.integers(1, 17))
+    mask = rng.integers(1, 4, n)  # acc, y or both (a projection needs an output)
+    check_plan(shapes, M, lambda i: (bool(mask[i] & 1), bool(mask[i] & 2)))
 
 
 def test_plan_balances_bytes():
