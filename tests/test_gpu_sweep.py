@@ -6,10 +6,11 @@ within 1e-6 relative of the oracle's double-precision value.  Cases: random
 projection lists at every width M = 1..16 (ragged K and N, 1..4 segments,
 empty projections, K = 64 and K = 8192), one full-size 2B-class layer at
 every width on the outlier workload, whole layer sets in the benchmark's
-launch (the 2B set at M = 1, 2, 4, 8 and on the outlier workload at M = 16,
-the 4B stack at M = 1, 4, 16; sampled rows against the oracle, every row
-against the per-projection launches), graph replays checked against the
-oracle, and a table that does not match its plan (nothing written).
+launch (the 2B set at M = 1, 2, 4, 8, 11 and on the outlier workload at
+M = 16, the 4B stack at M = 1, 4, 16; sampled rows against the oracle, every
+row against the per-projection launches), outputs deferred as 24-bit
+accumulators on ragged and misaligned outputs, graph replays checked against
+the oracle, and a table that does not match its plan (nothing written).
 """
 import sys
 
@@ -266,6 +267,60 @@ def test_sweep_whole_layer_set(env, whole_sets, set_name, workload, M):
         assert torch.equal(y, y2), key
         np.testing.assert_array_equal(acc.cpu().numpy()[:, rows], ra)
         check_y(y.cpu().numpy()[:, rows], ry, f"{key}")
+
+
+def test_sweep_packed_deferral_ragged(env):
+    """Workgroups whose outputs fit in LDS only as 24-bit accumulators (M =
+    16, K = 64 and 128, about 2800 rows per workgroup), on ragged N (N % 4 !=
+    0) and on a y that is not 16-byte aligned, so the packed write-out takes
+    both of its store forms: every output equals the per-projection launch,
+    sampled rows equal the oracle."""
+    torch, twd, orc = env
+    M = 16
+    specs = [(64, (145001,), True, True, False), (64, (70000, 74999), False, True, False),
+             (128, (72999,), True, False, False), (64, (144997,), True, True, True),
+             (64, (145003, 2), False, True, False)]
+    entries, checks = [], []
+    for i, (K, segs, want_acc, want_y, misaligned) in enumerate(specs):
+        W, segs, x = wl.random_case(seed=5100 + i, M=M, K=K, seg_rows=segs)
+        N = int(sum(segs))
+        packed, gammas = twd.prepare_weights(W, segs)
+        t, gam, grow = orc.ternarize_segments(W, segs)
+        assert gam == list(gammas)
+        rows = np.sort(np.random.default_rng([5200, i]).choice(N, SAMPLED_ROWS, replace=False))
+        q, sc = orc.quantize_act(x)
+        ra = orc.linear(q, t[rows].copy())
+        ry = orc.dequant(ra, sc, grow[rows].copy())
+        del W, t
+        wt = torch.from_numpy(twd.tile_for_sweep(packed, N, K)).cuda()
+        wp = torch.from_numpy(packed).cuda()
+        xd = dev_bf16(torch, x)
+        acc = torch.full((M, N), -7, dtype=torch.int32, device="cuda") if want_acc else None
+        y = None
+        if want_y:
+            buf = torch.full((M * N + 1,), -7.0, device="cuda")
+            y = (buf[1:] if misaligned else buf[:-1]).view(M, N)
+            assert (y.data_ptr() % 16 != 0) == misaligned
+        entries.append((wt, segs, gammas, xd, acc, y))
+        checks.append((wp, segs, gammas, xd, rows, ra, ry))
+    sw = twd.Sweep(entries)
+    img = sw.table.cpu().numpy()
+    nwg, work_off = (int(v) for v in img[:32].view(np.int32)[[3, 7]])
+    defer = img[work_off:work_off + 144 * nwg].view(np.int32).reshape(nwg, 36)[:, 1]
+    log(f"sweep packed deferral: {nwg} workgroups, {int((defer == 2).sum())} packed, "
+        f"{int((defer == 1).sum())} with values, {int((defer == 0).sum())} in the stream")
+    assert (defer == 2).sum() > nwg // 2
+    sw.run()
+    torch.cuda.synchronize()
+    for (wt, segs, gammas, xd, acc, y), (wp, _, _, _, rows, ra, ry) in zip(entries, checks):
+        a2, y2 = twd.ternary_linear_bf16(wp, segs, gammas, xd)
+        torch.cuda.synchronize()
+        if acc is not None:
+            assert torch.equal(acc, a2)
+            np.testing.assert_array_equal(acc.cpu().numpy()[:, rows], ra)
+        if y is not None:
+            assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
+            check_y(y.cpu().numpy()[:, rows], ry, "packed deferral")
 
 
 def test_sweep_graph_replays_match_oracle(env):
