@@ -37,8 +37,10 @@ constexpr int kLdsHardCap = 160 * 1024;
 // fp32 y (and int32 acc) values where they fit, else as each output's
 // accumulator cut to 24 bits (|acc| <= 127 K < 2^20 for K <= 8192), three
 // bytes instead of four for y or eight for acc and y, from which the
-// write-out recomputes y exactly as the epilogue does.  (The packed form
-// costs the write-out about 1 us at M = 4, where the fp32 rows fit.)
+// write-out recomputes y exactly as the epilogue does -- for every tile
+// where they fit, else for each span's first tiles, as many as fit in
+// order, the rest storing in the stream.  (The packed form costs the
+// write-out about 1 us at M = 4, where the fp32 rows fit.)
 // Deferring only some spans was slower than deferring none: the workgroup
 // then pays both for the stores in the stream and for the write-out at the
 // end.
@@ -59,14 +61,21 @@ int lay_out_deferred(SweepWork &w, const std::vector<SweepProj> &P, int m, int s
         return off;
     }
     off = base;
-    for (int s = 0; s < w.nspan; ++s) {  // 24-bit accumulators
+    int deferred = 0;
+    const int per_tile = 3 * m * 16;  // a multiple of 16
+    for (int s = 0; s < w.nspan; ++s) {  // 24-bit accumulators, as many tiles as fit
         SweepSpan &sp = w.span[s];
         const SweepProj &d = P[sp.q];
         sp.aoff = -1;
-        sp.yoff = d.y || d.acc ? off : -1;
-        off += d.y || d.acc ? (3 * m * 16 * (sp.t1 - sp.t0) + 15) & ~15 : 0;
+        const int room = kLdsHardCap - off;
+        int nd = d.y || d.acc ? (room > 0 ? room / per_tile : 0) : 0;
+        nd = nd < sp.t1 - sp.t0 ? nd : sp.t1 - sp.t0;
+        sp.nd = nd;
+        sp.yoff = nd > 0 ? off : -1;
+        off += nd * per_tile;
+        deferred += nd;
     }
-    if (off <= kLdsHardCap) {
+    if (deferred > 0) {
         w.defer = 2;
         return off;
     }

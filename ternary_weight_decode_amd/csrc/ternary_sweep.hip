@@ -43,8 +43,10 @@
 // would suggest.  Where the workgroup's outputs fit in LDS beside its staged
 // activations (the planner decides), the epilogue keeps them there -- as the
 // fp32 y and int32 acc values, or, where only that fits, as 24-bit
-// accumulators from which y is recomputed -- and the workgroup writes each
-// token row's run of consecutive outputs at the end.
+// accumulators from which y is recomputed, for as many of each span's first
+// tiles as fit -- and the workgroup writes each token row's run of
+// consecutive outputs at the end; only the tiles past those store in the
+// stream.
 #include <type_traits>
 
 #include "kernel_common.h"
@@ -72,6 +74,7 @@ __device__ __forceinline__ SweepSpan span_at(cptr<SweepWork> wk, int s) {
     sp.xoff = wk->span[s].xoff;
     sp.yoff = wk->span[s].yoff;
     sp.aoff = wk->span[s].aoff;
+    sp.nd = wk->span[s].nd;
     return sp;
 }
 
@@ -180,10 +183,12 @@ struct SpanOut {
     bool vec;   // 16-byte stores: N % 4 == 0 and both outputs 16-byte aligned
     int def;    // outputs gathered in LDS: 1 as fp32 y / int32 acc rows (ydef /
                 // adef: [M][rows], null if absent), 2 as 24-bit accumulators
-                // (ydef: [M][rows] of 3 bytes); 0 stored in the stream
+                // of the span's first nd tiles (ydef: [M][rows] of 3 bytes,
+                // the later tiles stored in the stream); 0 stored in the stream
     uint8_t *ydef;
     uint8_t *adef;
-    int t0, rows;  // the span's first tile and 16 x its tile count
+    int t0, rows;  // the span's first tile and 16 x its deferred tile count
+    int nd;
 };
 
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -211,7 +216,7 @@ __device__ __forceinline__ void epilogue(const SpanOut &so, int t, int r, int g,
             *reinterpret_cast<v4i *>(so.adef + e) = tot;
         if (so.ydef)
             *reinterpret_cast<v4f *>(so.ydef + e) = yv;
-    } else if (r < M && n0 < so.N && so.def == 2 && so.ydef) {
+    } else if (r < M && n0 < so.N && so.def == 2 && t - so.t0 < so.nd) {
         // |acc| <= 127 K < 2^23: the low 24 bits keep it
         uint32_t *d = reinterpret_cast<uint32_t *>(
             so.ydef + 3 * (r * so.rows + 16 * (t - so.t0) + 4 * g));
@@ -285,7 +290,7 @@ __device__ __forceinline__ void write_deferred(const uint8_t *smem, const SweepS
 }
 
 // Write a packed deferred span's LDS rows ([M][rows] 24-bit accumulators, rows =
-// 16 (t1 - t0), from output row 16 t0) to acc and y, y recomputed from the
+// 16 nd, from output row 16 t0) to acc and y, y recomputed from the
 // accumulator with the epilogue's own fp32 operations (so the same bits):
 // each thread takes four consecutive outputs of a token row, 16-byte stores
 // where N % 4 == 0 and both outputs are 16-byte aligned, else 4-byte stores;
@@ -296,10 +301,10 @@ template <int M>
 __device__ __forceinline__ void write_packed(const uint8_t *smem, const SweepSpan &sp,
                                              cptr<SweepProj> P, const float *scale, int tid,
                                              int nthreads) {
-    if (sp.yoff < 0)
+    if (sp.yoff < 0 || sp.nd <= 0)
         return;
     const int N = P->N;
-    const int rows = 16 * (sp.t1 - sp.t0);
+    const int rows = 16 * sp.nd;
     const int n0 = 16 * sp.t0;
     const int valid = N - n0 < rows ? N - n0 : rows;
     int32_t *acc = P->acc;
@@ -586,7 +591,8 @@ void sweep_kernel(const SweepHeader *header_g, const SweepProj *projs_g,
         so.ydef = sp.yoff >= 0 ? smem + sp.yoff : nullptr;
         so.adef = sp.aoff >= 0 ? smem + sp.aoff : nullptr;
         so.t0 = sp.t0;
-        so.rows = 16 * (sp.t1 - sp.t0);
+        so.nd = sp.nd;
+        so.rows = 16 * (so.def == 2 ? sp.nd : sp.t1 - sp.t0);
     };
     load_span(0);  // (with no span: the table's zeroed entry, never used)
     v4i c0 = {0, 0, 0, 0}, c3 = c0, c4 = c0, c16 = c0;

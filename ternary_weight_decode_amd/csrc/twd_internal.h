@@ -129,8 +129,8 @@ constexpr uint32_t kSweepMagic = 0x53445754u;  // "TWDS"
 // (kSweepMaxSpans x 16 each), the next-tile counter of each span (16 B),
 // then the staged activation rows, then (where they fit) the deferred
 // outputs: per span, [M][16 (t1 - t0)] values of y and of acc, or where
-// those do not fit, [M][16 (t1 - t0)] accumulators of 24 bits (3 bytes
-// each, four consecutive ones in three words).
+// those do not fit, [M][16 nd] accumulators of 24 bits (3 bytes each, four
+// consecutive ones in three words) for the span's first nd tiles.
 constexpr int kSweepLdsHeader = 64 + 3 * kSweepMaxSpans * 16 * 4 + 16;
 
 struct SweepProj {       // 96 bytes
@@ -152,13 +152,15 @@ struct SweepSpan {       // tiles [t0, t1) of projection q, activations at xoff
     int q, t0, t1, xoff;
     int yoff, aoff;      // LDS byte offsets of the deferred y / acc rows, or -1; with
                          // packed deferral yoff holds the 24-bit accumulators
-    int pad[2];
+    int nd;              // packed deferral: the span's first nd tiles are deferred
+    int pad;
 };
 
 struct SweepWork {       // 144 bytes: one workgroup's spans, in order
     int nspan;
     int defer;           // the spans' outputs gathered in LDS, written at the end:
                          // 1 as fp32 y / int32 acc rows, 2 as 24-bit accumulators
+                         // (of each span's first nd tiles; the rest stored in the stream)
     int pad[2];
     SweepSpan span[kSweepMaxSpans];
 };

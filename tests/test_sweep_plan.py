@@ -19,7 +19,7 @@ PROJ = np.dtype([("w", "<u8"), ("x", "<u8"), ("acc", "<u8"), ("y", "<u8"), ("K",
                  ("N", "<i4"), ("passes", "<i4"), ("slices", "<i4"), ("stride", "<i4"),
                  ("nseg", "<i4"), ("bound", "<i4", 4), ("gamma", "<f4", 4), ("pad", "<i4", 2)])
 WORK = np.dtype([("nspan", "<i4"), ("defer", "<i4"), ("pad", "<i4", 2),
-                 ("span", "<i4", (4, 8))])  # q, t0, t1, xoff, yoff, aoff, pad, pad
+                 ("span", "<i4", (4, 8))])  # q, t0, t1, xoff, yoff, aoff, nd, pad
 LDS_HEADER = 64 + 3 * 4 * 16 * 4 + 16
 MAX_SPANS = 4
 
@@ -102,11 +102,11 @@ def check_plan(shapes, M, outputs):
             seen.extend((q, t) for t in range(t0, t1))
         assert lds <= h["lds"] <= 160 * 1024
         # deferred outputs, from the first 16-byte boundary past the staged
-        # rows, when the rows of all its spans fit in 160 KiB: per span, y
-        # then acc rows [M][16 (t1 - t0)] fp32 / int32 (defer = 1); where
-        # those do not fit, per span with any output, [M][16 (t1 - t0)]
-        # 24-bit accumulators, 3 bytes each, rounded up to 16 bytes, at yoff
-        # (defer = 2)
+        # rows: when the rows of all its spans fit in 160 KiB, per span, y
+        # then acc rows [M][16 (t1 - t0)] fp32 / int32 (defer = 1); else,
+        # per span with any output, the first nd tiles as [M][16 nd] 24-bit
+        # accumulators (3 bytes each) at yoff, nd as large as fits, span
+        # after span (defer = 2, if any tile fits)
         off = (lds + 15) & ~15
         expect = []
         for s in range(n):
@@ -123,15 +123,18 @@ def check_plan(shapes, M, outputs):
         for s in range(n):
             q, t0, t1 = (int(v) for v in w["span"][s][:3])
             a, y = outputs(q)
-            packed.append((packed_off if a or y else -1, -1))
-            packed_off += (3 * M * 16 * (t1 - t0) + 15) & ~15 if a or y else 0
+            nd = min(max(160 * 1024 - packed_off, 0) // (48 * M), t1 - t0) if a or y else 0
+            packed.append((packed_off if nd else -1, -1, nd))
+            packed_off += 48 * M * nd
         got = [(int(w["span"][s][4]), int(w["span"][s][5])) for s in range(n)]
+        nds = [int(w["span"][s][6]) for s in range(n)]
         if n and off <= 160 * 1024:
-            assert w["defer"] == 1 and got == expect
+            assert w["defer"] == 1 and got == expect and nds == [0] * n
             assert off <= h["lds"]
-        elif n and packed_off <= 160 * 1024:
-            assert w["defer"] == 2 and got == packed
-            assert packed_off <= h["lds"]
+        elif n and any(p[2] for p in packed):
+            assert w["defer"] == 2 and [p[:2] for p in packed] == got
+            assert nds == [p[2] for p in packed]
+            assert packed_off <= h["lds"] <= 160 * 1024
         else:
             assert w["defer"] == 0 and all(g == (-1, -1) for g in got)
     expect = [(q, t) for q, (K, s) in enumerate(shapes) for t in range(-(-sum(s) // 16))]
@@ -178,27 +181,28 @@ def test_plan_balances_bytes():
 
 
 @pytest.mark.parametrize("M,acc,deferring", [(1, False, 256), (4, False, 256), (1, True, 256),
-                                             (8, False, 256), (8, True, 256), (12, False, None),
-                                             (16, False, 0), (16, True, 0)])
+                                             (8, False, 256), (8, True, 256), (12, False, 256),
+                                             (16, False, 256), (16, True, 256)])
 def test_plan_defers_where_outputs_fit(M, acc, deferring):
-    """The 2B-class layer set: up to M = 8 every workgroup gathers its outputs
-    in LDS (as values where they fit, else as 24-bit accumulators, with or
-    without acc); at M = 12 some do; at M = 16 the staged activations leave
-    no room for every span's outputs in any workgroup, which then write in
-    the stream; a workgroup defers all its spans or none.  At M = 1 and 4 the
-    values fit everywhere."""
+    """The 2B-class layer set: at M = 1 and 4 every workgroup gathers its
+    outputs in LDS as values; up to M = 8 every workgroup gathers all of
+    them (as values where they fit, else as 24-bit accumulators, with or
+    without acc); at M = 12 and 16 the staged activations leave room for
+    only part of them in some workgroups, which defer the first tiles of
+    their spans and store the rest in the stream."""
     ls = [(2560, (2560, 640, 640)), (2560, (2560,)), (2560, (6912, 6912)), (6912, (2560,))] * 30
     img, p = plan(ls, M, outputs=lambda i: (acc, True))
     h, projs, work = decode(img)
     n = int(sum(int(w["defer"]) > 0 for w in work))
-    if deferring is None:
-        assert 0 < n < len(work)
-    else:
-        assert n == min(deferring, len(work))
+    assert n == min(deferring, len(work))
+    partial = sum(int(w["span"][s][6]) < int(w["span"][s][2]) - int(w["span"][s][1])
+                  for w in work if int(w["defer"]) == 2 for s in range(int(w["nspan"])))
     if M <= 4:
         assert all(int(w["defer"]) == 1 for w in work)
-    if M == 12:
-        assert any(int(w["defer"]) == 2 for w in work)
+    if M <= 8:
+        assert partial == 0
+    else:
+        assert partial > 0
     assert h["lds"] <= 160 * 1024
 
 
