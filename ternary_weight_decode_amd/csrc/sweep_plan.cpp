@@ -32,18 +32,15 @@ constexpr int kLdsHardCap = 160 * 1024;
 // of one projection are consecutive, so for each token row its outputs form
 // one run of 16 (t1 - t0) values: written at the end, each run goes out as
 // whole lines in one pass, instead of 64-byte pieces of 16 token rows
-// interleaved with the weight stream.  A workgroup defers when its staged
-// activations and the outputs of all its spans fit in LDS together: as the
-// fp32 y (and int32 acc) values where they fit, else as each output's
-// accumulator cut to 24 bits (|acc| <= 127 K < 2^20 for K <= 8192), three
-// bytes instead of four for y or eight for acc and y, from which the
-// write-out recomputes y exactly as the epilogue does -- for every tile
-// where they fit, else for each span's first tiles, as many as fit in
-// order, the rest storing in the stream.  (The packed form costs the
-// write-out about 1 us at M = 4, where the fp32 rows fit.)
-// Deferring only some spans was slower than deferring none: the workgroup
-// then pays both for the stores in the stream and for the write-out at the
-// end.
+// interleaved with the weight stream.  A workgroup keeps its outputs in LDS
+// beside its staged activations: as the fp32 y (and int32 acc) values where
+// all of them fit, else as each output's accumulator cut to 24 bits
+// (|acc| <= 127 K < 2^20 for K <= 8192), three bytes instead of four for y
+// or eight for acc and y, from which the write-out recomputes y exactly as
+// the epilogue does -- for every tile where they fit, else for each span's
+// first tiles, as many as fit, span after span, the later tiles storing in
+// the stream.  (The packed form costs the write-out about 1 us at M = 4,
+// where the fp32 values fit, so it is used only where they do not.)
 int lay_out_deferred(SweepWork &w, const std::vector<SweepProj> &P, int m, int staged_end) {
     const int base = (staged_end + 15) & ~15;
     int off = base;
