@@ -1293,19 +1293,22 @@ def summarize_util(args):
     cycles of the dispatch's own duration (2.4 GHz x 1024 SIMDs)."""
     pmc_dir, command = args.summarize_util
     M = args.M or wl.workload_widths(args.workload)[0]
+    sweep = args.util_kernels == "sweep"
     agg = {}
     for r in _csv_rows(pmc_dir, "counter_collection.csv"):
         name = _col(r, "Kernel_Name")
-        if not _linear_fused(name):
+        if not (_short(name).startswith("sweep_kernel<") if sweep else _linear_fused(name)):
             continue
         key = (_short(name), int(_col(r, "Grid_Size", "Grid_Size_X", "grid_size")) // 64)
         d = agg.setdefault(key, {})
         d.setdefault(_col(r, "Counter_Name"), []).append(float(_col(r, "Counter_Value")))
         d.setdefault("_dur", {})[_col(r, "Correlation_Id", "Dispatch_Id")] = (
             int(_col(r, "End_Timestamp")) - int(_col(r, "Start_Timestamp")))
-    lines = [f"# ternary linear, {args.workload}, M={M}: utilization counters", "",
+    what = "multi-projection sweep" if sweep else "ternary linear"
+    lines = [f"# {what}, {args.workload}, M={M}: utilization counters", "",
              "Command (from the repository root):", "", "    " + command, "",
-             "Means per dispatch of the fused linear kernels (one rocprofv3 --pmc run; "
+             f"Means per dispatch of the {'sweep kernel' if sweep else 'fused linear kernels'} "
+             "(one rocprofv3 --pmc run; "
              "dispatches run slower under counter collection than unprofiled).  MFMA busy "
              "share = SQ_VALU_MFMA_BUSY_CYCLES / (dispatch duration x 2.4 GHz x 1024 "
              "SIMDs).", "",
@@ -1326,7 +1329,8 @@ def summarize_util(args):
             f"{mean.get('SQ_INSTS_LDS', 0) / waves:.1f} | "
             f"{mean.get('SQ_LDS_BANK_CONFLICT', 0):,.0f} |")
     lines.append("")
-    out = os.path.join(args.profile_out, f"ternary_linear_{args.workload}_m{M}_util.md")
+    out = os.path.join(args.profile_out, f"{'sweep' if sweep else 'ternary_linear'}_"
+                       f"{args.workload}_m{M}_util.md")
     with open(out, "w") as f:
         f.write("\n".join(lines))
     print(out)
@@ -1374,6 +1378,8 @@ def main():
                     help="summarize rocprofv3 runs of the output-projection table")
     ap.add_argument("--summarize-util", nargs=2, metavar=("PMC_DIR", "COMMAND"),
                     help="no GPU: summarize a rocprofv3 --pmc run of the utilization counters")
+    ap.add_argument("--util-kernels", default="linear", choices=["linear", "sweep"],
+                    help="with --summarize-util: the fused linear kernels or the sweep")
     ap.add_argument("--profile-out", default=PROFILES)
     ap.add_argument("--profile-run-json", default=None,
                     help="stdout of the profiled kernel-trace run (its own live timing)")
