@@ -269,17 +269,20 @@ def test_sweep_whole_layer_set(env, whole_sets, set_name, workload, M):
         check_y(y.cpu().numpy()[:, rows], ry, f"{key}")
 
 
-def test_sweep_packed_deferral_ragged(env):
+@pytest.mark.parametrize("scale", [1, 2])
+def test_sweep_packed_deferral_ragged(env, scale):
     """Workgroups whose outputs fit in LDS only as 24-bit accumulators (M =
-    16, K = 64 and 128, about 2800 rows per workgroup), on ragged N (N % 4 !=
-    0) and on a y that is not 16-byte aligned, so the packed write-out takes
-    both of its store forms: every output equals the per-projection launch,
-    sampled rows equal the oracle."""
+    16, K = 64 and 128, about 2800 rows per workgroup; at scale 2 about 5600,
+    so that only each span's first tiles fit and the rest store in the
+    stream), on ragged N (N % 4 != 0) and on a y that is not 16-byte
+    aligned, so the packed write-out takes both of its store forms: every
+    output equals the per-projection launch, sampled rows equal the oracle."""
     torch, twd, orc = env
     M = 16
-    specs = [(64, (145001,), True, True, False), (64, (70000, 74999), False, True, False),
-             (128, (72999,), True, False, False), (64, (144997,), True, True, True),
-             (64, (145003, 2), False, True, False)]
+    specs = [(64, (145001 * scale,), True, True, False),
+             (64, (70000 * scale, 74999 * scale), False, True, False),
+             (128, (72999 * scale,), True, False, False), (64, (144997 * scale,), True, True, True),
+             (64, (145003 * scale, 2), False, True, False)]
     entries, checks = [], []
     for i, (K, segs, want_acc, want_y, misaligned) in enumerate(specs):
         W, segs, x = wl.random_case(seed=5100 + i, M=M, K=K, seg_rows=segs)
@@ -306,10 +309,16 @@ def test_sweep_packed_deferral_ragged(env):
     sw = twd.Sweep(entries)
     img = sw.table.cpu().numpy()
     nwg, work_off = (int(v) for v in img[:32].view(np.int32)[[3, 7]])
-    defer = img[work_off:work_off + 144 * nwg].view(np.int32).reshape(nwg, 36)[:, 1]
-    log(f"sweep packed deferral: {nwg} workgroups, {int((defer == 2).sum())} packed, "
-        f"{int((defer == 1).sum())} with values, {int((defer == 0).sum())} in the stream")
+    work = img[work_off:work_off + 144 * nwg].view(np.int32).reshape(nwg, 36)
+    defer = work[:, 1]
+    spans = work[:, 4:].reshape(nwg, 4, 8)  # q, t0, t1, xoff, yoff, aoff, nd, pad
+    partial = sum(int(spans[i, k, 6]) < int(spans[i, k, 2] - spans[i, k, 1])
+                  for i in range(nwg) if defer[i] == 2 for k in range(int(work[i, 0])))
+    log(f"sweep packed deferral x{scale}: {nwg} workgroups, {int((defer == 2).sum())} packed "
+        f"({partial} spans in part), {int((defer == 1).sum())} with values, "
+        f"{int((defer == 0).sum())} in the stream")
     assert (defer == 2).sum() > nwg // 2
+    assert (partial > 0) == (scale == 2)
     sw.run()
     torch.cuda.synchronize()
     for (wt, segs, gammas, xd, acc, y), (wp, _, _, _, rows, ra, ry) in zip(entries, checks):
